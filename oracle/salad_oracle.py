@@ -1,0 +1,410 @@
+"""fp64 reference implementation of SALAD's hybrid attention forward.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+Sources (web pages about arXiv 2601.16515; cited by tag and section):
+
+[S]  "SALAD: Achieve High-Sparsity Attention via Efficient Linear Attention
+     Tuning for Video Diffusion Transformer", structured summary at
+     paper.rainbus.top/paper/2601.16515.  Sections used: Prerequisites
+     (前置知识) > "Sparse Attention" (the {-inf, 0} mask) and "Linear
+     Attention" (H, Z, O formulas); Method step details (方法步骤详情),
+     steps 1-8.
+[I]  ijyty.com/news/870645, article on sparse attention in video diffusion
+     models.  Sections: 1.1 (spatial-temporal sliding-window attention and
+     the head-wise token re-ordering), 1.2 (Top-K block-sparse attention),
+     2.3 (the scalar gate), 4.1 (fixed-gate sensitivity, gate 0).
+[A]  news.axiwang.com/a/172924.html, popular-science article on SALAD.
+     Section 六 (technical details): ReLU linear branch with 3D rotary
+     position encoding; sigmoid gate from a token average.
+[G]  gist.science/fr/paper/2601.16515, French explainer.  Section 2
+     (Méthodologie): A hybrid architecture, B multi-level static/dynamic
+     scaling, C post-tuning branch dropping.
+
+Where the pages leave a step open, the reading taken is stated at the
+function.  Everything is float64 unless a function says it rounds.
+
+Head kinds: 0 = spatial (frame-major order, sliding window),
+1 = temporal (spatial-major order, sliding window), 2 = Top-K block sparse
+(frame-major order).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "HEAD_SPATIAL", "HEAD_TEMPORAL", "HEAD_TOPK",
+    "st_permutation", "head_order",
+    "rope_3d", "round_to_bf16", "round_to_io",
+    "to_working", "block_means", "block_scores", "topk_blocks", "topk_gap",
+    "swa_keys", "topk_keys", "sparse_attention", "sparse_attention_head",
+    "linear_state", "linear_apply", "gate", "combine",
+    "swa_pair_count", "topk_pair_count", "attn_forward",
+]
+
+HEAD_SPATIAL = 0
+HEAD_TEMPORAL = 1
+HEAD_TOPK = 2
+
+
+# --------------------------------------------------------------------------
+# Token order  ([I] 1.1)
+# --------------------------------------------------------------------------
+
+def st_permutation(F: int, Hg: int, Wg: int) -> np.ndarray:
+    """Working order of a temporal head: position p holds token ``pi[p]``.
+
+    [I] 1.1: the latent [F, Hg, Wg] is flattened with time slowest, so one
+    frame's tokens are contiguous and one spatial site recurs every Hg*Wg
+    tokens; temporal heads regroup the tokens by spatial site so that the
+    frames of one site become contiguous.  Reading: sites in row-major
+    (y, x) order, frames ascending inside a site, i.e. p = site*F + f holds
+    token f*Hg*Wg + site.
+    """
+    S = Hg * Wg
+    p = np.arange(F * S, dtype=np.int64)
+    return (p % F) * S + p // F
+
+
+def head_order(kind: int, F: int, Hg: int, Wg: int) -> np.ndarray:
+    """Working order for one head: identity unless the head is temporal
+    ([I] 1.1; Top-K heads keep the frame-major order, [I] 1.2 is silent)."""
+    if kind == HEAD_TEMPORAL:
+        return st_permutation(F, Hg, Wg)
+    return np.arange(F * Hg * Wg, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# Rounding of materialised tensors
+# --------------------------------------------------------------------------
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits (7 stored) and float32's exponent
+    range.  For |x| in [2^(e-1), 2^e) the spacing of bf16 values is
+    2^(e-8); below 2^-126 the spacing is fixed at 2^-133 (subnormals).
+    Dividing by the spacing is exact (a power of two), so ``np.rint`` (round
+    half to even) performs the single correct rounding.  Results of
+    magnitude >= 2^128 overflow to infinity.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    spacing = np.ldexp(1.0, np.maximum(e.astype(np.int64) - 8, -133))
+    y = np.rint(x / spacing) * spacing
+    y = np.where(np.abs(y) >= 2.0 ** 128, np.copysign(np.inf, x), y)
+    return np.where(np.isfinite(x), y, x)
+
+
+def round_to_io(x: np.ndarray, io_dtype: str) -> np.ndarray:
+    """Round a materialised tensor to the layer's storage type ("bf16" or
+    "f32"); the result stays float64."""
+    if io_dtype == "bf16":
+        return round_to_bf16(x)
+    if io_dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    raise ValueError(io_dtype)
+
+
+# --------------------------------------------------------------------------
+# 3D rotary position encoding  ([S] method step 3, [A] 六)
+# --------------------------------------------------------------------------
+
+def rope_3d(x: np.ndarray, F: int, Hg: int, Wg: int,
+            dims=(44, 42, 42), base: float = 10000.0) -> np.ndarray:
+    """Rotate each head vector of ``x`` [B, N, H, d] by its token's 3D position.
+
+    [S] step 3 and [A] 六 add a 3D rotary position encoding to the linear
+    branch; the layer configuration applies it to Q and K before both
+    branches.  Readings: token n = f*Hg*Wg + y*Wg + xx sits at integer
+    position (f, y, xx); the head dimension is cut into consecutive axis
+    segments of ``dims`` (frame, height, width); inside a segment of D dims
+    the pair (2i, 2i+1) turns by angle pos * base^(-2i/D).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, N, H, d = x.shape
+    if sum(dims) != d:
+        raise ValueError("rope dims must sum to head_dim")
+    n = np.arange(N)
+    pos = (n // (Hg * Wg), (n // Wg) % Hg, n % Wg)
+    out = x.copy()
+    off = 0
+    for axis, D in enumerate(dims):
+        for i in range(D // 2):
+            theta = base ** (-2.0 * i / D)
+            ang = pos[axis] * theta
+            c = np.cos(ang)[None, :, None]
+            s = np.sin(ang)[None, :, None]
+            a = x[..., off + 2 * i]
+            b = x[..., off + 2 * i + 1]
+            out[..., off + 2 * i] = a * c - b * s
+            out[..., off + 2 * i + 1] = a * s + b * c
+        off += D
+    return out
+
+
+def to_working(x: np.ndarray, orders) -> np.ndarray:
+    """Gather [B, N, H, d] into per-head working order [B, H, N, d]:
+    working row p of head h is token orders[h][p]."""
+    B, N, H, d = x.shape
+    return np.stack([x[:, orders[h], h, :] for h in range(H)], axis=1)
+
+
+# --------------------------------------------------------------------------
+# Top-K block selection  ([I] 1.2)
+# --------------------------------------------------------------------------
+
+def block_means(xw: np.ndarray, bs: int) -> np.ndarray:
+    """Mean of each block of ``bs`` consecutive rows of ``xw`` [N, d].
+
+    [I] 1.2, first step: cut the tokens into blocks and take each block's
+    mean vector.  Reading: the last block may be short and averages only
+    its valid rows.
+    """
+    N, d = xw.shape
+    nb = -(-N // bs)
+    out = np.empty((nb, d), dtype=np.float64)
+    for b in range(nb):
+        rows = xw[b * bs:min(N, (b + 1) * bs)]
+        out[b] = rows.sum(axis=0) / rows.shape[0]
+    return out
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
+    """Score of key block kb for query block qb: qbar[qb] . kbar[kb].
+
+    [I] 1.2, second step compares queries with key-block means.  Reading:
+    one selection per query block, scored by the block's mean query; the
+    mean over the block of q_i . kbar equals qbar . kbar by linearity, so
+    both descriptions agree.  Unscaled: the ranking ignores any positive
+    scale.
+    """
+    return np.asarray(qbar, np.float64) @ np.asarray(kbar, np.float64).T
+
+
+def topk_blocks(qbar: np.ndarray, kbar: np.ndarray, k: int) -> np.ndarray:
+    """Indices [nb_q, k] of the k best key blocks per query block, ascending.
+
+    Highest score first, equal scores resolved toward the lower block index
+    (a stable sort of the negated scores); no block is forced in.
+    """
+    S = block_scores(qbar, kbar)
+    order = np.argsort(-S, axis=1, kind="stable")[:, :k]
+    return np.sort(order, axis=1).astype(np.int64)
+
+
+def topk_gap(qbar: np.ndarray, kbar: np.ndarray, k: int) -> np.ndarray:
+    """Relative gap between the k-th and (k+1)-th best score per query
+    block (inf when every block is kept).  Rows with a gap of at most 1e-6
+    are near-ties whose selection legitimately depends on rounding order."""
+    S = block_scores(qbar, kbar)
+    nb = S.shape[1]
+    if k >= nb:
+        return np.full(S.shape[0], np.inf)
+    srt = -np.sort(-S, axis=1)
+    a, b = srt[:, k - 1], srt[:, k]
+    den = np.maximum(np.maximum(np.abs(a), np.abs(b)), np.finfo(np.float64).tiny)
+    return (a - b) / den
+
+
+# --------------------------------------------------------------------------
+# Sparse attention  ([S] Prerequisites > Sparse Attention; [I] 1.1, 1.2)
+# --------------------------------------------------------------------------
+
+def swa_keys(p: int, N: int, r: int) -> np.ndarray:
+    """Keys kept for working query p under a sliding window of radius r.
+
+    Reading of [S] Prerequisites > Sparse Attention and [I] 1.1: a
+    symmetric, non-causal window {j : |p - j| <= r} on the (permuted)
+    sequence, clipped at both ends.
+    """
+    return np.arange(max(0, p - r), min(N, p + r + 1), dtype=np.int64)
+
+
+def topk_keys(p: int, idx: np.ndarray, bs: int, N: int) -> np.ndarray:
+    """Keys kept for query p under Top-K selection: every row of every key
+    block selected for p's query block ([I] 1.2, third step)."""
+    qb = p // bs
+    return np.concatenate([np.arange(kb * bs, min(N, (kb + 1) * bs), dtype=np.int64)
+                           for kb in sorted(int(v) for v in idx[qb])])
+
+
+def sparse_attention(qw, kw, vw, keys_of, scale: float, rows=None) -> np.ndarray:
+    """Softmax attention of each working query over its kept keys.
+
+    [S] Prerequisites > Sparse Attention: scores outside the mask are -inf,
+    so each query's softmax runs over its kept keys only.  Reading: logits
+    are scale * q.k with scale = 1/sqrt(d) (the pages give no scale).
+    ``keys_of(p)`` returns the kept key indices; ``rows`` restricts the
+    queries computed (all by default).  Returns [len(rows), d].
+    """
+    qw = np.asarray(qw, np.float64)
+    kw = np.asarray(kw, np.float64)
+    vw = np.asarray(vw, np.float64)
+    N, d = qw.shape
+    if rows is None:
+        rows = range(N)
+    rows = list(rows)
+    out = np.empty((len(rows), vw.shape[1]), dtype=np.float64)
+    for i, p in enumerate(rows):
+        J = keys_of(int(p))
+        logits = scale * (kw[J] @ qw[p])
+        w = np.exp(logits - logits.max())
+        out[i] = (w @ vw[J]) / w.sum()
+    return out
+
+
+def sparse_attention_head(kind: int, qw, kw, vw, *, r: int, bs: int, k: int,
+                          scale: float, rows=None, idx=None):
+    """Sparse branch for one working-order head.  Returns (O_s rows, idx)
+    where idx is the Top-K selection [nb, k] (None for window heads)."""
+    N = qw.shape[0]
+    if kind == HEAD_TOPK:
+        if idx is None:
+            idx = topk_blocks(block_means(qw, bs), block_means(kw, bs), k)
+        return sparse_attention(qw, kw, vw, lambda p: topk_keys(p, idx, bs, N),
+                                scale, rows), idx
+    return sparse_attention(qw, kw, vw, lambda p: swa_keys(p, N, r), scale, rows), None
+
+
+def swa_pair_count(N: int, r: int) -> int:
+    """Number of (query, key) pairs with |i - j| <= r in a length-N sequence."""
+    r = min(r, N - 1)
+    return N * (2 * r + 1) - r * (r + 1)
+
+
+def topk_pair_count(idx: np.ndarray, bs: int, N: int) -> int:
+    """Number of (query, key) pairs computed under a Top-K selection."""
+    nb = idx.shape[0]
+    rows_in = np.array([min(N, (b + 1) * bs) - b * bs for b in range(nb)])
+    return int(sum(rows_in[qb] * rows_in[idx[qb]].sum() for qb in range(nb)))
+
+
+# --------------------------------------------------------------------------
+# Linear attention  ([S] Prerequisites > Linear Attention, step 3)
+# --------------------------------------------------------------------------
+
+def linear_state(k: np.ndarray, v: np.ndarray):
+    """H = relu(K)^T V  [d, d_v] and Z = relu(K)^T 1  [d] over all tokens
+    ([S] Prerequisites > Linear Attention, kernel phi = ReLU)."""
+    pk = np.maximum(np.asarray(k, np.float64), 0.0)
+    return pk.T @ np.asarray(v, np.float64), pk.sum(axis=0)
+
+
+def linear_apply(q: np.ndarray, H: np.ndarray, Z: np.ndarray, eps: float = 1e-6):
+    """O_l = relu(Q) H / (relu(Q) Z + eps), row by row.
+
+    The pages' form has no eps; reading: eps = 1e-6 keeps a query whose
+    features are all non-positive at O_l = 0 instead of 0/0.
+    """
+    pq = np.maximum(np.asarray(q, np.float64), 0.0)
+    return (pq @ H) / (pq @ Z + eps)[:, None]
+
+
+# --------------------------------------------------------------------------
+# Gate and combine  ([S] steps 4-6, [I] 2.3, [A] 六, [G] 2.B)
+# --------------------------------------------------------------------------
+
+def gate(x: np.ndarray, w: np.ndarray, b: float) -> float:
+    """s = sigmoid(w . mean_n X[n, :] + b) for one sample's X [N, C].
+
+    [I] 2.3 and [A] 六: average the hidden state over tokens, then a linear
+    layer and a sigmoid give one scalar in (0, 1).  ([S] step 5 prints the
+    mean outside the sigmoid; the token-average-first order is taken.)
+    """
+    m = np.asarray(x, np.float64).mean(axis=0)
+    t = float(np.dot(np.asarray(w, np.float64), m) + b)
+    return 1.0 / (1.0 + np.exp(-t))
+
+
+def combine(o_s: np.ndarray, o_l: np.ndarray, w_p: np.ndarray, s: float) -> np.ndarray:
+    """O = O_s + s * (O_l W_p)  ([S] steps 4 and 6).
+
+    [S] step 4 passes the linear output through a zero-initialised
+    projection; reading: W_p is [d_in, d_out], shared by the heads of a
+    layer, applied as row-vector times matrix, with no bias.
+    """
+    return np.asarray(o_s, np.float64) + s * (np.asarray(o_l, np.float64) @ np.asarray(w_p, np.float64))
+
+
+# --------------------------------------------------------------------------
+# Whole layer
+# --------------------------------------------------------------------------
+
+def attn_forward(q, k, v, x, w_p, gate_w, gate_b, *, grid, head_kinds,
+                 window_radius, block, topk, io_dtype="bf16", rope=False,
+                 rope_dims=(44, 42, 42), rope_base=10000.0, softmax_scale=None,
+                 linear_eps=1e-6, s_override=None, rows=None):
+    """Hybrid attention layer output for Q, K, V [B, N, H, d] and X [B, N, C].
+
+    Steps ([S] steps 2-6): optional 3D RoPE on Q and K (materialised in the
+    storage type ``io_dtype``); per-head working order ([I] 1.1); sparse
+    branch per head (window or Top-K); linear branch on the same Q, K, V;
+    gate per sample; O = O_s + s * (O_l W_p) written back in token order.
+
+    ``rows`` (optional, a list of (b, n, h) triples) limits the sparse
+    branch to those output rows; the result then maps each triple to its
+    output vector.  Otherwise returns a dict with "out" [B, N, H, d] and
+    the stage results ("o_s", "o_l", "H", "Z", "s", "idx", "orders").
+    """
+    F, Hg, Wg = grid
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, N, H, d = q.shape
+    if N != F * Hg * Wg:
+        raise ValueError("N must equal F*Hg*Wg")
+    scale = 1.0 / np.sqrt(d) if not softmax_scale or softmax_scale <= 0 else softmax_scale
+    if rope:
+        q = round_to_io(rope_3d(q, F, Hg, Wg, rope_dims, rope_base), io_dtype)
+        k = round_to_io(rope_3d(k, F, Hg, Wg, rope_dims, rope_base), io_dtype)
+    orders = [head_order(int(head_kinds[h]), F, Hg, Wg) for h in range(H)]
+    inv = [np.argsort(o) for o in orders]
+
+    s = np.empty(B)
+    Hs = np.empty((B, H, d, v.shape[3]))
+    Zs = np.empty((B, H, d))
+    for b in range(B):
+        s[b] = gate(x[b], gate_w, gate_b) if s_override is None else float(s_override[b])
+        for h in range(H):
+            Hs[b, h], Zs[b, h] = linear_state(k[b, :, h], v[b, :, h])
+
+    idx_all = {}
+    if rows is not None:
+        result = {}
+        work = {}
+        for (b, n, h) in rows:
+            kind = int(head_kinds[h])
+            key = (b, h)
+            if key not in work:
+                work[key] = tuple(t[b, orders[h], h] for t in (q, k, v))
+            qw, kw, vw = work[key]
+            if kind == HEAD_TOPK and key not in idx_all:
+                idx_all[key] = topk_blocks(block_means(qw, block), block_means(kw, block), topk)
+            o_s, _ = sparse_attention_head(kind, qw, kw, vw, r=window_radius, bs=block,
+                                           k=topk, scale=scale, rows=[int(inv[h][n])],
+                                           idx=idx_all.get(key))
+            o_l = linear_apply(q[b, n:n + 1, h], Hs[b, h], Zs[b, h], linear_eps)
+            result[(b, n, h)] = combine(o_s, o_l, w_p, s[b])[0]
+        return result
+
+    out = np.empty((B, N, H, v.shape[3]))
+    o_s_all = np.empty_like(out)
+    o_l_all = np.empty_like(out)
+    for b in range(B):
+        for h in range(H):
+            kind = int(head_kinds[h])
+            qw, kw, vw = (t[b, orders[h], h] for t in (q, k, v))
+            o_s_w, idx = sparse_attention_head(kind, qw, kw, vw, r=window_radius, bs=block,
+                                               k=topk, scale=scale)
+            if idx is not None:
+                idx_all[(b, h)] = idx
+            o_s = o_s_w[inv[h]]  # back to token order
+            o_l = linear_apply(q[b, :, h], Hs[b, h], Zs[b, h], linear_eps)
+            o_s_all[b, :, h] = o_s
+            o_l_all[b, :, h] = o_l
+            out[b, :, h] = combine(o_s, o_l, w_p, s[b])
+    return {"out": out, "o_s": o_s_all, "o_l": o_l_all, "H": Hs, "Z": Zs, "s": s,
+            "idx": idx_all, "orders": orders, "q_used": q, "k_used": k}
