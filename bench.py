@@ -1,0 +1,195 @@
+"""Throughput of the hybrid attention layer on one MI355X.
+
+One step = one salad_attn_forward call (every stage of the layer: gate,
+head-wise permutation, sparse attention, linear state and apply, combine)
+over one batch of synthetic input already resident in HBM.
+
+Default workload: 480p-like ST sliding window, N = 31,200 tokens (20 x 30 x
+52 latent), 12 heads of 128, bf16, half the heads temporal, window radius
+1601 (90 % sparsity).  value = effective TFLOP/s = 4 * d * (computed
+query-key pairs) / layer time; ms_per_step is the layer time (ms/layer).
+
+Also reported:
+  roofline      the sparse-attention kernel's own launch time, read from
+                HIP events the library records on its stream during the
+                timed steps, against the bf16 dense MFMA peak;
+  cpu_baseline  the fp64 oracle on a bounded sample of the same layer on
+                this host's cores, extrapolated to the whole layer.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/layer and effective TFLOP/s of hybrid attention at N=31,200, 90% sparsity"
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "attn_counters.json")
+
+
+def pair_count(w) -> int:
+    """Computed query-key pairs per layer (window heads: closed form; Top-K
+    heads: every selected block's rows, which needs the selection)."""
+    from sparse_linear_hybrid_st_amd.configs import window_pairs
+    n_win = sum(1 for k in w.head_kinds if k != 2)
+    return w.batch * n_win * window_pairs(w.N, w.window_radius)
+
+
+def topk_pairs_from_idx(w, idx) -> int:
+    import numpy as np
+    nb = -(-w.N // w.block)
+    rows = np.array([min(w.N, (b + 1) * w.block) - b * w.block for b in range(nb)], np.int64)
+    tot = 0
+    for h, k in enumerate(w.head_kinds):
+        if k != 2:
+            continue
+        for b in range(w.batch):
+            sel = idx[b, h]                                   # [nb, k]
+            tot += int((rows[:, None] * rows[sel]).sum())
+    return tot
+
+
+def source_sha() -> str:
+    src = os.path.join(ROOT, "sparse_linear_hybrid_st_amd", "csrc", "attn.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def cpu_baseline(w, inp, flops_total: float, target_s: float = 15.0):
+    """Time the fp64 oracle on a bounded sample of the layer and extrapolate."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle as O
+    from sparse_linear_hybrid_st_amd import inputs as I
+
+    args = [I.as_f64(inp[n]) for n in ("q", "k", "v", "x", "w_p", "gate_w")]
+    kw = dict(grid=w.grid, head_kinds=w.head_kinds, window_radius=w.window_radius,
+              block=w.block, topk=w.topk, io_dtype=w.io_dtype, rope=w.rope,
+              rope_dims=w.rope_dims, rope_base=w.rope_base)
+    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
+        if threadpoolctl.threadpool_info() else 1
+    t0 = time.perf_counter()
+    O.attn_forward(*args, inp["gate_b"], rows=[], **kw)       # per-layer part: gate, H, Z
+    t_fixed = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    total_rows = w.batch * w.N * w.n_heads
+    n_rows, t_rows = 64, 0.0
+    while True:                                                  # grow the sample to ~target_s
+        rows = [(int(rng.integers(w.batch)), int(rng.integers(w.N)), int(rng.integers(w.n_heads)))
+                for _ in range(n_rows)]
+        t0 = time.perf_counter()
+        O.attn_forward(*args, inp["gate_b"], rows=rows, **kw)
+        t_rows = time.perf_counter() - t0 - t_fixed
+        if t_rows + t_fixed >= target_s / 3 or n_rows >= total_rows:
+            break
+        n_rows *= 4
+    per_row = max(t_rows, 1e-9) / n_rows
+    t_layer = t_fixed + per_row * total_rows
+    return {
+        "value": flops_total / t_layer / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        "kind": "oracle", "ms_per_layer_extrapolated": t_layer * 1e3,
+        "sample": (f"fp64 numpy oracle: the per-layer part (gate, linear state of all heads) "
+                   f"once ({t_fixed:.2f} s) plus {n_rows} random output rows (sparse attention, "
+                   f"linear apply, combine) in {t_rows:.2f} s, extrapolated to all "
+                   f"{total_rows} rows"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="480p-stswa-h12")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the layer shards by (sample, head) with no communication, so a multi-GPU figure "
+              "is N independent single-GPU layers; it is not measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_linear_hybrid_st_amd as S
+    from sparse_linear_hybrid_st_amd import configs as C
+    from sparse_linear_hybrid_st_amd import inputs as I
+
+    w = C.all_workloads()[args.workload]
+    print(f"[bench] workload {w.name}: {w.description}", file=sys.stderr, flush=True)
+    inp = I.make_inputs(w)
+    p = S.problem_from_workload(w)
+    dev = {n: inp[n].cuda() for n in ("q", "k", "v", "x", "w_p", "gate_w")}
+    out = torch.empty_like(dev["q"])
+    s_out = torch.empty(w.batch, dtype=torch.float32, device="cuda")
+    idx = torch.zeros((w.batch, w.n_heads, p.n_blocks, w.topk), dtype=torch.int32, device="cuda")
+    ws = S.workspace(p)
+
+    def step():
+        S.salad_attn_forward(p, dev["q"], dev["k"], dev["v"], dev["x"], dev["w_p"], dev["gate_w"],
+                             inp["gate_b"], out, ws, s_out=s_out, idx_out=idx)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    pairs = pair_count(w)
+    if 2 in w.head_kinds:
+        pairs += topk_pairs_from_idx(w, idx.cpu().numpy())
+    flops = 4.0 * w.head_dim * pairs
+
+    S.salad_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    calls, attn_ms = S.salad_profile_read()
+    S.salad_profile_enable(False)
+    ms = wall * 1e3 / args.steps
+    attn_avg = attn_ms / max(calls, 1)
+    achieved = flops / (attn_avg * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(PROFILE_COUNTERS):
+        c = json.load(open(PROFILE_COUNTERS))
+        if c.get("source_sha") == source_sha() and c.get("workload") == w.name:
+            traffic = c.get("traffic_bytes_per_launch")
+
+    rec = {
+        "metric": METRIC, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "ms_per_layer": ms,
+        "config": {"workload": w.name, "batch": w.batch, "tokens": w.N, "grid": list(w.grid),
+                   "heads": w.n_heads, "head_dim": w.head_dim,
+                   "head_kinds": "".join("STK"[k] for k in w.head_kinds),
+                   "window_radius": w.window_radius, "block": w.block, "topk": w.topk,
+                   "rope": w.rope, "computed_pairs": pairs,
+                   "density": pairs / (w.batch * w.n_heads * w.N * w.N)},
+        "roofline": {"bound": "mfma", "kernel": "sparse attention (attn_bf16_kernel)",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
+                     "avg_launch_ms": attn_avg, "launches": calls},
+    }
+    if w.io_dtype != "bf16":
+        rec["dtype"] = "f32"
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, inp, flops, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

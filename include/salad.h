@@ -1,0 +1,185 @@
+/*
+ * salad.h -- C ABI of the MI355X (gfx950) hybrid attention library.
+ *
+ * One attention layer of SALAD (arXiv 2601.16515): a high-sparsity branch
+ * (sliding-window attention over head-wise token-permuted sequences, or
+ * Top-K block-sparse attention) and a ReLU linear-attention branch on the
+ * same Q/K/V, combined as  out = O_s + s * (O_l W_p)  with the gate
+ * s = sigmoid(w . mean_tokens(X) + b).
+ *
+ * Sources, cited by tag and section:
+ *  [S] "SALAD: Achieve High-Sparsity Attention via Efficient Linear
+ *      Attention Tuning for Video Diffusion Transformer" -- structured
+ *      summary, paper.rainbus.top/paper/2601.16515: Prerequisites >
+ *      Sparse Attention, Linear Attention; Method step details, steps 1-8.
+ *  [I] ijyty.com/news/870645 (sparse attention in video diffusion
+ *      models): 1.1 ST sliding window and head-wise token re-ordering,
+ *      1.2 Top-K block-sparse attention, 2.3 gate, 4.1 fixed gates.
+ *  [A] news.axiwang.com/a/172924.html: section 六 (technical details).
+ *  [G] gist.science/fr/paper/2601.16515: section 2 (Méthodologie).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Shapes: B batch, N = F*Hg*Wg tokens (frame-major: token
+ *  n = f*Hg*Wg + y*Wg + x), H heads, d head dim (64 or 128), C = H*d.
+ *  Boundary layout [B, N, H, d] row-major: one (token, head) row is d
+ *  contiguous elements.  X is [B, N, C].
+ *  Working layout [B, H, N, d]: row p of head h holds token pi_h(p), where
+ *  pi_h is the identity for spatial and Top-K heads and, for temporal heads,
+ *  pi(p) = (p mod F)*Hg*Wg + floor(p/F) (sites row-major, frames fastest;
+ *  [I] 1.1).
+ *  Storage type (io_dtype) applies to Q, K, V, X, W_p, gate w and out:
+ *  SALAD_F32 (float) or SALAD_BF16 (bfloat16 bits, uint16).  Stage results
+ *  O_s, O_l, H, Z and s are float32; block means are float64.
+ *
+ *  Ownership: every buffer is allocated and freed by the caller.  Device
+ *  pointers must be 16-byte aligned and contiguous in the stated layout.
+ *  Scratch memory comes only from the caller's workspace (ws, ws_bytes),
+ *  sized by salad_workspace_size; the library allocates no device memory
+ *  and keeps no pointer after a call returns.
+ *
+ *  Execution: calls enqueue kernels on `stream` and return without
+ *  synchronising.  Results are deterministic (no floating-point atomics).
+ *
+ *  Errors: every argument is validated before anything is enqueued.  On a
+ *  non-OK status nothing was launched and no output was touched;
+ *  salad_last_error() gives a thread-local message.  SALAD_ERR_HIP reports
+ *  a failed launch; device faults surface at the caller's next sync.
+ *  NaN/Inf inputs propagate.
+ */
+#ifndef SALAD_H
+#define SALAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SALAD_OK = 0,
+  SALAD_ERR_NULL = 1,        /* a required pointer is NULL                   */
+  SALAD_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes           */
+  SALAD_ERR_UNSUPPORTED = 3, /* valid but not built (e.g. d not in {64,128}) */
+  SALAD_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned      */
+  SALAD_ERR_WORKSPACE = 5,   /* ws NULL or ws_bytes below the required size  */
+  SALAD_ERR_HIP = 6          /* a kernel launch failed                       */
+} salad_status;
+
+typedef enum { SALAD_F32 = 0, SALAD_BF16 = 1 } salad_dtype;
+
+enum { SALAD_HEAD_SPATIAL = 0, SALAD_HEAD_TEMPORAL = 1, SALAD_HEAD_TOPK = 2 };
+
+#define SALAD_MAX_HEADS 256
+
+/* The layer's problem statement ([S] method steps 2-6, [I] 1.1-1.2). */
+typedef struct {
+  int32_t batch;                      /* B >= 1                                   */
+  int32_t n_heads;                    /* H in [1, SALAD_MAX_HEADS]                */
+  int32_t head_dim;                   /* d in {64, 128}                           */
+  int32_t grid_f, grid_h, grid_w;     /* latent F x Hg x Wg; N = F*Hg*Wg          */
+  uint8_t head_kind[SALAD_MAX_HEADS]; /* per head: SALAD_HEAD_* (first H used)    */
+  int32_t window_radius;              /* window heads keep key j iff |p-j| <= r   */
+  int32_t block;                      /* Top-K block size (queries and keys)      */
+  int32_t topk;                       /* Top-K: key blocks kept per query block   */
+  float softmax_scale;                /* <= 0 selects 1/sqrt(d)                   */
+  float linear_eps;                   /* linear denominator guard (1e-6 typical)  */
+  int32_t rope;                       /* 1: 3D RoPE on Q and K before both branches */
+  int32_t rope_dims[3];               /* frame/height/width segment sizes, even, sum d */
+  float rope_base;                    /* rotary base (10000)                      */
+  int32_t io_dtype;                   /* salad_dtype                              */
+} salad_problem;
+
+/* Bytes of workspace that any entry point below may need for problem *p
+ * (the largest over all of them).  Errors: NULL, SHAPE, UNSUPPORTED. */
+salad_status salad_workspace_size(const salad_problem *p, size_t *bytes);
+
+/* Head-wise token permutation ([I] 1.1), optionally with 3D RoPE ([S] step 3,
+ * [A] 六).  inverse = 0: src [B,N,H,d] (boundary) -> dst [B,H,N,d] (working);
+ * with apply_rope = 1 each row is rotated by its token's (f, y, x) position
+ * before the store: pair (2i, 2i+1) of an axis segment of D dims turns by
+ * pos * rope_base^(-2i/D), computed in float64 and rounded once to the
+ * storage type.  inverse = 1: src working -> dst boundary (apply_rope must
+ * be 0).  Element type: io_dtype.  src and dst must not overlap. */
+salad_status salad_permute(const salad_problem *p, int apply_rope, int inverse,
+                           const void *src, void *dst, hipStream_t stream);
+
+/* Top-K block selection ([I] 1.2, first two steps).  For every Top-K head:
+ * block means of the working Q and K over blocks of p->block rows (the last
+ * block averages its valid rows), accumulated in float64; score of key block
+ * kb for query block qb = qbar[qb] . kbar[kb] in float64; keep the p->topk
+ * highest, equal scores resolved toward the lower block index; write them
+ * ascending to idx [B, H, nb, topk] (int32, nb = ceil(N/block)).  Rows of
+ * non-Top-K heads are not written.  qbar/kbar (float64 [B,H,nb,d]) receive
+ * the means when non-NULL, else they live in the workspace. */
+salad_status salad_block_select(const salad_problem *p, const void *qw, const void *kw,
+                                int32_t *idx, double *qbar, double *kbar,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Sparse branch ([S] Prerequisites > Sparse Attention; [I] 1.1, 1.2):
+ * o_s[b,h,p,:] = sum_{j in S(p)} softmax_j(scale * q_p . k_j) v_j over the
+ * working rows, with S(p) = {j : |p-j| <= r} for window heads and the rows
+ * of the key blocks idx[b,h,p/block,:] for Top-K heads.  qw, kw, vw working
+ * layout in io_dtype; o_s float32 working layout.  idx may be NULL when no
+ * head is Top-K. */
+salad_status salad_sparse_attn(const salad_problem *p, const void *qw, const void *kw,
+                               const void *vw, const int32_t *idx, float *o_s,
+                               hipStream_t stream);
+
+/* Linear-attention state ([S] Prerequisites > Linear Attention):
+ * h[b,h] = relu(K)^T V  (float32 [B,H,d,d], h[i][j] = sum_n relu(k_n[i]) v_n[j])
+ * and z[b,h] = relu(K)^T 1 (float32 [B,H,d]) over all N tokens.  kw, vw are
+ * working layout (the sums ignore token order).  Split over N with a
+ * fixed-order reduction through the workspace. */
+salad_status salad_linear_state(const salad_problem *p, const void *kw, const void *vw,
+                                float *h, float *z, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Linear-attention output ([S] Prerequisites > Linear Attention):
+ * o_l[b,h,p,:] = relu(q_p)^T H / (relu(q_p) . Z + linear_eps), working layout,
+ * float32 out. */
+salad_status salad_linear_apply(const salad_problem *p, const void *qw, const float *h,
+                                const float *z, float *o_l, hipStream_t stream);
+
+/* Gate ([S] step 5, [I] 2.3, [A] 六): s[b] = sigmoid(w . mean_n X[b,n,:] + bias),
+ * X [B,N,C] and w [C] in io_dtype, s float32 [B] on the device. */
+salad_status salad_gate(const salad_problem *p, const void *x, const void *w, float bias,
+                        float *s, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Combine ([S] steps 4 and 6): out[b, pi_h(p), h, :] =
+ * o_s[b,h,p,:] + s[b] * (o_l[b,h,p,:] W_p), W_p [d_in, d_out] row-major in
+ * io_dtype, shared by all heads, no bias.  o_s, o_l float32 working layout;
+ * s float32 [B] device; out boundary layout in io_dtype. */
+salad_status salad_combine(const salad_problem *p, const float *o_s, const float *o_l,
+                           const void *w_p, const float *s, void *out, hipStream_t stream);
+
+/* Whole layer ([S] steps 2-6): q, k, v [B,N,H,d], x [B,N,C], w_p [d,d],
+ * gate_w [C] in io_dtype -> out [B,N,H,d] in io_dtype.  s_override (device
+ * float [B]) replaces the gate when non-NULL; s_out (device float [B]) and
+ * idx_out ([B,H,nb,topk] int32, Top-K heads only) receive the gate values
+ * and the block selection when non-NULL.  Workspace: salad_workspace_size. */
+salad_status salad_attn_forward(const salad_problem *p, const void *q, const void *k,
+                                const void *v, const void *x, const void *w_p,
+                                const void *gate_w, float gate_b, const float *s_override,
+                                void *out, float *s_out, int32_t *idx_out, void *ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* Measurement hook.  While enabled (on != 0), salad_attn_forward records a
+ * pair of HIP events around its sparse-attention kernel launch(es) on the
+ * caller's stream (the first 4096 calls after enabling are recorded).
+ * salad_profile_read waits for the recorded events, returns the number of
+ * timed calls and their summed duration in milliseconds, and clears the
+ * record.  Process-wide state; not thread-safe; not for use under graph
+ * capture.  Errors: SALAD_ERR_NULL (read with NULL outputs), SALAD_ERR_HIP. */
+salad_status salad_profile_enable(int on);
+salad_status salad_profile_read(int *calls, double *total_ms);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *salad_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SALAD_H */

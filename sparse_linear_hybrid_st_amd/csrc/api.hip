@@ -1,0 +1,410 @@
+// C-ABI entry points: argument validation (before anything is enqueued),
+// workspace carving and launch order.  See include/salad.h for the contract.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/salad.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace salad;
+
+namespace {
+
+thread_local std::string g_err;
+
+salad_status fail(salad_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+salad_status hip_status(hipError_t e, const char *where) {
+  if (e == hipSuccess) return SALAD_OK;
+  return fail(SALAD_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Info {
+  Geom g;
+  int bf16;
+  int any_topk, any_window;
+  size_t esize;
+};
+
+salad_status validate(const salad_problem *p, Info *inf) {
+  if (!p) return fail(SALAD_ERR_NULL, "problem is NULL");
+  if (p->batch < 1) return fail(SALAD_ERR_SHAPE, "batch must be >= 1 (got %d)", p->batch);
+  if (p->n_heads < 1 || p->n_heads > SALAD_MAX_HEADS)
+    return fail(SALAD_ERR_SHAPE, "n_heads must be in [1, %d] (got %d)", SALAD_MAX_HEADS, p->n_heads);
+  if (p->io_dtype != SALAD_F32 && p->io_dtype != SALAD_BF16)
+    return fail(SALAD_ERR_SHAPE, "io_dtype must be SALAD_F32 or SALAD_BF16 (got %d)", p->io_dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(SALAD_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  if (p->io_dtype == SALAD_BF16 && p->head_dim != 128)
+    return fail(SALAD_ERR_UNSUPPORTED, "bf16 kernels are built for head_dim 128 only");
+  if (p->grid_f < 1 || p->grid_h < 1 || p->grid_w < 1)
+    return fail(SALAD_ERR_SHAPE, "grid dims must be >= 1");
+  const long long N = (long long)p->grid_f * p->grid_h * p->grid_w;
+  if (N > (1ll << 28)) return fail(SALAD_ERR_SHAPE, "N = F*Hg*Wg too large (%lld)", N);
+  if ((long long)p->batch * p->n_heads * N * p->head_dim > (1ll << 40))
+    return fail(SALAD_ERR_SHAPE, "tensor too large");
+  Geom &g = inf->g;
+  memset(&g, 0, sizeof g);
+  g.B = p->batch;
+  g.H = p->n_heads;
+  g.D = p->head_dim;
+  g.N = int(N);
+  g.F = p->grid_f;
+  g.Hg = p->grid_h;
+  g.Wg = p->grid_w;
+  inf->any_topk = inf->any_window = 0;
+  for (int h = 0; h < g.H; ++h) {
+    const int k = p->head_kind[h];
+    if (k == SALAD_HEAD_TEMPORAL) g.temporal[h >> 6] |= 1ull << (h & 63);
+    if (k == SALAD_HEAD_TOPK) g.topk[h >> 6] |= 1ull << (h & 63);
+    if (k < 0 || k > 2) return fail(SALAD_ERR_SHAPE, "head_kind[%d] = %d is not a SALAD_HEAD_* value", h, k);
+    if (k == SALAD_HEAD_TOPK) inf->any_topk = 1; else inf->any_window = 1;
+  }
+  if (inf->any_window && p->window_radius < 0)
+    return fail(SALAD_ERR_SHAPE, "window_radius must be >= 0 (got %d)", p->window_radius);
+  g.r = p->window_radius < 0 ? 0 : p->window_radius;
+  if (inf->any_topk) {
+    if (p->block < 1) return fail(SALAD_ERR_SHAPE, "block must be >= 1 (got %d)", p->block);
+    g.block = p->block;
+    g.nb = int((N + p->block - 1) / p->block);
+    if (p->topk < 1 || p->topk > g.nb)
+      return fail(SALAD_ERR_SHAPE, "topk must be in [1, %d] (got %d)", g.nb, p->topk);
+    g.k = p->topk;
+    if (p->io_dtype == SALAD_BF16 && p->block != 64)
+      return fail(SALAD_ERR_UNSUPPORTED, "bf16 Top-K kernels are built for block 64 only (got %d)", p->block);
+    if (g.nb > 4096) return fail(SALAD_ERR_UNSUPPORTED, "more than 4096 key blocks (%d)", g.nb);
+  } else {
+    g.block = p->block > 0 ? p->block : 64;
+    g.nb = int((N + g.block - 1) / g.block);
+    g.k = p->topk;
+  }
+  g.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf(float(p->head_dim));
+  g.eps = p->linear_eps;
+  g.rope_base = p->rope_base;
+  for (int i = 0; i < 3; ++i) g.rope_dims[i] = p->rope_dims[i];
+  if (p->rope) {
+    if (p->rope != 1) return fail(SALAD_ERR_SHAPE, "rope must be 0 or 1");
+    int sum = 0;
+    for (int i = 0; i < 3; ++i) {
+      if (p->rope_dims[i] < 0 || (p->rope_dims[i] & 1))
+        return fail(SALAD_ERR_SHAPE, "rope_dims must be even and >= 0");
+      sum += p->rope_dims[i];
+    }
+    if (sum != p->head_dim) return fail(SALAD_ERR_SHAPE, "rope_dims must sum to head_dim");
+    if (!(p->rope_base > 0.f)) return fail(SALAD_ERR_SHAPE, "rope_base must be > 0");
+  }
+  inf->bf16 = p->io_dtype == SALAD_BF16;
+  inf->esize = inf->bf16 ? 2 : 4;
+  return SALAD_OK;
+}
+
+// Workspace plan.  Regions are 256-byte aligned.
+struct Plan {
+  size_t means, lin_partial, gate_partial;  // per-stage scratch
+  size_t wq, wk, wv, idx, o_s, o_l, h, z, s;  // forward-only buffers
+  size_t total_stage, total_forward;
+};
+
+size_t up(size_t x) { return (x + 255) & ~size_t(255); }
+
+Plan plan(const Info &inf) {
+  const Geom &g = inf.g;
+  Plan pl;
+  const size_t BH = size_t(g.B) * g.H;
+  const size_t rows = BH * g.N;
+  const size_t means = inf.any_topk ? 2 * up(BH * g.nb * g.D * sizeof(double)) : 0;
+  const size_t lin = up(BH * linear_splits(g) * (size_t(g.D) * g.D + g.D) * sizeof(float));
+  const size_t gate = up(size_t(g.B) * gate_splits(g) * g.H * g.D * sizeof(float));
+  pl.means = 0;
+  pl.lin_partial = 0;
+  pl.gate_partial = 0;
+  pl.total_stage = means > lin ? (means > gate ? means : gate) : (lin > gate ? lin : gate);
+  // forward: buffers after a shared scratch region of total_stage bytes
+  size_t off = pl.total_stage;
+  pl.wq = off; off += up(rows * g.D * inf.esize);
+  pl.wk = off; off += up(rows * g.D * inf.esize);
+  pl.wv = off; off += up(rows * g.D * inf.esize);
+  pl.idx = off; off += inf.any_topk ? up(BH * g.nb * g.k * sizeof(int32_t)) : 0;
+  pl.o_s = off; off += up(rows * g.D * sizeof(float));
+  pl.o_l = off; off += up(rows * g.D * sizeof(float));
+  pl.h = off; off += up(BH * g.D * g.D * sizeof(float));
+  pl.z = off; off += up(BH * g.D * sizeof(float));
+  pl.s = off; off += up(size_t(g.B) * sizeof(float));
+  pl.total_forward = off;
+  return pl;
+}
+
+#define CHECK(x)                       \
+  do {                                 \
+    salad_status _s = (x);             \
+    if (_s != SALAD_OK) return _s;     \
+  } while (0)
+
+salad_status need(const void *ptr, const char *name) {
+  if (!ptr) return fail(SALAD_ERR_NULL, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(SALAD_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return SALAD_OK;
+}
+
+salad_status need_ws(void *ws, size_t ws_bytes, size_t needed) {
+  if (needed == 0) return SALAD_OK;
+  if (!ws) return fail(SALAD_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", needed);
+  if (!aligned16(ws)) return fail(SALAD_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < needed)
+    return fail(SALAD_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, needed);
+  return SALAD_OK;
+}
+
+View working_view(const Geom &g, const void *base) {
+  View v;
+  v.base = base;
+  v.sB = (long long)g.H * g.N * g.D;
+  v.sH = (long long)g.N * g.D;
+  v.sN = g.D;
+  v.perm = 0;
+  return v;
+}
+
+// Event pairs around the sparse-attention launch of salad_attn_forward.
+struct Profile {
+  int on = 0, used = 0;
+  hipEvent_t ev[2 * 4096];
+  int created = 0;
+} g_prof;
+
+hipError_t prof_mark(int which, hipStream_t st) {
+  if (!g_prof.on || g_prof.used >= 4096) return hipSuccess;
+  const int i = 2 * g_prof.used + which;
+  while (g_prof.created <= i) {
+    hipError_t e = hipEventCreate(&g_prof.ev[g_prof.created]);
+    if (e != hipSuccess) return e;
+    ++g_prof.created;
+  }
+  hipError_t e = hipEventRecord(g_prof.ev[i], st);
+  if (which == 1) ++g_prof.used;
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+salad_status salad_profile_enable(int on) {
+  g_prof.on = on != 0;
+  g_prof.used = 0;
+  return SALAD_OK;
+}
+
+salad_status salad_profile_read(int *calls, double *total_ms) {
+  if (!calls || !total_ms) return fail(SALAD_ERR_NULL, "calls / total_ms is NULL");
+  double tot = 0.0;
+  for (int i = 0; i < g_prof.used; ++i) {
+    hipError_t e = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_status(e, "salad_profile_read");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_status(e, "salad_profile_read");
+    tot += ms;
+  }
+  *calls = g_prof.used;
+  *total_ms = tot;
+  g_prof.used = 0;
+  return SALAD_OK;
+}
+
+salad_status salad_workspace_size(const salad_problem *p, size_t *bytes) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  if (!bytes) return fail(SALAD_ERR_NULL, "bytes is NULL");
+  *bytes = plan(inf).total_forward;
+  return SALAD_OK;
+}
+
+salad_status salad_permute(const salad_problem *p, int apply_rope, int inverse, const void *src,
+                           void *dst, hipStream_t stream) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  CHECK(need(src, "src"));
+  CHECK(need(dst, "dst"));
+  if (inverse && apply_rope) return fail(SALAD_ERR_SHAPE, "apply_rope needs inverse = 0");
+  if (apply_rope && !p->rope) return fail(SALAD_ERR_SHAPE, "apply_rope needs problem->rope = 1 (dims, base)");
+  if (src == dst) return fail(SALAD_ERR_SHAPE, "src and dst must not overlap");
+  return hip_status(launch_permute(inf.g, inf.bf16, apply_rope, inverse, src, dst, stream), "salad_permute");
+}
+
+salad_status salad_block_select(const salad_problem *p, const void *qw, const void *kw, int32_t *idx,
+                                double *qbar, double *kbar, void *ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  CHECK(need(qw, "qw"));
+  CHECK(need(kw, "kw"));
+  CHECK(need(idx, "idx"));
+  if (!inf.any_topk) return fail(SALAD_ERR_SHAPE, "no Top-K head in the problem");
+  const Geom &g = inf.g;
+  const size_t one = up(size_t(g.B) * g.H * g.nb * g.D * sizeof(double));
+  const size_t needed = (qbar ? 0 : one) + (kbar ? 0 : one);
+  CHECK(need_ws(ws, ws_bytes, needed));
+  if (qbar) CHECK(need(qbar, "qbar"));
+  if (kbar) CHECK(need(kbar, "kbar"));
+  char *w = (char *)ws;
+  double *qm = qbar ? qbar : (double *)w;
+  double *km = kbar ? kbar : (double *)(w + (qbar ? 0 : one));
+  return hip_status(launch_block_select(g, inf.bf16, working_view(g, qw), working_view(g, kw), qm, km,
+                                        idx, stream),
+                    "salad_block_select");
+}
+
+salad_status salad_sparse_attn(const salad_problem *p, const void *qw, const void *kw, const void *vw,
+                               const int32_t *idx, float *o_s, hipStream_t stream) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  CHECK(need(qw, "qw"));
+  CHECK(need(kw, "kw"));
+  CHECK(need(vw, "vw"));
+  CHECK(need(o_s, "o_s"));
+  if (inf.any_topk) CHECK(need(idx, "idx"));
+  const Geom &g = inf.g;
+  return hip_status(launch_sparse_attn(g, inf.bf16, working_view(g, qw), working_view(g, kw),
+                                       working_view(g, vw), idx, o_s, stream),
+                    "salad_sparse_attn");
+}
+
+salad_status salad_linear_state(const salad_problem *p, const void *kw, const void *vw, float *h,
+                                float *z, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  CHECK(need(kw, "kw"));
+  CHECK(need(vw, "vw"));
+  CHECK(need(h, "h"));
+  CHECK(need(z, "z"));
+  const Geom &g = inf.g;
+  const size_t needed = up(size_t(g.B) * g.H * linear_splits(g) * (size_t(g.D) * g.D + g.D) * sizeof(float));
+  CHECK(need_ws(ws, ws_bytes, needed));
+  return hip_status(launch_linear_state(g, inf.bf16, working_view(g, kw), working_view(g, vw),
+                                        (float *)ws, h, z, stream),
+                    "salad_linear_state");
+}
+
+salad_status salad_linear_apply(const salad_problem *p, const void *qw, const float *h, const float *z,
+                                float *o_l, hipStream_t stream) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  CHECK(need(qw, "qw"));
+  CHECK(need(h, "h"));
+  CHECK(need(z, "z"));
+  CHECK(need(o_l, "o_l"));
+  const Geom &g = inf.g;
+  return hip_status(launch_linear_apply(g, inf.bf16, working_view(g, qw), h, z, o_l, stream),
+                    "salad_linear_apply");
+}
+
+salad_status salad_gate(const salad_problem *p, const void *x, const void *w, float bias, float *s,
+                        void *ws, size_t ws_bytes, hipStream_t stream) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  CHECK(need(x, "x"));
+  CHECK(need(w, "w"));
+  CHECK(need(s, "s"));
+  const Geom &g = inf.g;
+  const size_t needed = up(size_t(g.B) * gate_splits(g) * g.H * g.D * sizeof(float));
+  CHECK(need_ws(ws, ws_bytes, needed));
+  return hip_status(launch_gate(g, inf.bf16, x, w, bias, (float *)ws, s, stream), "salad_gate");
+}
+
+salad_status salad_combine(const salad_problem *p, const float *o_s, const float *o_l, const void *w_p,
+                           const float *s, void *out, hipStream_t stream) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  CHECK(need(o_s, "o_s"));
+  CHECK(need(o_l, "o_l"));
+  CHECK(need(w_p, "w_p"));
+  CHECK(need(s, "s"));
+  CHECK(need(out, "out"));
+  return hip_status(launch_combine(inf.g, inf.bf16, o_s, o_l, w_p, s, out, stream), "salad_combine");
+}
+
+salad_status salad_attn_forward(const salad_problem *p, const void *q, const void *k, const void *v,
+                                const void *x, const void *w_p, const void *gate_w, float gate_b,
+                                const float *s_override, void *out, float *s_out, int32_t *idx_out,
+                                void *ws, size_t ws_bytes, hipStream_t stream) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  CHECK(need(q, "q"));
+  CHECK(need(k, "k"));
+  CHECK(need(v, "v"));
+  CHECK(need(w_p, "w_p"));
+  CHECK(need(out, "out"));
+  if (!s_override) {
+    CHECK(need(x, "x"));
+    CHECK(need(gate_w, "gate_w"));
+  } else {
+    CHECK(need(s_override, "s_override"));
+  }
+  if (s_out) CHECK(need(s_out, "s_out"));
+  if (idx_out) CHECK(need(idx_out, "idx_out"));
+  const Geom &g = inf.g;
+  const Plan pl = plan(inf);
+  CHECK(need_ws(ws, ws_bytes, pl.total_forward));
+  char *w = (char *)ws;
+  void *scratch = w;
+  void *wq = w + pl.wq, *wk = w + pl.wk, *wv = w + pl.wv;
+  int32_t *idx = idx_out ? idx_out : (int32_t *)(w + pl.idx);
+  float *o_s = (float *)(w + pl.o_s), *o_l = (float *)(w + pl.o_l);
+  float *hm = (float *)(w + pl.h), *zv = (float *)(w + pl.z);
+  float *s = s_out ? s_out : (float *)(w + pl.s);
+
+  hipError_t e;
+  if (s_override) {
+    if (s_out) {
+      e = hipMemcpyAsync(s_out, s_override, sizeof(float) * g.B, hipMemcpyDeviceToDevice, stream);
+      if (e != hipSuccess) return hip_status(e, "salad_attn_forward: copy s");
+    } else {
+      s = const_cast<float *>(s_override);
+    }
+  } else {
+    e = launch_gate(g, inf.bf16, x, gate_w, gate_b, (float *)scratch, s, stream);
+    if (e != hipSuccess) return hip_status(e, "salad_attn_forward: gate");
+  }
+  const int rope = p->rope;
+  if ((e = launch_permute(g, inf.bf16, rope, 0, q, wq, stream)) != hipSuccess ||
+      (e = launch_permute(g, inf.bf16, rope, 0, k, wk, stream)) != hipSuccess ||
+      (e = launch_permute(g, inf.bf16, 0, 0, v, wv, stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_forward: permute");
+  const View qv = working_view(g, wq), kv = working_view(g, wk), vv = working_view(g, wv);
+  if (inf.any_topk) {
+    const size_t one = up(size_t(g.B) * g.H * g.nb * g.D * sizeof(double));
+    e = launch_block_select(g, inf.bf16, qv, kv, (double *)scratch, (double *)(w + one), idx, stream);
+    if (e != hipSuccess) return hip_status(e, "salad_attn_forward: block select");
+  }
+  if ((e = prof_mark(0, stream)) != hipSuccess ||
+      (e = launch_sparse_attn(g, inf.bf16, qv, kv, vv, idx, o_s, stream)) != hipSuccess ||
+      (e = prof_mark(1, stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_forward: sparse attention");
+  if ((e = launch_linear_state(g, inf.bf16, kv, vv, (float *)scratch, hm, zv, stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_forward: linear state");
+  if ((e = launch_linear_apply(g, inf.bf16, qv, hm, zv, o_l, stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_forward: linear apply");
+  if ((e = launch_combine(g, inf.bf16, o_s, o_l, w_p, s, out, stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_forward: combine");
+  return SALAD_OK;
+}
+
+const char *salad_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Device-side helpers shared by the gfx950 kernels of the hybrid attention
+// library: storage-type conversion, tensor views with the head-wise token
+// order, and the launch geometry of one layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace salad {
+
+typedef uint16_t bf16_t;  // bfloat16 bits
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kMaxHeads = 256;
+
+// ---- storage-type conversion --------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(uint32_t(h) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+// float64 -> bfloat16 with a single rounding (nearest even).  Rounding to
+// float32 first would round twice.  The integer add carries into the
+// exponent exactly like the float32 trick above, here at bit 45 of the
+// float64 pattern; results outside bf16's normal range fall back to the
+// float32 route, whose extra rounding only matters there.
+__device__ __forceinline__ bf16_t f64_to_bf16(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  uint64_t mag = u & 0x7fffffffffffffffull;
+  int e = int(mag >> 52);
+  // bf16 normal range: unbiased exponent in [-126, 127], i.e. e in [897, 1150]
+  if (e < 897 || e > 1150) {
+    if (mag == 0) return bf16_t((u >> 48) & 0x8000u);
+    return f32_to_bf16(float(x));
+  }
+  uint64_t r = (mag + ((1ull << 44) - 1) + ((mag >> 45) & 1ull)) >> 45;  // 11-bit exp, 7-bit mant
+  int e2 = int(r >> 7);
+  if (e2 > 1150) return bf16_t(((u >> 48) & 0x8000u) | 0x7f80u);       // rounded up to inf
+  uint32_t out = uint32_t((e2 - 1023 + 127) << 7) | uint32_t(r & 0x7f);
+  return bf16_t(((u >> 48) & 0x8000u) | out);
+}
+
+template <typename T> struct io;
+template <> struct io<float> {
+  static __device__ __forceinline__ float ld(const float *p) { return *p; }
+  static __device__ __forceinline__ void st(float *p, float v) { *p = v; }
+  static __device__ __forceinline__ float from_f64(double v) { return float(v); }
+};
+template <> struct io<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t *p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void st(bf16_t *p, float v) { *p = f32_to_bf16(v); }
+  static __device__ __forceinline__ bf16_t from_f64(double v) { return f64_to_bf16(v); }
+};
+
+// ---- geometry ------------------------------------------------------------
+
+// Per-layer geometry passed by value to every kernel.
+struct Geom {
+  int B, H, D, N;
+  int F, Hg, Wg;
+  uint64_t temporal[4];  // bit h: head h is temporal (spatial-major order)
+  uint64_t topk[4];      // bit h: head h is Top-K
+  int r;                 // window radius
+  int block, k, nb;      // Top-K block size, kept blocks, number of blocks
+  float scale;           // softmax scale
+  float eps;             // linear denominator guard
+  int rope_dims[3];
+  float rope_base;
+};
+
+__device__ __forceinline__ bool bit(const uint64_t *m, int h) {
+  return (m[h >> 6] >> (h & 63)) & 1ull;
+}
+
+// Working position p of a temporal head holds this token.
+__device__ __forceinline__ int st_token(const Geom &g, int p) {
+  return (p % g.F) * (g.Hg * g.Wg) + p / g.F;
+}
+// ... and token n sits at this working position.
+__device__ __forceinline__ int st_position(const Geom &g, int n) {
+  int S = g.Hg * g.Wg;
+  return (n % S) * g.F + n / S;
+}
+
+// Row addressing of a [B, *, *, d] tensor.  Element offset of (b, h, row)
+// is b*sB + h*sH + row*sN; when `perm` is set, working row p of a temporal
+// head is read from token st_token(p) (boundary layout gathered on load).
+struct View {
+  const void *base;
+  long long sB, sH, sN;
+  int perm;
+};
+
+__device__ __forceinline__ long long row_offset(const Geom &g, const View &v, int b, int h, int p) {
+  int tok = (v.perm && bit(g.temporal, h)) ? st_token(g, p) : p;
+  return (long long)b * v.sB + (long long)h * v.sH + (long long)tok * v.sN;
+}
+
+// RoPE angle for pair i of an axis segment of D dims at integer position
+// pos: pos * base^(-2i/D), in float64.
+__device__ __forceinline__ void rope_cs(int pos, int i, int D, double base, double *c, double *s) {
+  double theta = pow(base, -2.0 * double(i) / double(D));
+  sincos(double(pos) * theta, s, c);
+}
+
+}  // namespace salad

@@ -1,0 +1,154 @@
+// Gate s = sigmoid(w . mean_n X[n,:] + b) and the combine
+// out = O_s + s * (O_l W_p) scattered back to token order.
+//
+// Sources: SALAD structured summary (paper.rainbus.top/paper/2601.16515),
+// method steps 4 (zero-initialised projection of the linear output),
+// 5 (scalar gate in (0,1)) and 6 (residual sum); ijyty.com/news/870645
+// section 2.3 and news.axiwang.com section 六 (token average, then a linear
+// layer and a sigmoid).
+//
+// Both are HBM-bound.  The gate reads X once: per sample, 256 row chunks
+// write fp32 column sums to the workspace and one workgroup finishes the
+// mean, the dot product (fp64) and the sigmoid -- a fixed summation order.
+#include "common.h"
+#include "kernels.h"
+
+namespace salad {
+
+// Column sums of X[b, rows of chunk s, :].  Grid (splits, B); thread t owns
+// 8-column groups t, t+256, ...
+template <typename T>
+__global__ void __launch_bounds__(256) gate_partial_kernel(Geom g, const T *__restrict__ x,
+                                                           float *__restrict__ partial, int splits) {
+  const int s = blockIdx.x, b = blockIdx.y, C = g.H * g.D;
+  const int rows = (g.N + splits - 1) / splits;
+  const int n0 = s * rows, n1 = min(g.N, n0 + rows);
+  constexpr int VEC = 8;
+  for (int cg = threadIdx.x; cg * VEC < C; cg += 256) {
+    float acc[VEC] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int n = n0; n < n1; ++n) {
+      const T *src = x + ((long long)b * g.N + n) * C + cg * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += io<T>::ld(src + e);
+    }
+    float *dst = partial + ((long long)b * splits + s) * C + cg * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dst[e] = acc[e];
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) gate_final_kernel(Geom g, const float *__restrict__ partial,
+                                                         int splits, const T *__restrict__ w, float bias,
+                                                         float *__restrict__ s_out) {
+  const int b = blockIdx.x, C = g.H * g.D;
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int c = threadIdx.x; c < C; c += 256) {
+    double col = 0.0;
+    for (int s = 0; s < splits; ++s) col += double(partial[((long long)b * splits + s) * C + c]);
+    acc += double(io<T>::ld(w + c)) * (col / double(g.N));
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double t = red[0] + double(bias);
+    s_out[b] = float(1.0 / (1.0 + exp(-t)));
+  }
+}
+
+hipError_t launch_gate(const Geom &g, int bf16, const void *x, const void *w, float bias,
+                       float *partial, float *s, hipStream_t st) {
+  const int splits = gate_splits(g);
+  dim3 grid(splits, g.B);
+  if (bf16) {
+    gate_partial_kernel<bf16_t><<<grid, 256, 0, st>>>(g, (const bf16_t *)x, partial, splits);
+    gate_final_kernel<bf16_t><<<g.B, 256, 0, st>>>(g, partial, splits, (const bf16_t *)w, bias, s);
+  } else {
+    gate_partial_kernel<float><<<grid, 256, 0, st>>>(g, (const float *)x, partial, splits);
+    gate_final_kernel<float><<<g.B, 256, 0, st>>>(g, partial, splits, (const float *)w, bias, s);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Combine.  Grid (ceil(N/64), B*H); 64 working rows per workgroup; thread t
+// computes rows 4*(t/16)..+3 and columns (t%16) + 16*m of O_l W_p (fp32),
+// then out[b, pi(p), h, :] = o_s + s * that, in the storage type.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) combine_kernel(Geom g, const float *__restrict__ o_s,
+                                                      const float *__restrict__ o_l,
+                                                      const T *__restrict__ w_p,
+                                                      const float *__restrict__ s,
+                                                      T *__restrict__ out) {
+  extern __shared__ float smem[];
+  float *Wp = smem;            // [D][D]
+  float *Ol = smem + D * D;    // [64][D + 1]
+  constexpr int NC = D / 16, LD = D + 1;
+  const int bh = blockIdx.y, h = bh % g.H, b = bh / g.H;
+  const int p0 = blockIdx.x * 64, t = threadIdx.x;
+  for (int e = t; e < D * D; e += 256) Wp[e] = io<T>::ld(w_p + e);
+  for (int e = t; e < 64 * D; e += 256) {
+    const int r = e / D, c = e % D, p = p0 + r;
+    Ol[r * LD + c] = p < g.N ? o_l[((long long)bh * g.N + p) * D + c] : 0.f;
+  }
+  __syncthreads();
+  const int rg = t >> 4, cg = t & 15;
+  float acc[4][NC];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int m = 0; m < NC; ++m) acc[a][m] = 0.f;
+  for (int i = 0; i < D; ++i) {
+    float ol[4], wv[NC];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) ol[a] = Ol[(4 * rg + a) * LD + i];
+#pragma unroll
+    for (int m = 0; m < NC; ++m) wv[m] = Wp[i * D + cg + 16 * m];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int m = 0; m < NC; ++m) acc[a][m] = fmaf(ol[a], wv[m], acc[a][m]);
+  }
+  const float sb = s[b];
+  const bool temporal = bit(g.temporal, h);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int p = p0 + 4 * rg + a;
+    if (p >= g.N) continue;
+    const int tok = temporal ? st_token(g, p) : p;
+    const float *os = o_s + ((long long)bh * g.N + p) * D;
+    T *dst = out + (((long long)b * g.N + tok) * g.H + h) * D;
+#pragma unroll
+    for (int m = 0; m < NC; ++m) {
+      const int c = cg + 16 * m;
+      io<T>::st(dst + c, os[c] + sb * acc[a][m]);
+    }
+  }
+}
+
+hipError_t launch_combine(const Geom &g, int bf16, const float *o_s, const float *o_l,
+                          const void *w_p, const float *s, void *out, hipStream_t st) {
+  dim3 grid((g.N + 63) / 64, g.B * g.H);
+  const size_t lds = (size_t(g.D) * g.D + 64 * (g.D + 1)) * sizeof(float);
+#define SALAD_COMBINE(T, DD)                                                                 \
+  do {                                                                                       \
+    hipFuncSetAttribute((const void *)combine_kernel<T, DD>,                                 \
+                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));               \
+    combine_kernel<T, DD><<<grid, 256, lds, st>>>(g, o_s, o_l, (const T *)w_p, s, (T *)out); \
+  } while (0)
+  if (bf16) {
+    if (g.D == 128) SALAD_COMBINE(bf16_t, 128); else SALAD_COMBINE(bf16_t, 64);
+  } else {
+    if (g.D == 128) SALAD_COMBINE(float, 128); else SALAD_COMBINE(float, 64);
+  }
+#undef SALAD_COMBINE
+  return hipGetLastError();
+}
+
+}  // namespace salad

@@ -1,0 +1,49 @@
+// Host-side launchers of the gfx950 kernels (one per stage of the layer).
+// Every launcher enqueues on `st` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace salad {
+
+// Query blocks scored per workgroup by the Top-K selection kernel (bounded
+// by its LDS use: qpb * (d + nb) doubles).
+inline int topk_queries_per_group(int nb, int d) {
+  int q = int((64 * 1024) / (size_t(d + nb) * sizeof(double)));
+  return q < 1 ? 1 : (q > 8 ? 8 : q);
+}
+
+// Token chunks per (b, h) used by the split-N linear-state reduction.
+inline int linear_splits(const Geom &g) {
+  int chunks = (g.N + 127) / 128;
+  int want = (512 + g.B * g.H - 1) / (g.B * g.H);
+  return want < 1 ? 1 : (want > chunks ? chunks : want);
+}
+
+// Row chunks per sample used by the gate's token mean.
+inline int gate_splits(const Geom &g) {
+  int want = 256;
+  return want > g.N ? g.N : want;
+}
+
+hipError_t launch_permute(const Geom &g, int bf16, int rope, int inverse, const void *src,
+                          void *dst, hipStream_t st);
+hipError_t launch_block_select(const Geom &g, int bf16, View qv, View kv, double *qbar,
+                               double *kbar, int32_t *idx, hipStream_t st);
+// partial: [B*H][S][D*D + D] floats of workspace (S = linear_splits).
+hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float *partial,
+                               float *h, float *z, hipStream_t st);
+hipError_t launch_linear_apply(const Geom &g, int bf16, View qv, const float *h, const float *z,
+                               float *o_l, hipStream_t st);
+// partial: [B][gate_splits][C] floats of workspace.
+hipError_t launch_gate(const Geom &g, int bf16, const void *x, const void *w, float bias,
+                       float *partial, float *s, hipStream_t st);
+hipError_t launch_combine(const Geom &g, int bf16, const float *o_s, const float *o_l,
+                          const void *w_p, const float *s, void *out, hipStream_t st);
+hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv,
+                              const int32_t *idx, float *o_s, hipStream_t st);
+
+}  // namespace salad

@@ -1,0 +1,91 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before touching the GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_linear_hybrid_st_amd as S
+from sparse_linear_hybrid_st_amd import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "salad.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:salad_status|const char \*)\s*(salad_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_exported_set():
+    assert _declared() == sorted(S.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = S.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(salad_\w+)$", out, re.M))
+    for name in _declared():
+        assert hasattr(lib, name)
+        assert name in exported, name
+
+
+def _status(p):
+    n = ctypes.c_size_t(0)
+    return S.lib().salad_workspace_size(ctypes.byref(p), ctypes.byref(n)), n.value
+
+
+def test_workspace_size_of_workloads():
+    for w in configs.all_workloads().values():
+        st, n = _status(S.problem_from_workload(w))
+        assert st == 0 and n > 0, (w.name, S.lib().salad_last_error())
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, 2), ("n_heads", 0, 2), ("n_heads", 257, 2), ("head_dim", 96, 3),
+    ("grid_f", 0, 2), ("io_dtype", 7, 2), ("window_radius", -1, 2),
+])
+def test_bad_problem_is_rejected(field, value, code):
+    p = S.problem_from_workload(configs.swa_480p())
+    setattr(p, field, value)
+    st, _ = _status(p)
+    assert st == code, S.lib().salad_last_error()
+    assert S.lib().salad_last_error()
+
+
+def test_bad_topk_and_rope_and_kind():
+    p = S.problem_from_workload(configs.topk_480p())
+    p.topk = p.n_blocks + 1
+    assert _status(p)[0] == 2
+    p = S.problem_from_workload(configs.topk_480p())
+    p.block = 32                     # bf16 Top-K kernels use 64-row blocks
+    assert _status(p)[0] == 3
+    p = S.problem_from_workload(configs.cfg_rope_480p())
+    p.rope_dims[0] = 43
+    assert _status(p)[0] == 2
+    p = S.problem_from_workload(configs.swa_480p())
+    p.head_kind[3] = 9
+    assert _status(p)[0] == 2
+    p = S.problem_from_workload(configs.tiny_f32())
+    p.io_dtype = S.SALAD_BF16          # bf16 needs d = 128
+    assert _status(p)[0] == 3
+
+
+def test_null_and_misaligned_pointers_fail_before_launch():
+    L = S.lib()
+    p = S.problem_from_workload(configs.tiny_f32())
+    assert L.salad_permute(ctypes.byref(p), 0, 0, None, None, None) == 1
+    odd = ctypes.c_void_p(0x1008)
+    assert L.salad_permute(ctypes.byref(p), 0, 0, odd, ctypes.c_void_p(0x2000), None) == 4
+    assert L.salad_permute(ctypes.byref(p), 1, 1, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), None) == 2
+    a = ctypes.c_void_p(0x10000)
+    # workspace too small / missing
+    assert L.salad_gate(ctypes.byref(p), a, a, 0.0, a, None, 0, None) == 5
+    assert L.salad_gate(ctypes.byref(p), a, a, 0.0, a, a, 16, None) == 5
+    assert L.salad_attn_forward(ctypes.byref(p), a, a, a, a, a, a, 0.0, None, a, None, None,
+                                a, 16, None) == 5
+    assert b"workspace" in L.salad_last_error()
+    assert L.salad_workspace_size(None, None) == 1
