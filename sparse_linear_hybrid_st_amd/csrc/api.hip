@@ -129,7 +129,7 @@ Plan plan(const Info &inf) {
   const size_t rows = BH * g.N;
   const size_t means = inf.any_topk ? 2 * up(BH * g.nb * g.D * sizeof(double)) : 0;
   const size_t lin = up(BH * linear_splits(g) * (size_t(g.D) * g.D + g.D) * sizeof(float));
-  const size_t gate = up(size_t(g.B) * gate_splits(g) * g.H * g.D * sizeof(float));
+  const size_t gate = up(gate_ws_bytes(g));
   pl.means = 0;
   pl.lin_partial = 0;
   pl.gate_partial = 0;
@@ -322,7 +322,7 @@ salad_status salad_gate(const salad_problem *p, const void *x, const void *w, fl
   CHECK(need(w, "w"));
   CHECK(need(s, "s"));
   const Geom &g = inf.g;
-  const size_t needed = up(size_t(g.B) * gate_splits(g) * g.H * g.D * sizeof(float));
+  const size_t needed = up(gate_ws_bytes(g));
   CHECK(need_ws(ws, ws_bytes, needed));
   return hip_status(launch_gate(g, inf.bf16, x, w, bias, (float *)ws, s, stream), "salad_gate");
 }

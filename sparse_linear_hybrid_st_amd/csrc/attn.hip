@@ -93,11 +93,18 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(Geom g, View qv, View kv, 
 constexpr int kD = 128;   // head dim
 constexpr int kBN = 64;   // keys per tile
 
-// K tile: row = key (256 B), 16-byte unit u of row j stored at u ^ (j & 15).
-__device__ __forceinline__ int k_unit(int j, int u) { return u ^ (j & 15); }
-// V^T tile: row = feature (128 B = 16 granules of 4 keys); granule G of row
-// rho stored at G ^ (((rho >> 1) ^ (rho >> 3)) & 15).
-__device__ __forceinline__ int v_gran(int rho, int G) { return G ^ (((rho >> 1) ^ (rho >> 3)) & 15); }
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// K and V tiles are stored row-major ([key][d], 256-byte rows) in LDS.  The
+// 16-byte unit u of row j sits at u ^ kv_swz(j).  kv_swz is a bijection on
+// the low 4 bits of j that swaps its two 2-bit halves, so
+//   * the K operand reads (16 consecutive keys, one unit) hit 16 distinct
+//     units, and
+//   * the transposing V reads (4 consecutive keys x one 64-byte segment)
+//     hit 4 distinct segments.
+__device__ __forceinline__ int kv_swz(int j) { return ((j & 3) << 2) | ((j >> 2) & 3); }
 
 struct AttnArgs {
   Geom g;
@@ -108,18 +115,34 @@ struct AttnArgs {
   int n_heads_sel;       // heads handled by this launch
   uint8_t heads[kMaxHeads];
   int tiles_per_head;    // query tiles per (b, head)
+  int n_blocks;          // grid size (for the XCD-aware order)
 };
 
+// Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
+// that each XCD walks a contiguous range of query tiles (neighbouring tiles
+// share most of their key window, which then stays in that XCD's L2).
+__device__ __forceinline__ int xcd_order(int bid, int T) {
+  const int q = T >> 3, r = T & 7, x = bid & 7, k = bid >> 3;
+  return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
 template <int NW>
-__global__ void __launch_bounds__(NW * 64) attn_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   constexpr int BM = NW * 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kBN * kD];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[kD * kBN];
+  constexpr int TILE = kBN * kD;                 // elements per K or V tile
+  constexpr int DMA_PER_WAVE = (TILE * 2 / 1024) / NW;  // 1-KB DMA ops per tensor per wave
+  // Two named buffers per tensor (not one indexed array): with distinct LDS
+  // objects the compiler can tell that the DMA into one buffer does not
+  // feed the reads of the other, so it does not wait for the next tile's
+  // DMA before computing on the current one.
+  __shared__ __attribute__((aligned(1024))) bf16_t K0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t K1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t V0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t V1[TILE];
   const Geom &g = a.g;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, hl = lane >> 5, l32 = lane & 31;
 
-  // tile -> (b, head, query tile)
-  const int tile = blockIdx.x;
+  const int tile = xcd_order(blockIdx.x, a.n_blocks);
   const int qt = tile % a.tiles_per_head;
   const int bhs = tile / a.tiles_per_head;
   const int h = a.heads[bhs % a.n_heads_sel];
@@ -131,7 +154,8 @@ __global__ void __launch_bounds__(NW * 64) attn_bf16_kernel(AttnArgs a) {
   const bf16_t *kbase = (const bf16_t *)a.k.base;
   const bf16_t *vbase = (const bf16_t *)a.v.base;
 
-  // this wave's queries as B operands: lane -> query q0 + 32w + l32, features 16ks + 8hl + e
+  // this wave's queries as MFMA B operands: lane -> query q0 + 32w + l32,
+  // features 16ks + 8hl + e
   const int pq = q0 + 32 * w + l32;
   bf16x8 qf[8];
   {
@@ -140,7 +164,6 @@ __global__ void __launch_bounds__(NW * 64) attn_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8 *)(qbase + off + (2 * ks + hl) * 8);
   }
 
-  // key tile range
   int n_tiles, kt_first = 0;
   const int32_t *sel = nullptr;
   if (a.topk_mode) {
@@ -152,168 +175,168 @@ __global__ void __launch_bounds__(NW * 64) attn_bf16_kernel(AttnArgs a) {
     kt_first = lo / kBN;
     n_tiles = hi / kBN - kt_first + 1;
   }
-  // wave's own query range (for skipping and mask-free tiles)
   const int wq_lo = q0 + 32 * w, wq_hi = min(q0 + 32 * w + 31, g.N - 1);
 
-  const float sl2 = g.scale * 1.4426950408889634f;  // scale * log2(e)
-  f32x16 o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // loader mapping (per thread): K: units (row, u) over 64 x 16; V: 4-key
-  // groups kq x feature chunk c over 16 x 16.
-  constexpr int KLOADS = (kBN * 16) / (NW * 64);
-  constexpr int VLOADS = (16 * 16) / (NW * 64);
-  u32x4 kreg[KLOADS];
-  u32x4 vreg[VLOADS][4];
-
-  // first key row of tile `it`; an out-of-range block index (only possible
-  // if idx was not produced by the selection) maps past the end, where
-  // every row is zero-filled and masked
+  // First key row of tile `it`.  An out-of-range block index (only possible
+  // if idx was not produced by the selection) maps past the end, where every
+  // row is masked.
   auto tile_start = [&](int it) -> int {
     if (!a.topk_mode) return (kt_first + it) * kBN;
     const int kb = sel[it];
     return (kb >= 0 && kb < g.nb) ? kb * g.block : g.N;
   };
-  auto load_tile = [&](int k0) {
+  // DMA one K and one V tile into buffer `buf`: op i of wave w fills LDS
+  // rows 4*(i*NW + w) .. +3; lane l writes physical unit l%16 of row l/16,
+  // so it fetches logical unit (l%16) ^ kv_swz(row).  Rows past N re-read
+  // row N-1 (finite data; those keys are masked).
+  auto issue_tile = [&](int k0, bf16_t *__restrict__ Kd, bf16_t *__restrict__ Vd) {
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int e = t + i * NW * 64;
-      const int row = e >> 4, u = e & 15;
-      const int j = k0 + row;
-      kreg[i] = j < g.N ? *(const u32x4 *)(kbase + row_offset(g, a.k, b, h, j) + u * 8)
-                        : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int e = t + i * NW * 64;
-      const int c = e & 15, kq = e >> 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = k0 + kq * 4 + r;
-        vreg[i][r] = j < g.N ? *(const u32x4 *)(vbase + row_offset(g, a.v, b, h, j) + c * 8)
-                             : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int e = t + i * NW * 64;
-      const int row = e >> 4, u = e & 15;
-      *(u32x4 *)(Ks + row * kD + k_unit(row, u) * 8) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int e = t + i * NW * 64;
-      const int c = e & 15, kq = e >> 4;
-      // feature c*8 + f for keys 4kq .. 4kq+3 -> one 8-byte granule
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const int word = f >> 1, sh = (f & 1) * 16;
-        const uint32_t k0v = (vreg[i][0][word] >> sh) & 0xffffu;
-        const uint32_t k1v = (vreg[i][1][word] >> sh) & 0xffffu;
-        const uint32_t k2v = (vreg[i][2][word] >> sh) & 0xffffu;
-        const uint32_t k3v = (vreg[i][3][word] >> sh) & 0xffffu;
-        const int rho = c * 8 + f;
-        u32x2 gv = {k0v | (k1v << 16), k2v | (k3v << 16)};
-        *(u32x2 *)(Vt + rho * kBN + v_gran(rho, kq) * 4) = gv;
-      }
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int row = 4 * (i * NW + w) + (lane >> 4);
+      const int u = (lane & 15) ^ kv_swz(row);
+      const int j = min(k0 + row, g.N - 1);
+      lds_void *kd = (lds_void *)(Kd + (4 * (i * NW + w)) * kD);
+      lds_void *vd = (lds_void *)(Vd + (4 * (i * NW + w)) * kD);
+      __builtin_amdgcn_global_load_lds((const void *)(kbase + row_offset(g, a.k, b, h, j) + u * 8), kd, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(vbase + row_offset(g, a.v, b, h, j) + u * 8), vd, 16, 0, 0);
     }
   };
 
-  if (n_tiles > 0) load_tile(tile_start(0));
-  for (int it = 0; it < n_tiles; ++it) {
-    const int k0 = tile_start(it);
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (it + 1 < n_tiles) load_tile(tile_start(it + 1));
+  // Lane-constant LDS element offsets.  K operand (row kb*32 + l32, logical
+  // unit 2ks + hl): the swizzle key depends on l32 only, so unit
+  // (2ks + hl) ^ swz = 2 (ks ^ (swz >> 1)) + (hl ^ (swz & 1)).
+  const int kswz = kv_swz(l32);
+  const int k_lane = l32 * kD + 8 * (hl ^ (kswz & 1));
+  const int k_x = kswz >> 1;
+  // V^T operand, transposing read r of d-block db for k-step kk:
+  // row = 32*(kk/2) + 16*(kk%2) + 8r + 4hl + jl/4 and
+  // d = 32db + 16*(gq%2) + 4*(jl%4); its swizzle key depends on (lane, r).
+  const int gq = lane >> 4, jl = lane & 15;
+  int v_off[2][4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int row = 8 * r + 4 * hl + (jl >> 2);
+      const int d = 32 * db + 16 * (gq & 1) + 4 * (jl & 3);
+      v_off[r][db] = row * kD + (((d >> 3) ^ kv_swz(row)) << 3) + (d & 4);
+    }
 
-    // does this wave have any kept pair in this tile?
+  const float c2 = g.scale * 1.4426950408889634f;  // softmax scale * log2(e)
+  f32x16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;  // running max (raw score units), partial row sum
+
+  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto compute = [&](int k0, const bf16_t *__restrict__ Ks, const bf16_t *__restrict__ Vs) {
     const int k1 = min(k0 + kBN, g.N) - 1;
     bool any, full;
     if (a.topk_mode) {
-      any = true;
+      any = k0 < g.N;
       full = (k0 + kBN) <= g.N;
     } else {
       any = (k0 <= wq_hi + g.r) && (k1 >= wq_lo - g.r) && (wq_lo <= wq_hi);
       full = (k0 + kBN <= g.N) && (k0 >= wq_hi - g.r) && (k0 + kBN - 1 <= wq_lo + g.r);
     }
-    if (!any) continue;
-
-    // S^T[key][query] for 2 blocks of 32 keys
-    f32x16 s[2];
+    if (!any) return;
+    // S^T[key][query] = K Q^T, two blocks of 32 keys
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const int row = kb * 32 + l32;
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 ka = *(const bf16x8 *)(Ks + row * kD + k_unit(row, 2 * ks + hl) * 8);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 ka = *(const bf16x8 *)(Ks + kb * 32 * kD + k_lane + 16 * (ks ^ k_x));
         s[kb] = mfma_32x32x16(ka, qf[ks], s[kb]);
       }
-    }
-    // scale to log2 units, mask
     float mx = -INFINITY;
+    if (full) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[kb][r] * sl2;
-        if (!full) {
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
           const int j = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
           const bool keep = j < g.N && (a.topk_mode || abs(pq - j) <= g.r);
-          v = keep ? v : -INFINITY;
+          s[kb][r] = keep ? s[kb][r] : -INFINITY;
+          mx = fmaxf(mx, s[kb][r]);
         }
-        s[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
+    // rescale only when some lane's max moved (the common case late in a row is no change)
+    if (__any(m_new > m_run)) {
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float moff = m_run == -INFINITY ? 0.f : m_run * c2;
     bf16x8 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        uint16_t tmp[8];
+        bf16x8 pv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = exp2f(s[kb][8 * half + e] - m_use);
-          psum += pv;
-          tmp[e] = f32_to_bf16(pv);
+          // v_exp_f32 directly: arguments are <= 0, tiny results flush to 0
+          const float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e], c2, -moff));
+          l_run += pe;
+          pv[e] = (__bf16)pe;
         }
-        pb[2 * kb + half] = *(const bf16x8 *)tmp;
+        pb[2 * kb + half] = pv;
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    // O^T[d][q] += V^T[d][keys] P^T[keys][q]; k-step kk covers, for half hl,
-    // keys 32*(kk/2) + 8*(2*(kk%2) + e/4) + 4*hl + e%4 (e = 0..7)
+    // O^T[d][q] += V^T[d][keys] P^T[keys][q].  k-step kk, half hl, element
+    // e = 4r + e' covers key 32*(kk/2) + 8*(2*(kk%2) + r) + 4*hl + e'; the
+    // matching V^T operand comes from two transposing reads (r = 0, 1).
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int kb = kk >> 1, k2 = kk & 1;
-      const int G0 = (kb * 32 + 8 * (2 * k2) + 4 * hl) >> 2;
-      const int G1 = (kb * 32 + 8 * (2 * k2 + 1) + 4 * hl) >> 2;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int rho = 32 * db + l32;
-        const u32x2 lo = *(const u32x2 *)(Vt + rho * kBN + v_gran(rho, G0) * 4);
-        const u32x2 hi = *(const u32x2 *)(Vt + rho * kBN + v_gran(rho, G1) * 4);
-        u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+        s16x4 part[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4 *)(Vs + 16 * kk * kD + v_off[r][db]));
+        typedef __attribute__((ext_vector_type(8))) short s16x8;
+        s16x8 va = {part[0][0], part[0][1], part[0][2], part[0][3],
+                    part[1][0], part[1][1], part[1][2], part[1][3]};
         o[db] = mfma_32x32x16(*(const bf16x8 *)&va, pb[kk], o[db]);
       }
     }
+  };
+
+  // Double-buffered tile loop, unrolled by two so each half names its
+  // buffers statically.  Before computing tile it: wait for this wave's DMA
+  // of tile it (vmcnt 0), barrier (every wave's DMA landed and every wave is
+  // done with the other buffer), then start the DMA of tile it+1.
+  // Tile starts are read before each DMA is issued and carried along, so no
+  // global load (and its wait) sits between a DMA and the LDS reads.
+  int k_cur = n_tiles > 0 ? tile_start(0) : 0;
+  if (n_tiles > 0) issue_tile(k_cur, K0, V0);
+  for (int it = 0; it < n_tiles; it += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    const int k_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
+    if (it + 1 < n_tiles) issue_tile(k_nxt, K1, V1);
+    compute(k_cur, K0, V0);
+    if (it + 1 >= n_tiles) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    const int k_nn = it + 2 < n_tiles ? tile_start(it + 2) : 0;
+    if (it + 2 < n_tiles) issue_tile(k_nn, K0, V0);
+    compute(k_nxt, K1, V1);
+    k_cur = k_nn;
   }
 
-  // finish: l over both half-waves, divide, store fp32 working rows
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (pq >= g.N) return;
   const float inv = 1.f / l_tot;
@@ -356,6 +379,7 @@ hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv
     const int BM = mode ? 64 : 128;
     a.tiles_per_head = (g.N + BM - 1) / BM;
     const unsigned grid = unsigned(a.tiles_per_head) * a.n_heads_sel * g.B;
+    a.n_blocks = int(grid);
     if (mode)
       attn_bf16_kernel<2><<<grid, 128, 0, st>>>(a);
     else

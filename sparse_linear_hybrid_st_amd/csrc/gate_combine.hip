@@ -7,71 +7,87 @@
 // section 2.3 and news.axiwang.com section 六 (token average, then a linear
 // layer and a sigmoid).
 //
-// Both are HBM-bound.  The gate reads X once: per sample, 256 row chunks
-// write fp32 column sums to the workspace and one workgroup finishes the
-// mean, the dot product (fp64) and the sigmoid -- a fixed summation order.
+// Both are HBM-bound.  The gate reads X once: per sample, row chunks write
+// fp32 column sums to the workspace, 256-column blocks finish the means and
+// their dot product with w (fp64), and one thread per sample adds the block
+// results and applies the sigmoid -- a fixed summation order throughout.
 #include "common.h"
 #include "kernels.h"
 
 namespace salad {
 
 // Column sums of X[b, rows of chunk s, :].  Grid (splits, B); thread t owns
-// 8-column groups t, t+256, ...
+// 8-column groups t, t+256, ... and reads them with one 16-byte load per row.
 template <typename T>
 __global__ void __launch_bounds__(256) gate_partial_kernel(Geom g, const T *__restrict__ x,
                                                            float *__restrict__ partial, int splits) {
   const int s = blockIdx.x, b = blockIdx.y, C = g.H * g.D;
   const int rows = (g.N + splits - 1) / splits;
   const int n0 = s * rows, n1 = min(g.N, n0 + rows);
-  constexpr int VEC = 8;
-  for (int cg = threadIdx.x; cg * VEC < C; cg += 256) {
-    float acc[VEC] = {0, 0, 0, 0, 0, 0, 0, 0};
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  for (int cg = threadIdx.x; cg * 8 < C; cg += 256) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int n = n0; n < n1; ++n) {
-      const T *src = x + ((long long)b * g.N + n) * C + cg * VEC;
+      const T *src = x + ((long long)b * g.N + n) * C + cg * 8;
+      T v[8];
+      *(u32x4 *)v = *(const u32x4 *)src;
+      if (sizeof(T) == 4) *(u32x4 *)(v + 4) = *(const u32x4 *)(src + 4);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += io<T>::ld(src + e);
+      for (int e = 0; e < 8; ++e) acc[e] += io<T>::ld(v + e);
     }
-    float *dst = partial + ((long long)b * splits + s) * C + cg * VEC;
+    float *dst = partial + ((long long)b * splits + s) * C + cg * 8;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) dst[e] = acc[e];
+    for (int e = 0; e < 8; ++e) dst[e] = acc[e];
   }
 }
 
+// Column means and their dot product with w, per 256-column block (fp64,
+// fixed-order tree): dots[b][blk].
 template <typename T>
-__global__ void __launch_bounds__(256) gate_final_kernel(Geom g, const float *__restrict__ partial,
-                                                         int splits, const T *__restrict__ w, float bias,
-                                                         float *__restrict__ s_out) {
-  const int b = blockIdx.x, C = g.H * g.D;
+__global__ void __launch_bounds__(256) gate_dot_kernel(Geom g, const float *__restrict__ partial,
+                                                       int splits, const T *__restrict__ w,
+                                                       double *__restrict__ dots) {
+  const int blk = blockIdx.x, b = blockIdx.y, C = g.H * g.D;
+  const int c = blk * 256 + threadIdx.x;
   __shared__ double red[256];
-  double acc = 0.0;
-  for (int c = threadIdx.x; c < C; c += 256) {
+  double v = 0.0;
+  if (c < C) {
     double col = 0.0;
     for (int s = 0; s < splits; ++s) col += double(partial[((long long)b * splits + s) * C + c]);
-    acc += double(io<T>::ld(w + c)) * (col / double(g.N));
+    v = double(io<T>::ld(w + c)) * (col / double(g.N));
   }
-  red[threadIdx.x] = acc;
+  red[threadIdx.x] = v;
   __syncthreads();
   for (int st = 128; st > 0; st >>= 1) {
     if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    const double t = red[0] + double(bias);
-    s_out[b] = float(1.0 / (1.0 + exp(-t)));
-  }
+  if (threadIdx.x == 0) dots[(long long)b * gridDim.x + blk] = red[0];
+}
+
+__global__ void gate_final_kernel(int nblk, const double *__restrict__ dots, float bias,
+                                  float *__restrict__ s_out) {
+  const int b = threadIdx.x;
+  if (b >= blockDim.x) return;
+  double t = double(bias);
+  for (int i = 0; i < nblk; ++i) t += dots[(long long)b * nblk + i];
+  s_out[b] = float(1.0 / (1.0 + exp(-t)));
 }
 
 hipError_t launch_gate(const Geom &g, int bf16, const void *x, const void *w, float bias,
                        float *partial, float *s, hipStream_t st) {
   const int splits = gate_splits(g);
-  dim3 grid(splits, g.B);
+  const int C = g.H * g.D, nblk = (C + 255) / 256;
+  double *dots = (double *)(partial + size_t(g.B) * splits * C);
+  dim3 grid(splits, g.B), grid2(nblk, g.B);
   if (bf16) {
     gate_partial_kernel<bf16_t><<<grid, 256, 0, st>>>(g, (const bf16_t *)x, partial, splits);
-    gate_final_kernel<bf16_t><<<g.B, 256, 0, st>>>(g, partial, splits, (const bf16_t *)w, bias, s);
+    gate_dot_kernel<bf16_t><<<grid2, 256, 0, st>>>(g, partial, splits, (const bf16_t *)w, dots);
   } else {
     gate_partial_kernel<float><<<grid, 256, 0, st>>>(g, (const float *)x, partial, splits);
-    gate_final_kernel<float><<<g.B, 256, 0, st>>>(g, partial, splits, (const float *)w, bias, s);
+    gate_dot_kernel<float><<<grid2, 256, 0, st>>>(g, partial, splits, (const float *)w, dots);
   }
+  gate_final_kernel<<<1, g.B, 0, st>>>(nblk, dots, bias, s);
   return hipGetLastError();
 }
 

@@ -25,8 +25,14 @@ inline int linear_splits(const Geom &g) {
 
 // Row chunks per sample used by the gate's token mean.
 inline int gate_splits(const Geom &g) {
-  int want = 256;
+  int want = 1024;
   return want > g.N ? g.N : want;
+}
+
+// Workspace bytes of the gate: column partial sums + per-block dot products.
+inline size_t gate_ws_bytes(const Geom &g) {
+  const size_t C = size_t(g.H) * g.D;
+  return size_t(g.B) * gate_splits(g) * C * sizeof(float) + size_t(g.B) * ((C + 255) / 256) * sizeof(double) + 256;
 }
 
 hipError_t launch_permute(const Geom &g, int bf16, int rope, int inverse, const void *src,
@@ -38,7 +44,7 @@ hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float 
                                float *h, float *z, hipStream_t st);
 hipError_t launch_linear_apply(const Geom &g, int bf16, View qv, const float *h, const float *z,
                                float *o_l, hipStream_t st);
-// partial: [B][gate_splits][C] floats of workspace.
+// partial: gate_ws_bytes of workspace ([B][gate_splits][C] floats, then doubles).
 hipError_t launch_gate(const Geom &g, int bf16, const void *x, const void *w, float bias,
                        float *partial, float *s, hipStream_t st);
 hipError_t launch_combine(const Geom &g, int bf16, const float *o_s, const float *o_l,
