@@ -36,7 +36,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Info {
   Geom g;
-  int bf16;
+  int bf16, rope;
   int any_topk, any_window;
   size_t esize;
 };
@@ -108,15 +108,22 @@ salad_status validate(const salad_problem *p, Info *inf) {
     if (sum != p->head_dim) return fail(SALAD_ERR_SHAPE, "rope_dims must sum to head_dim");
     if (!(p->rope_base > 0.f)) return fail(SALAD_ERR_SHAPE, "rope_base must be > 0");
   }
+  g.f_magic = 0;
+  if (g.F > 1 && (unsigned long long)N * g.F < (1ull << 32))
+    g.f_magic = uint32_t(((1ull << 32) + g.F - 1) / g.F);
   inf->bf16 = p->io_dtype == SALAD_BF16;
+  inf->rope = p->rope;
   inf->esize = inf->bf16 ? 2 : 4;
   return SALAD_OK;
 }
 
-// Workspace plan.  Regions are 256-byte aligned.
+// Workspace plan.  Regions are 256-byte aligned.  The stage entry points use
+// the first total_stage bytes.  salad_attn_forward adds, after that shared
+// scratch: for bf16 (fused) the RoPE'd working Q/K (only with rope), the
+// block selection, Hp and Z; for f32 (staged) working copies of Q/K/V, the
+// selection, O_s, O_l, H and Z.  Both end with the gate values.
 struct Plan {
-  size_t means, lin_partial, gate_partial;  // per-stage scratch
-  size_t wq, wk, wv, idx, o_s, o_l, h, z, s;  // forward-only buffers
+  size_t wq, wk, wv, idx, o_s, o_l, h, z, s, hp;
   size_t total_stage, total_forward;
 };
 
@@ -124,26 +131,34 @@ size_t up(size_t x) { return (x + 255) & ~size_t(255); }
 
 Plan plan(const Info &inf) {
   const Geom &g = inf.g;
-  Plan pl;
+  Plan pl = {};
   const size_t BH = size_t(g.B) * g.H;
   const size_t rows = BH * g.N;
   const size_t means = inf.any_topk ? 2 * up(BH * g.nb * g.D * sizeof(double)) : 0;
   const size_t lin = up(BH * linear_splits(g) * (size_t(g.D) * g.D + g.D) * sizeof(float));
   const size_t gate = up(gate_ws_bytes(g));
-  pl.means = 0;
-  pl.lin_partial = 0;
-  pl.gate_partial = 0;
   pl.total_stage = means > lin ? (means > gate ? means : gate) : (lin > gate ? lin : gate);
-  // forward: buffers after a shared scratch region of total_stage bytes
   size_t off = pl.total_stage;
-  pl.wq = off; off += up(rows * g.D * inf.esize);
-  pl.wk = off; off += up(rows * g.D * inf.esize);
-  pl.wv = off; off += up(rows * g.D * inf.esize);
-  pl.idx = off; off += inf.any_topk ? up(BH * g.nb * g.k * sizeof(int32_t)) : 0;
-  pl.o_s = off; off += up(rows * g.D * sizeof(float));
-  pl.o_l = off; off += up(rows * g.D * sizeof(float));
-  pl.h = off; off += up(BH * g.D * g.D * sizeof(float));
-  pl.z = off; off += up(BH * g.D * sizeof(float));
+  const size_t idx_bytes = inf.any_topk ? up(BH * g.nb * g.k * sizeof(int32_t)) : 0;
+  if (inf.bf16) {
+    const bool rope = inf.rope != 0;
+    pl.wq = off; off += rope ? up(rows * g.D * inf.esize) : 0;
+    pl.wk = off; off += up(rows * g.D * inf.esize);
+    pl.wv = off; off += up(rows * g.D * inf.esize);
+    pl.idx = off; off += idx_bytes;
+    pl.h = off; off += up(BH * g.D * g.D * sizeof(float));
+    pl.hp = off; off += up(BH * g.D * g.D * sizeof(bf16_t));
+    pl.z = off; off += up(BH * g.D * sizeof(float));
+  } else {
+    pl.wq = off; off += up(rows * g.D * inf.esize);
+    pl.wk = off; off += up(rows * g.D * inf.esize);
+    pl.wv = off; off += up(rows * g.D * inf.esize);
+    pl.idx = off; off += idx_bytes;
+    pl.o_s = off; off += up(rows * g.D * sizeof(float));
+    pl.o_l = off; off += up(rows * g.D * sizeof(float));
+    pl.h = off; off += up(BH * g.D * g.D * sizeof(float));
+    pl.z = off; off += up(BH * g.D * sizeof(float));
+  }
   pl.s = off; off += up(size_t(g.B) * sizeof(float));
   pl.total_forward = off;
   return pl;
@@ -168,6 +183,18 @@ salad_status need_ws(void *ws, size_t ws_bytes, size_t needed) {
   if (ws_bytes < needed)
     return fail(SALAD_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, needed);
   return SALAD_OK;
+}
+
+// Boundary layout [B, N, H, d] read in each head's working order (temporal
+// heads gather token st_token(p) for working row p).
+View boundary_view(const Geom &g, const void *base) {
+  View v;
+  v.base = base;
+  v.sB = (long long)g.N * g.H * g.D;
+  v.sH = g.D;
+  v.sN = (long long)g.H * g.D;
+  v.perm = 1;
+  return v;
 }
 
 View working_view(const Geom &g, const void *base) {
@@ -324,7 +351,7 @@ salad_status salad_gate(const salad_problem *p, const void *x, const void *w, fl
   const Geom &g = inf.g;
   const size_t needed = up(gate_ws_bytes(g));
   CHECK(need_ws(ws, ws_bytes, needed));
-  return hip_status(launch_gate(g, inf.bf16, x, w, bias, (float *)ws, s, stream), "salad_gate");
+  return hip_status(launch_gate(g, inf.bf16, x, w, bias, ws, s, stream), "salad_gate");
 }
 
 salad_status salad_combine(const salad_problem *p, const float *o_s, const float *o_l, const void *w_p,
@@ -378,10 +405,47 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
       s = const_cast<float *>(s_override);
     }
   } else {
-    e = launch_gate(g, inf.bf16, x, gate_w, gate_b, (float *)scratch, s, stream);
+    e = launch_gate(g, inf.bf16, x, gate_w, gate_b, scratch, s, stream);
     if (e != hipSuccess) return hip_status(e, "salad_attn_forward: gate");
   }
   const int rope = p->rope;
+
+  if (inf.bf16) {
+    // Fused path.  The linear-state pass reads K and V in each head's
+    // working order (gathered from the boundary layout) and writes the
+    // contiguous working copies the attention kernel streams; Q is gathered
+    // by the attention kernel itself.  With RoPE, Q and K are rotated into
+    // working copies first.  The linear branch, projection, gate and inverse
+    // permutation run in the attention epilogue.
+    View qv = boundary_view(g, q), kv_in = boundary_view(g, k);
+    bf16_t *k_copy = (bf16_t *)wk;
+    if (rope) {
+      if ((e = launch_permute(g, 1, 1, 0, q, wq, stream)) != hipSuccess ||
+          (e = launch_permute(g, 1, 1, 0, k, wk, stream)) != hipSuccess)
+        return hip_status(e, "salad_attn_forward: rope");
+      qv = working_view(g, wq);
+      kv_in = working_view(g, wk);
+      k_copy = nullptr;  // already in working order
+    }
+    const View kv = working_view(g, wk), vv = working_view(g, wv);
+    bf16_t *hp = (bf16_t *)(w + pl.hp);
+    if ((e = launch_linear_partials(g, kv_in, boundary_view(g, v), (float *)scratch, k_copy,
+                                    (bf16_t *)wv, stream)) != hipSuccess ||
+        (e = launch_linear_finalize(g, 1, (const float *)scratch, w_p, s, hm, hp, zv, stream)) != hipSuccess)
+      return hip_status(e, "salad_attn_forward: linear state");
+    if (inf.any_topk) {
+      const size_t one = up(size_t(g.B) * g.H * g.nb * g.D * sizeof(double));
+      e = launch_block_select(g, 1, qv, kv, (double *)scratch, (double *)(w + one), idx, stream);
+      if (e != hipSuccess) return hip_status(e, "salad_attn_forward: block select");
+    }
+    if ((e = prof_mark(0, stream)) != hipSuccess ||
+        (e = launch_attn_fused(g, qv, kv, vv, idx, hp, zv, boundary_view(g, out), stream)) != hipSuccess ||
+        (e = prof_mark(1, stream)) != hipSuccess)
+      return hip_status(e, "salad_attn_forward: attention");
+    return SALAD_OK;
+  }
+
+  // f32: staged path through working copies
   if ((e = launch_permute(g, inf.bf16, rope, 0, q, wq, stream)) != hipSuccess ||
       (e = launch_permute(g, inf.bf16, rope, 0, k, wk, stream)) != hipSuccess ||
       (e = launch_permute(g, inf.bf16, 0, 0, v, wv, stream)) != hipSuccess)

@@ -110,7 +110,10 @@ struct AttnArgs {
   Geom g;
   View q, k, v;
   const int32_t *idx;
-  float *o_s;            // working layout fp32 output
+  float *o_s;            // staged: working layout fp32 output
+  const bf16_t *hp;      // fused: [B*H][128][128] bf16, s_b * (H W_p)^T
+  const float *z;        // fused: [B*H][128] linear normaliser state
+  View out;              // fused: output rows (boundary layout, scattered)
   int topk_mode;         // 0: window heads, 1: Top-K heads
   int n_heads_sel;       // heads handled by this launch
   uint8_t heads[kMaxHeads];
@@ -126,7 +129,7 @@ __device__ __forceinline__ int xcd_order(int bid, int T) {
   return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 
-template <int NW>
+template <int NW, bool FUSED>
 __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   constexpr int BM = NW * 32;
   constexpr int TILE = kBN * kD;                 // elements per K or V tile
@@ -338,8 +341,70 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (pq >= g.N) return;
   const float inv = 1.f / l_tot;
+
+  if constexpr (FUSED) {
+    // Linear branch, projection, gate and combine for this wave's queries:
+    //   out = O_s + relu(q) Hp / (relu(q) . Z + eps),  Hp = s_b (H W_p)^T
+    // Hp rows 0..63 go to K0 and rows 64..127 to V0 (same swizzle as K).
+    __syncthreads();  // every wave is done with the last key tile
+    const bf16_t *hsrc = a.hp + (long long)bh * kD * kD;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int row = 4 * (i * NW + w) + (lane >> 4);
+      const int u = (lane & 15) ^ kv_swz(row);
+      __builtin_amdgcn_global_load_lds((const void *)(hsrc + row * kD + u * 8),
+                                       (lds_void *)(K0 + (4 * (i * NW + w)) * kD), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(hsrc + (64 + row) * kD + u * 8),
+                                       (lds_void *)(V0 + (4 * (i * NW + w)) * kD), 16, 0, 0);
+    }
+    // relu(q) operands and the normaliser relu(q) . Z (this lane's 64 features
+    // plus the other half-wave's)
+    const float *zr = a.z + (long long)bh * kD;
+    bf16x8 rq[8];
+    float den = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const f32x4 z0 = *(const f32x4 *)(zr + 16 * ks + 8 * hl);
+      const f32x4 z1 = *(const f32x4 *)(zr + 16 * ks + 8 * hl + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qv = fmaxf(float(qf[ks][e]), 0.f);
+        rq[ks][e] = (__bf16)qv;  // exact: relu of a bf16 value
+        den = fmaf(qv, e < 4 ? z0[e] : z1[e - 4], den);
+      }
+    }
+    den += __shfl_xor(den, 32);
+    const float inv_den = 1.f / (den + g.eps);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    f32x16 lin[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) lin[db] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16_t *hb = (db < 2 ? K0 : V0) + (db & 1) * 32 * kD;
+        const bf16x8 ha = *(const bf16x8 *)(hb + k_lane + 16 * (ks ^ k_x));
+        lin[db] = mfma_32x32x16(ha, rq[ks], lin[db]);
+      }
+    if (pq >= g.N) return;
+    bf16_t *orow = (bf16_t *)a.out.base + row_offset(g, a.out, b, h, pq);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = (__bf16)(o[db][4 * r4 + e] * inv + lin[db][4 * r4 + e] * inv_den);
+        *(bf16x4 *)(orow + 32 * db + 8 * r4 + 4 * hl) = v;
+      }
+    return;
+  }
+
+  if (pq >= g.N) return;
   float *dst = a.o_s + ((long long)bh * g.N + pq) * kD;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -351,24 +416,13 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     }
 }
 
-hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv,
-                              const int32_t *idx, float *o_s, hipStream_t st) {
-  if (!bf16) {
-    dim3 grid((g.N + 63) / 64, g.B * g.H);
-    if (g.D == 128)
-      attn_f32_kernel<128><<<grid, 64, 0, st>>>(g, qv, kv, vv, idx, o_s);
-    else
-      attn_f32_kernel<64><<<grid, 64, 0, st>>>(g, qv, kv, vv, idx, o_s);
-    return hipGetLastError();
-  }
+namespace {
+// One launch per head kind: window heads use 128-query tiles (4 waves),
+// Top-K heads one 64-query block per workgroup (2 waves).
+template <bool FUSED>
+hipError_t launch_bf16(AttnArgs a, hipStream_t st) {
+  const Geom &g = a.g;
   for (int mode = 0; mode < 2; ++mode) {
-    AttnArgs a;
-    a.g = g;
-    a.q = qv;
-    a.k = kv;
-    a.v = vv;
-    a.idx = idx;
-    a.o_s = o_s;
     a.topk_mode = mode;
     a.n_heads_sel = 0;
     for (int h = 0; h < g.H; ++h) {
@@ -381,13 +435,48 @@ hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv
     const unsigned grid = unsigned(a.tiles_per_head) * a.n_heads_sel * g.B;
     a.n_blocks = int(grid);
     if (mode)
-      attn_bf16_kernel<2><<<grid, 128, 0, st>>>(a);
+      attn_bf16_kernel<2, FUSED><<<grid, 128, 0, st>>>(a);
     else
-      attn_bf16_kernel<4><<<grid, 256, 0, st>>>(a);
+      attn_bf16_kernel<4, FUSED><<<grid, 256, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv,
+                              const int32_t *idx, float *o_s, hipStream_t st) {
+  if (!bf16) {
+    dim3 grid((g.N + 63) / 64, g.B * g.H);
+    if (g.D == 128)
+      attn_f32_kernel<128><<<grid, 64, 0, st>>>(g, qv, kv, vv, idx, o_s);
+    else
+      attn_f32_kernel<64><<<grid, 64, 0, st>>>(g, qv, kv, vv, idx, o_s);
+    return hipGetLastError();
+  }
+  AttnArgs a = {};
+  a.g = g;
+  a.q = qv;
+  a.k = kv;
+  a.v = vv;
+  a.idx = idx;
+  a.o_s = o_s;
+  return launch_bf16<false>(a, st);
+}
+
+hipError_t launch_attn_fused(const Geom &g, View qv, View kv, View vv, const int32_t *idx,
+                             const bf16_t *hp, const float *z, View outv, hipStream_t st) {
+  AttnArgs a = {};
+  a.g = g;
+  a.q = qv;
+  a.k = kv;
+  a.v = vv;
+  a.idx = idx;
+  a.hp = hp;
+  a.z = z;
+  a.out = outv;
+  return launch_bf16<true>(a, st);
 }
 
 }  // namespace salad

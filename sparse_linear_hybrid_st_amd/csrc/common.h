@@ -77,15 +77,27 @@ struct Geom {
   float eps;             // linear denominator guard
   int rope_dims[3];
   float rope_base;
+  uint32_t f_magic;      // ceil(2^32 / F) when F > 1 and N * F < 2^32, else 0
 };
 
 __device__ __forceinline__ bool bit(const uint64_t *m, int h) {
   return (m[h >> 6] >> (h & 63)) & 1ull;
 }
 
+// floor(p / F).  With f_magic = ceil(2^32 / F) = (2^32 + e) / F, 0 <= e < F,
+// p * f_magic / 2^32 = p/F + p*e / (F * 2^32), and the excess is below 1/F
+// whenever p * F < 2^32, which cannot lift floor(p/F) since the fractional
+// part of p/F is at most (F-1)/F.  The host sets f_magic only when
+// N * F < 2^32 (else 0: plain division).
+__device__ __forceinline__ int div_f(const Geom &g, int p) {
+  if (g.F == 1) return p;
+  return g.f_magic ? int(__umulhi(uint32_t(p), g.f_magic)) : p / g.F;
+}
+
 // Working position p of a temporal head holds this token.
 __device__ __forceinline__ int st_token(const Geom &g, int p) {
-  return (p % g.F) * (g.Hg * g.Wg) + p / g.F;
+  const int q = div_f(g, p);
+  return (p - q * g.F) * (g.Hg * g.Wg) + q;
 }
 // ... and token n sits at this working position.
 __device__ __forceinline__ int st_position(const Geom &g, int n) {

@@ -7,87 +7,84 @@
 // section 2.3 and news.axiwang.com section 六 (token average, then a linear
 // layer and a sigmoid).
 //
-// Both are HBM-bound.  The gate reads X once: per sample, row chunks write
-// fp32 column sums to the workspace, 256-column blocks finish the means and
-// their dot product with w (fp64), and one thread per sample adds the block
-// results and applies the sigmoid -- a fixed summation order throughout.
+// Both are HBM-bound.  The gate reads X once: per sample, row chunks reduce
+// to partial dot products w . sum X[n] (fp32 inside a thread, fp64 across
+// threads and chunks) and one workgroup per sample finishes the mean and the
+// sigmoid -- a fixed summation order throughout.
 #include "common.h"
 #include "kernels.h"
 
 namespace salad {
 
-// Column sums of X[b, rows of chunk s, :].  Grid (splits, B); thread t owns
-// 8-column groups t, t+256, ... and reads them with one 16-byte load per row.
+// The gate is linear before the sigmoid: w . mean_n X[n] = (1/N) sum_n w . X[n],
+// so each workgroup reduces its row chunk straight to one number.
+// Grid (splits, B); thread t owns 8-column groups t, t+256, ...: it
+// accumulates sum_rows w[c] * X[n][c] in fp32 (one 16-byte load per row),
+// then the workgroup adds the 256 thread sums in fp64 (fixed-order tree).
 template <typename T>
 __global__ void __launch_bounds__(256) gate_partial_kernel(Geom g, const T *__restrict__ x,
-                                                           float *__restrict__ partial, int splits) {
+                                                           const T *__restrict__ w,
+                                                           double *__restrict__ partial, int splits) {
   const int s = blockIdx.x, b = blockIdx.y, C = g.H * g.D;
   const int rows = (g.N + splits - 1) / splits;
   const int n0 = s * rows, n1 = min(g.N, n0 + rows);
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  float acc = 0.f;
   for (int cg = threadIdx.x; cg * 8 < C; cg += 256) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float wv[8], cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wv[e] = io<T>::ld(w + cg * 8 + e);
     for (int n = n0; n < n1; ++n) {
       const T *src = x + ((long long)b * g.N + n) * C + cg * 8;
       T v[8];
       *(u32x4 *)v = *(const u32x4 *)src;
       if (sizeof(T) == 4) *(u32x4 *)(v + 4) = *(const u32x4 *)(src + 4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += io<T>::ld(v + e);
+      for (int e = 0; e < 8; ++e) cs[e] += io<T>::ld(v + e);
     }
-    float *dst = partial + ((long long)b * splits + s) * C + cg * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dst[e] = acc[e];
+    for (int e = 0; e < 8; ++e) acc = fmaf(wv[e], cs[e], acc);
   }
-}
-
-// Column means and their dot product with w, per 256-column block (fp64,
-// fixed-order tree): dots[b][blk].
-template <typename T>
-__global__ void __launch_bounds__(256) gate_dot_kernel(Geom g, const float *__restrict__ partial,
-                                                       int splits, const T *__restrict__ w,
-                                                       double *__restrict__ dots) {
-  const int blk = blockIdx.x, b = blockIdx.y, C = g.H * g.D;
-  const int c = blk * 256 + threadIdx.x;
   __shared__ double red[256];
-  double v = 0.0;
-  if (c < C) {
-    double col = 0.0;
-    for (int s = 0; s < splits; ++s) col += double(partial[((long long)b * splits + s) * C + c]);
-    v = double(io<T>::ld(w + c)) * (col / double(g.N));
-  }
-  red[threadIdx.x] = v;
+  red[threadIdx.x] = double(acc);
   __syncthreads();
   for (int st = 128; st > 0; st >>= 1) {
     if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
     __syncthreads();
   }
-  if (threadIdx.x == 0) dots[(long long)b * gridDim.x + blk] = red[0];
+  if (threadIdx.x == 0) partial[(long long)b * splits + s] = red[0];
 }
 
-__global__ void gate_final_kernel(int nblk, const double *__restrict__ dots, float bias,
-                                  float *__restrict__ s_out) {
-  const int b = threadIdx.x;
-  if (b >= blockDim.x) return;
-  double t = double(bias);
-  for (int i = 0; i < nblk; ++i) t += dots[(long long)b * nblk + i];
-  s_out[b] = float(1.0 / (1.0 + exp(-t)));
+// s_b = sigmoid(sum_s partial[b][s] / N + bias): one workgroup per sample,
+// thread t adds splits t, t+256, ... in order, then a fixed-order tree.
+__global__ void __launch_bounds__(256) gate_final_kernel(int N, int splits, const double *__restrict__ partial,
+                                                         float bias, float *__restrict__ s_out) {
+  const int b = blockIdx.x;
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < splits; i += 256) acc += partial[(long long)b * splits + i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double t = red[0] / double(N) + double(bias);
+    s_out[b] = float(1.0 / (1.0 + exp(-t)));
+  }
 }
 
 hipError_t launch_gate(const Geom &g, int bf16, const void *x, const void *w, float bias,
-                       float *partial, float *s, hipStream_t st) {
+                       void *ws, float *s, hipStream_t st) {
   const int splits = gate_splits(g);
-  const int C = g.H * g.D, nblk = (C + 255) / 256;
-  double *dots = (double *)(partial + size_t(g.B) * splits * C);
-  dim3 grid(splits, g.B), grid2(nblk, g.B);
-  if (bf16) {
-    gate_partial_kernel<bf16_t><<<grid, 256, 0, st>>>(g, (const bf16_t *)x, partial, splits);
-    gate_dot_kernel<bf16_t><<<grid2, 256, 0, st>>>(g, partial, splits, (const bf16_t *)w, dots);
-  } else {
-    gate_partial_kernel<float><<<grid, 256, 0, st>>>(g, (const float *)x, partial, splits);
-    gate_dot_kernel<float><<<grid2, 256, 0, st>>>(g, partial, splits, (const float *)w, dots);
-  }
-  gate_final_kernel<<<1, g.B, 0, st>>>(nblk, dots, bias, s);
+  double *partial = (double *)ws;
+  dim3 grid(splits, g.B);
+  if (bf16)
+    gate_partial_kernel<bf16_t><<<grid, 256, 0, st>>>(g, (const bf16_t *)x, (const bf16_t *)w, partial, splits);
+  else
+    gate_partial_kernel<float><<<grid, 256, 0, st>>>(g, (const float *)x, (const float *)w, partial, splits);
+  gate_final_kernel<<<g.B, 256, 0, st>>>(g.N, splits, partial, bias, s);
   return hipGetLastError();
 }
 

@@ -29,11 +29,8 @@ inline int gate_splits(const Geom &g) {
   return want > g.N ? g.N : want;
 }
 
-// Workspace bytes of the gate: column partial sums + per-block dot products.
-inline size_t gate_ws_bytes(const Geom &g) {
-  const size_t C = size_t(g.H) * g.D;
-  return size_t(g.B) * gate_splits(g) * C * sizeof(float) + size_t(g.B) * ((C + 255) / 256) * sizeof(double) + 256;
-}
+// Workspace bytes of the gate: one double per (sample, row chunk).
+inline size_t gate_ws_bytes(const Geom &g) { return size_t(g.B) * gate_splits(g) * sizeof(double); }
 
 hipError_t launch_permute(const Geom &g, int bf16, int rope, int inverse, const void *src,
                           void *dst, hipStream_t st);
@@ -42,11 +39,23 @@ hipError_t launch_block_select(const Geom &g, int bf16, View qv, View kv, double
 // partial: [B*H][S][D*D + D] floats of workspace (S = linear_splits).
 hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float *partial,
                                float *h, float *z, hipStream_t st);
+// Fused-layer pieces (bf16, d = 128).
+// Also writes working-layout copies of K / V when kw_out / vw_out are non-null.
+hipError_t launch_linear_partials(const Geom &g, View kv, View vv, float *partial, bf16_t *kw_out,
+                                  bf16_t *vw_out, hipStream_t st);
+// h: [B*H][128][128] fp32 state (workspace); hp: [B*H][128][128] bf16 =
+// s_b * (H W_p)^T; z: [B*H][128] fp32.
+hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial, const void *w_p,
+                                  const float *s, float *h, bf16_t *hp, float *z, hipStream_t st);
+// Sparse attention with the linear branch, projection, gate and inverse
+// permutation fused into the epilogue; out in the boundary layout.
+hipError_t launch_attn_fused(const Geom &g, View qv, View kv, View vv, const int32_t *idx,
+                             const bf16_t *hp, const float *z, View outv, hipStream_t st);
 hipError_t launch_linear_apply(const Geom &g, int bf16, View qv, const float *h, const float *z,
                                float *o_l, hipStream_t st);
-// partial: gate_ws_bytes of workspace ([B][gate_splits][C] floats, then doubles).
+// ws: gate_ws_bytes of workspace.
 hipError_t launch_gate(const Geom &g, int bf16, const void *x, const void *w, float bias,
-                       float *partial, float *s, hipStream_t st);
+                       void *ws, float *s, hipStream_t st);
 hipError_t launch_combine(const Geom &g, int bf16, const float *o_s, const float *o_l,
                           const void *w_p, const float *s, void *out, hipStream_t st);
 hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv,

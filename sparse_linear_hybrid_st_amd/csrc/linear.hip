@@ -6,11 +6,12 @@
 // method step 3 (the branch runs on the same Q, K, V as the sparse one).
 //
 // bf16 path (d = 128), on MFMA v_mfma_f32_32x32x16_bf16:
-//   state: the contraction runs over tokens, the slow index of K and V, so
-//   each 128-token tile is written to LDS transposed ([d][token], XOR
-//   swizzled) and the 4 waves each accumulate a 64x64 quadrant of H; the N
-//   tokens are split over workgroups and the partial states are summed in a
-//   fixed order by a second kernel (deterministic, no atomics).
+//   state: the contraction runs over tokens, the slow index of K and V;
+//   64-token tiles sit in LDS row-major and transposing LDS reads
+//   (ds_read_b64_tr_b16) deliver 4 consecutive tokens of a feature per
+//   lane; the 4 waves each accumulate a 64x64 quadrant of H; the N tokens
+//   are split over workgroups and the partial states are summed in a fixed
+//   order by a second kernel (deterministic, no atomics).
 //   apply: H is split into bf16 hi + lo halves (about 16 significant bits)
 //   so the output keeps near-fp32 accuracy; relu(q) is exact in bf16.
 // f32 path (d = 64 or 128): plain VALU loops.
@@ -28,6 +29,9 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
+__global__ void linear_reduce_kernel(int D, int S, const float *__restrict__ partial,
+                                     float *__restrict__ h, float *__restrict__ z);
+
 __device__ __forceinline__ u32x4 relu_bf16x8(u32x4 v) {
   // clear each 16-bit half whose sign bit is set
 #pragma unroll
@@ -41,28 +45,39 @@ __device__ __forceinline__ u32x4 relu_bf16x8(u32x4 v) {
 }
 
 // ---------------------------------------------------------------------------
-// State, bf16, d = 128.  Grid (S, B*H); 256 threads.
-// Tile: 128 tokens.  Load mapping: thread t reads 16-byte chunk c = t%16 of
-// rows 8*(t/16) .. +7, so each load instruction covers 4 full 256-byte rows.
-// LDS layout of Kt/Vt: row = feature (128), 16 units of 8 tokens; unit u of
-// row rho is stored at u ^ swz(rho), swz(rho) = (rho ^ (rho >> 3)) & 15,
-// which keeps both the transposed stores (rows 8 apart) and the MFMA operand
-// reads (16 consecutive rows) on distinct 16-byte bank groups.
+// State, bf16, d = 128.  Grid (S, B*H); 256 threads; split s covers working
+// rows [s*chunk, (s+1)*chunk).  Tiles of 64 tokens: thread t loads 16-byte
+// chunk c = t%16 of rows t/16 + 16i (i < 4) of K and V -- each load
+// instruction covers four whole 256-byte rows -- and, when kw_out / vw_out
+// are given, stores them to those working-layout copies (the pass that
+// already reads K and V produces the contiguous per-head copies the
+// attention kernel streams).  relu(K) and V go to LDS row-major; unit u of
+// row j sits at u ^ lin_swz(j).  The MFMA operands, which need 4 consecutive
+// tokens of one feature per lane, come from ds_read_b64_tr_b16: each 16-lane
+// group reads 4 rows x 64 bytes, which lin_swz spreads over distinct banks.
+// Wave w accumulates the 64x64 quadrant (i0, j0) = (64*(w/2), 64*(w%2)) of H.
+// The next tile's global loads are issued before the current tile's MFMAs.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int kt_swz(int rho) { return (rho ^ (rho >> 3)) & 15; }
+__device__ __forceinline__ int lin_swz(int j) { return ((j & 3) << 2) | ((j >> 2) & 3); }
 
-__global__ void __launch_bounds__(256) linear_state_bf16_kernel(Geom g, View kv, View vv,
+typedef __attribute__((ext_vector_type(4))) short s16x4_l;
+typedef __attribute__((address_space(3))) s16x4_l lds_s16x4_l;
+
+__global__ void __launch_bounds__(256, 2) linear_state_bf16_kernel(Geom g, View kv, View vv,
                                                                 float *__restrict__ partial,
-                                                                int S, int chunk) {
-  constexpr int D = 128, TT = 128;
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[D * TT];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * TT];
+                                                                int S, int chunk,
+                                                                bf16_t *__restrict__ kw_out,
+                                                                bf16_t *__restrict__ vw_out) {
+  constexpr int D = 128, TT = 64;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[TT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[TT * D];
   const int s = blockIdx.x, bh = blockIdx.y, h = bh % g.H, b = bh / g.H;
   const int n0 = s * chunk, n1 = min(g.N, n0 + chunk);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int c = t & 15, rg = t >> 4;
   const bf16_t *kb = (const bf16_t *)kv.base;
   const bf16_t *vb = (const bf16_t *)vv.base;
+  const long long wbase = (long long)bh * g.N * D;  // working-layout copy of this (b, h)
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -71,53 +86,69 @@ __global__ void __launch_bounds__(256) linear_state_bf16_kernel(Geom g, View kv,
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int i0 = (w >> 1) * 64, j0 = (w & 1) * 64;
-  const int hl = lane >> 5, l32 = lane & 31;
-
-  for (int base = n0; base < n1; base += TT) {
-    u32x4 kr[8], vr[8];
+  const int hl = lane >> 5, gq = lane >> 4, jl = lane & 15;
+  // lane-constant part of the transposing reads: row 8hl + 4r + jl/4,
+  // feature f0 + 4*(jl%4) with f0 = base + 16*(gq%2)
+  int toff[2][2][2];  // [operand A/B][block][r]
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int n = base + rg * 8 + i;
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int op = 0; op < 2; ++op) {
+        const int row = 8 * hl + 4 * r + (jl >> 2);
+        const int f = (op ? j0 : i0) + 32 * bi + 16 * (gq & 1) + 4 * (jl & 3);
+        toff[op][bi][r] = row * D + (((f >> 3) ^ lin_swz(row)) << 3) + (f & 4);
+      }
+
+  u32x4 kr[4], vr[4];
+  auto load = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = base + rg + 16 * i;
       if (n < n1) {
-        kr[i] = relu_bf16x8(*(const u32x4 *)(kb + row_offset(g, kv, b, h, n) + c * 8));
+        kr[i] = *(const u32x4 *)(kb + row_offset(g, kv, b, h, n) + c * 8);
         vr[i] = *(const u32x4 *)(vb + row_offset(g, vv, b, h, n) + c * 8);
       } else {
         kr[i] = u32x4{0, 0, 0, 0};
         vr[i] = u32x4{0, 0, 0, 0};
       }
     }
+  };
+  if (n0 < n1) load(n0);
+  for (int base = n0; base < n1; base += TT) {
     __syncthreads();  // previous tile's operand reads are done
-    // transpose 8 rows x 8 features into 8 rows of Kt/Vt (one 16-byte unit each)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int rho = c * 8 + e;
-      const int sh = (e & 1) * 16, word = e >> 1;
-      u32x4 ko, vo;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t k_lo = (kr[2 * i][word] >> sh) & 0xffffu, k_hi = (kr[2 * i + 1][word] >> sh) & 0xffffu;
-        uint32_t v_lo = (vr[2 * i][word] >> sh) & 0xffffu, v_hi = (vr[2 * i + 1][word] >> sh) & 0xffffu;
-        ko[i] = k_lo | (k_hi << 16);
-        vo[i] = v_lo | (v_hi << 16);
-        z[e] += bf16_to_f32(bf16_t(k_lo)) + bf16_to_f32(bf16_t(k_hi));
+    for (int i = 0; i < 4; ++i) {
+      const int row = rg + 16 * i, n = base + row;
+      if (n < n1) {
+        if (kw_out) *(u32x4 *)(kw_out + wbase + (long long)n * D + c * 8) = kr[i];
+        if (vw_out) *(u32x4 *)(vw_out + wbase + (long long)n * D + c * 8) = vr[i];
       }
-      const int unit = rg ^ kt_swz(rho);
-      *(u32x4 *)(Kt + rho * TT + unit * 8) = ko;
-      *(u32x4 *)(Vt + rho * TT + unit * 8) = vo;
+      const u32x4 rk = relu_bf16x8(kr[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        z[e] += bf16_to_f32(bf16_t((rk[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
+      const int unit = c ^ lin_swz(row);
+      *(u32x4 *)(Ks + row * D + unit * 8) = rk;
+      *(u32x4 *)(Vs + row * D + unit * 8) = vr[i];
     }
     __syncthreads();
+    if (base + TT < n1) load(base + TT);
 #pragma unroll
     for (int ks = 0; ks < TT / 16; ++ks) {
       bf16x8 a[2], bb[2];
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi) {
-        const int rho = i0 + 32 * bi + l32;
-        a[bi] = *(const bf16x8 *)(Kt + rho * TT + ((2 * ks + hl) ^ kt_swz(rho)) * 8);
-      }
-#pragma unroll
-      for (int bj = 0; bj < 2; ++bj) {
-        const int rho = j0 + 32 * bj + l32;
-        bb[bj] = *(const bf16x8 *)(Vt + rho * TT + ((2 * ks + hl) ^ kt_swz(rho)) * 8);
+        const s16x4_l p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_l *)(Ks + 16 * ks * D + toff[0][bi][0]));
+        const s16x4_l p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_l *)(Ks + 16 * ks * D + toff[0][bi][1]));
+        const s16x4_l q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_l *)(Vs + 16 * ks * D + toff[1][bi][0]));
+        const s16x4_l q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_l *)(Vs + 16 * ks * D + toff[1][bi][1]));
+        typedef __attribute__((ext_vector_type(8))) short s16x8_l;
+        s16x8_l av = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        s16x8_l bv = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+        a[bi] = *(const bf16x8 *)&av;
+        bb[bi] = *(const bf16x8 *)&bv;
       }
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi)
@@ -134,12 +165,12 @@ __global__ void __launch_bounds__(256) linear_state_bf16_kernel(Geom g, View kv,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = i0 + 32 * bi + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const int j = j0 + 32 * bj + l32;
+        const int j = j0 + 32 * bj + (lane & 31);
         out[i * D + j] = acc[bi][bj][r];
       }
   // Z: reduce the 16 row groups in a fixed order
   __syncthreads();
-  float *zs = (float *)Kt;  // [16][128]
+  float *zs = (float *)Ks;  // [16][128]
 #pragma unroll
   for (int e = 0; e < 8; ++e) zs[rg * D + c * 8 + e] = z[e];
   __syncthreads();
@@ -199,8 +230,8 @@ __global__ void __launch_bounds__(256) linear_state_f32_kernel(Geom g, View kv, 
 }
 
 // Fixed-order sum of the S partial states: h[bh] = sum_s partial[bh][s].
-__global__ void __launch_bounds__(256) linear_reduce_kernel(int D, int S, const float *__restrict__ partial,
-                                                            float *__restrict__ h, float *__restrict__ z) {
+__global__ void linear_reduce_kernel(int D, int S, const float *__restrict__ partial,
+                                     float *__restrict__ h, float *__restrict__ z) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int per = D * D + D;
@@ -214,6 +245,68 @@ __global__ void __launch_bounds__(256) linear_reduce_kernel(int D, int S, const 
     z[(long long)bh * D + (e - D * D)] = acc;
 }
 
+// ---------------------------------------------------------------------------
+// Projection for the fused layer (bf16, d = 128): fold the static projection
+// and the gate into the summed state,
+//   Hp = s_b * H W_p,   so that   s_b * (O_l W_p) = relu(q) Hp / (relu(q) . Z + eps)
+// (the normaliser is one scalar per token, so it commutes with W_p).  Hp is
+// written transposed, as bf16 rows [d_out][d_in] (the MFMA A operand of the
+// fused epilogue).  Grid (16, B*H): workgroup (blk, bh) computes rows
+// i = 8*blk .. +7 of H W_p; thread t owns row 8*blk + t/32 and columns
+// (t%32) + 32m.  W_p is staged in LDS as fp32.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) linear_project_kernel(Geom g, const float *__restrict__ hm,
+                                                             const T *__restrict__ w_p,
+                                                             const float *__restrict__ s_gate,
+                                                             bf16_t *__restrict__ hp) {
+  constexpr int D = 128;
+  __shared__ float Ws[D * D];
+  __shared__ float Hs[8][D];
+  const int blk = blockIdx.x, bh = blockIdx.y, b = bh / g.H, t = threadIdx.x;
+  for (int e = t; e < D * D; e += 256) Ws[e] = io<T>::ld(w_p + e);
+  for (int e = t; e < 8 * D; e += 256) Hs[e / D][e % D] = hm[((long long)bh * D + 8 * blk) * D + e];
+  __syncthreads();
+  const int ii = t >> 5, jg = t & 31;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < D; ++k) {
+    const float hv = Hs[ii][k];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = fmaf(hv, Ws[k * D + jg + 32 * m], acc[m]);
+  }
+  const float sb = s_gate[b];
+  bf16_t *dst = hp + (long long)bh * D * D;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const __bf16 v = (__bf16)(sb * acc[m]);
+    dst[(jg + 32 * m) * D + 8 * blk + ii] = *(const bf16_t *)&v;
+  }
+}
+
+hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial, const void *w_p,
+                                  const float *s, float *h, bf16_t *hp, float *z, hipStream_t st) {
+  const int S = linear_splits(g);
+  dim3 grid1((g.D * g.D + g.D + 255) / 256, g.B * g.H);
+  linear_reduce_kernel<<<grid1, 256, 0, st>>>(g.D, S, partial, h, z);
+  dim3 grid2(16, g.B * g.H);
+  if (bf16)
+    linear_project_kernel<bf16_t><<<grid2, 256, 0, st>>>(g, h, (const bf16_t *)w_p, s, hp);
+  else
+    linear_project_kernel<float><<<grid2, 256, 0, st>>>(g, h, (const float *)w_p, s, hp);
+  return hipGetLastError();
+}
+
+// Partial states only (the fused layer finalizes them itself), optionally
+// writing working-layout copies of K and V.
+hipError_t launch_linear_partials(const Geom &g, View kv, View vv, float *partial, bf16_t *kw_out,
+                                  bf16_t *vw_out, hipStream_t st) {
+  const int S = linear_splits(g);
+  int chunk = (g.N + S - 1) / S;
+  chunk = (chunk + 127) / 128 * 128;
+  linear_state_bf16_kernel<<<dim3(S, g.B * g.H), 256, 0, st>>>(g, kv, vv, partial, S, chunk, kw_out, vw_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float *partial, float *h,
                                float *z, hipStream_t st) {
   const int S = linear_splits(g);
@@ -221,7 +314,7 @@ hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float 
   chunk = (chunk + 127) / 128 * 128;
   dim3 grid(S, g.B * g.H);
   if (bf16) {
-    linear_state_bf16_kernel<<<grid, 256, 0, st>>>(g, kv, vv, partial, S, chunk);
+    linear_state_bf16_kernel<<<grid, 256, 0, st>>>(g, kv, vv, partial, S, chunk, nullptr, nullptr);
   } else if (g.D == 128) {
     linear_state_f32_kernel<128><<<grid, 256, 0, st>>>(g, kv, vv, partial, S, chunk);
   } else {
