@@ -344,67 +344,84 @@ def attn_forward(q, k, v, x, w_p, gate_w, gate_b, *, grid, head_kinds,
     branch per head (window or Top-K); linear branch on the same Q, K, V;
     gate per sample; O = O_s + s * (O_l W_p) written back in token order.
 
-    ``rows`` (optional, a list of (b, n, h) triples) limits the sparse
-    branch to those output rows; the result then maps each triple to its
-    output vector.  Otherwise returns a dict with "out" [B, N, H, d] and
-    the stage results ("o_s", "o_l", "H", "Z", "s", "idx", "orders").
+    Everything but the gate is per (sample, head), so each head's inputs
+    are prepared only when that head is needed.  ``rows`` (optional, a list
+    of (b, n, h) triples) limits the output to those rows and returns a
+    dict mapping each triple to its output vector.  Otherwise returns a dict
+    with "out" [B, N, H, d] and the stage results ("o_s", "o_l", "H", "Z",
+    "s", "idx", "orders", "q_used", "k_used").
     """
     F, Hg, Wg = grid
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
     B, N, H, d = q.shape
     if N != F * Hg * Wg:
         raise ValueError("N must equal F*Hg*Wg")
     scale = 1.0 / np.sqrt(d) if not softmax_scale or softmax_scale <= 0 else softmax_scale
-    if rope:
-        q = round_to_io(rope_3d(q, F, Hg, Wg, rope_dims, rope_base), io_dtype)
-        k = round_to_io(rope_3d(k, F, Hg, Wg, rope_dims, rope_base), io_dtype)
     orders = [head_order(int(head_kinds[h]), F, Hg, Wg) for h in range(H)]
     inv = [np.argsort(o) for o in orders]
 
     s = np.empty(B)
-    Hs = np.empty((B, H, d, v.shape[3]))
-    Zs = np.empty((B, H, d))
     for b in range(B):
         s[b] = gate(x[b], gate_w, gate_b) if s_override is None else float(s_override[b])
-        for h in range(H):
-            Hs[b, h], Zs[b, h] = linear_state(k[b, :, h], v[b, :, h])
 
-    idx_all = {}
+    cache = {}
+
+    def head(b, h):
+        """Token-order q, k (RoPE'd if enabled), v, working-order copies and
+        the linear state of one (sample, head)."""
+        key = (b, h)
+        if key not in cache:
+            qh = np.asarray(q[b:b + 1, :, h:h + 1], np.float64)
+            kh = np.asarray(k[b:b + 1, :, h:h + 1], np.float64)
+            if rope:
+                qh = round_to_io(rope_3d(qh, F, Hg, Wg, rope_dims, rope_base), io_dtype)
+                kh = round_to_io(rope_3d(kh, F, Hg, Wg, rope_dims, rope_base), io_dtype)
+            qh, kh = qh[0, :, 0], kh[0, :, 0]
+            vh = np.asarray(v[b, :, h], np.float64)
+            Hm, Zv = linear_state(kh, vh)
+            o = orders[h]
+            cache[key] = dict(q=qh, k=kh, v=vh, qw=qh[o], kw=kh[o], vw=vh[o], H=Hm, Z=Zv, idx=None)
+            if int(head_kinds[h]) == HEAD_TOPK:
+                c = cache[key]
+                c["idx"] = topk_blocks(block_means(c["qw"], block), block_means(c["kw"], block), topk)
+        return cache[key]
+
     if rows is not None:
         result = {}
-        work = {}
         for (b, n, h) in rows:
-            kind = int(head_kinds[h])
-            key = (b, h)
-            if key not in work:
-                work[key] = tuple(t[b, orders[h], h] for t in (q, k, v))
-            qw, kw, vw = work[key]
-            if kind == HEAD_TOPK and key not in idx_all:
-                idx_all[key] = topk_blocks(block_means(qw, block), block_means(kw, block), topk)
-            o_s, _ = sparse_attention_head(kind, qw, kw, vw, r=window_radius, bs=block,
-                                           k=topk, scale=scale, rows=[int(inv[h][n])],
-                                           idx=idx_all.get(key))
-            o_l = linear_apply(q[b, n:n + 1, h], Hs[b, h], Zs[b, h], linear_eps)
+            c = head(b, h)
+            o_s, _ = sparse_attention_head(int(head_kinds[h]), c["qw"], c["kw"], c["vw"],
+                                           r=window_radius, bs=block, k=topk, scale=scale,
+                                           rows=[int(inv[h][n])], idx=c["idx"])
+            o_l = linear_apply(c["q"][n:n + 1], c["H"], c["Z"], linear_eps)
             result[(b, n, h)] = combine(o_s, o_l, w_p, s[b])[0]
         return result
 
     out = np.empty((B, N, H, v.shape[3]))
     o_s_all = np.empty_like(out)
     o_l_all = np.empty_like(out)
+    Hs = np.empty((B, H, d, v.shape[3]))
+    Zs = np.empty((B, H, d))
+    q_used = np.empty((B, N, H, d))
+    k_used = np.empty((B, N, H, d))
+    idx_all = {}
     for b in range(B):
         for h in range(H):
+            c = head(b, h)
             kind = int(head_kinds[h])
-            qw, kw, vw = (t[b, orders[h], h] for t in (q, k, v))
-            o_s_w, idx = sparse_attention_head(kind, qw, kw, vw, r=window_radius, bs=block,
-                                               k=topk, scale=scale)
-            if idx is not None:
-                idx_all[(b, h)] = idx
+            o_s_w, _ = sparse_attention_head(kind, c["qw"], c["kw"], c["vw"], r=window_radius,
+                                             bs=block, k=topk, scale=scale, idx=c["idx"])
+            if c["idx"] is not None:
+                idx_all[(b, h)] = c["idx"]
             o_s = o_s_w[inv[h]]  # back to token order
-            o_l = linear_apply(q[b, :, h], Hs[b, h], Zs[b, h], linear_eps)
+            o_l = linear_apply(c["q"], c["H"], c["Z"], linear_eps)
             o_s_all[b, :, h] = o_s
             o_l_all[b, :, h] = o_l
             out[b, :, h] = combine(o_s, o_l, w_p, s[b])
+            Hs[b, h], Zs[b, h] = c["H"], c["Z"]
+            q_used[b, :, h], k_used[b, :, h] = c["q"], c["k"]
+            del cache[(b, h)]
     return {"out": out, "o_s": o_s_all, "o_l": o_l_all, "H": Hs, "Z": Zs, "s": s,
-            "idx": idx_all, "orders": orders, "q_used": q, "k_used": k}
+            "idx": idx_all, "orders": orders, "q_used": q_used, "k_used": k_used}
