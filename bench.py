@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--workload", default="480p-stswa-h12")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a "
+                         "known-size reference for the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -160,6 +163,15 @@ def main():
     ms = wall * 1e3 / args.steps
     attn_avg = attn_ms / max(calls, 1)
     achieved = flops / (attn_avg * 1e-3) / 1e12
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     traffic = None
     if os.path.exists(PROFILE_COUNTERS):

@@ -143,7 +143,10 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16_t V0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t V1[TILE];
   const Geom &g = a.g;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, hl = lane >> 5, l32 = lane & 31;
+  // the wave index is uniform per wave; readfirstlane lets the compiler use
+  // it as a scalar (the DMA destination in M0 must be wave-uniform)
+  const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
 
   const int tile = xcd_order(blockIdx.x, a.n_blocks);
   const int qt = tile % a.tiles_per_head;
@@ -188,20 +191,34 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     const int kb = sel[it];
     return (kb >= 0 && kb < g.nb) ? kb * g.block : g.N;
   };
-  // DMA one K and one V tile into buffer `buf`: op i of wave w fills LDS
-  // rows 4*(i*NW + w) .. +3; lane l writes physical unit l%16 of row l/16,
-  // so it fetches logical unit (l%16) ^ kv_swz(row).  Rows past N re-read
-  // row N-1 (finite data; those keys are masked).
+  // DMA one K and one V tile into a buffer: op i of wave w fills LDS rows
+  // 4*(i*NW + w) .. +3; lane l writes physical unit l%16 of row l/16, so it
+  // fetches logical unit (l%16) ^ kv_swz(row).  K and V are in the working
+  // layout (rows of this (b, h) are sN elements apart, checked on the host),
+  // so a lane's address is a per-head base plus a lane-constant offset.
+  // Rows past N (only in the last tile) re-read row N-1: finite data whose
+  // keys are masked.
+  const bf16_t *kbh = kbase + (long long)b * a.k.sB + (long long)h * a.k.sH;
+  const bf16_t *vbh = vbase + (long long)b * a.v.sB + (long long)h * a.v.sH;
+  const int sN = int(a.k.sN);
+  int dma_row[DMA_PER_WAVE], dma_off[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    dma_row[i] = 4 * (i * NW + w) + (lane >> 4);
+    dma_off[i] = dma_row[i] * sN + (((lane & 15) ^ kv_swz(dma_row[i])) << 3);
+  }
   auto issue_tile = [&](int k0, bf16_t *__restrict__ Kd, bf16_t *__restrict__ Vd) {
+    const bool tail = k0 + kBN > g.N;
+    const bf16_t *kt = kbh + (long long)k0 * sN;
+    const bf16_t *vt = vbh + (long long)k0 * sN;
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int row = 4 * (i * NW + w) + (lane >> 4);
-      const int u = (lane & 15) ^ kv_swz(row);
-      const int j = min(k0 + row, g.N - 1);
+      int off = dma_off[i];
+      if (tail) off -= (k0 + dma_row[i] - min(k0 + dma_row[i], g.N - 1)) * sN;
       lds_void *kd = (lds_void *)(Kd + (4 * (i * NW + w)) * kD);
       lds_void *vd = (lds_void *)(Vd + (4 * (i * NW + w)) * kD);
-      __builtin_amdgcn_global_load_lds((const void *)(kbase + row_offset(g, a.k, b, h, j) + u * 8), kd, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(vbase + row_offset(g, a.v, b, h, j) + u * 8), vd, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(kt + off), kd, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(vt + off), vd, 16, 0, 0);
     }
   };
 
@@ -246,12 +263,18 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     // S^T[key][query] = K Q^T, two blocks of 32 keys
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < 8; ks += 2) {
+      bf16x8 ka[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *(const bf16x8 *)(Ks + kb * 32 * kD + k_lane + 16 * (ks ^ k_x));
-        s[kb] = mfma_32x32x16(ka, qf[ks], s[kb]);
-      }
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          ka[u][kb] = *(const bf16x8 *)(Ks + kb * 32 * kD + k_lane + 16 * ((ks + u) ^ k_x));
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_32x32x16(ka[u][kb], qf[ks + u], s[kb]);
+    }
     float mx = -INFINITY;
     if (full) {
 #pragma unroll
@@ -264,7 +287,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const bool keep = j < g.N && (a.topk_mode || abs(pq - j) <= g.r);
+          // bitwise, not short-circuit: keeps the mask a select, not a branch
+          const bool keep = (j < g.N) & (bool(a.topk_mode) | (abs(pq - j) <= g.r));
           s[kb][r] = keep ? s[kb][r] : -INFINITY;
           mx = fmaxf(mx, s[kb][r]);
         }
@@ -302,18 +326,17 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     // matching V^T operand comes from two transposing reads (r = 0, 1).
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+      // all four d-blocks' operands of this k-step first, then the MFMAs
+      typedef __attribute__((ext_vector_type(8))) short s16x8;
+      s16x8 va[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        s16x4 part[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-          part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4 *)(Vs + 16 * kk * kD + v_off[r][db]));
-        typedef __attribute__((ext_vector_type(8))) short s16x8;
-        s16x8 va = {part[0][0], part[0][1], part[0][2], part[0][3],
-                    part[1][0], part[1][1], part[1][2], part[1][3]};
-        o[db] = mfma_32x32x16(*(const bf16x8 *)&va, pb[kk], o[db]);
+        const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Vs + 16 * kk * kD + v_off[0][db]));
+        const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Vs + 16 * kk * kD + v_off[1][db]));
+        va[db] = s16x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(*(const bf16x8 *)&va[db], pb[kk], o[db]);
     }
   };
 
@@ -445,6 +468,14 @@ hipError_t launch_bf16(AttnArgs a, hipStream_t st) {
 }
 }  // namespace
 
+// The bf16 kernel streams K and V from a layout whose rows of one (b, h)
+// are contiguous and equally spaced (the working layout), with the same
+// strides for both.
+static bool kv_streamable(const View &kv, const View &vv) {
+  return !kv.perm && !vv.perm && kv.sB == vv.sB && kv.sH == vv.sH && kv.sN == vv.sN &&
+         kv.sN < (1ll << 20);
+}
+
 hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv,
                               const int32_t *idx, float *o_s, hipStream_t st) {
   if (!bf16) {
@@ -455,6 +486,7 @@ hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv
       attn_f32_kernel<64><<<grid, 64, 0, st>>>(g, qv, kv, vv, idx, o_s);
     return hipGetLastError();
   }
+  if (!kv_streamable(kv, vv)) return hipErrorInvalidValue;
   AttnArgs a = {};
   a.g = g;
   a.q = qv;
@@ -467,6 +499,7 @@ hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv
 
 hipError_t launch_attn_fused(const Geom &g, View qv, View kv, View vv, const int32_t *idx,
                              const bf16_t *hp, const float *z, View outv, hipStream_t st) {
+  if (!kv_streamable(kv, vv)) return hipErrorInvalidValue;
   AttnArgs a = {};
   a.g = g;
   a.q = qv;
