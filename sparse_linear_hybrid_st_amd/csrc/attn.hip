@@ -198,27 +198,32 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   // so a lane's address is a per-head base plus a lane-constant offset.
   // Rows past N (only in the last tile) re-read row N-1: finite data whose
   // keys are masked.
-  const bf16_t *kbh = kbase + (long long)b * a.k.sB + (long long)h * a.k.sH;
-  const bf16_t *vbh = vbase + (long long)b * a.v.sB + (long long)h * a.v.sH;
+  // The DMAs are buffer loads: a descriptor per head (base, byte extent) in
+  // SGPRs, the tile start as a scalar offset and a lane-constant byte
+  // offset, so issuing a tile costs no per-lane address arithmetic.
   const int sN = int(a.k.sN);
-  int dma_row[DMA_PER_WAVE], dma_off[DMA_PER_WAVE];
+  const unsigned head_bytes = unsigned((long long)(g.N - 1) * sN * 2 + kD * 2);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(kbase + (long long)b * a.k.sB + (long long)h * a.k.sH), 0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(vbase + (long long)b * a.v.sB + (long long)h * a.v.sH), 0, head_bytes, 0x00020000);
+  int dma_row[DMA_PER_WAVE], dma_off[DMA_PER_WAVE];  // row in tile, byte offset
 #pragma unroll
   for (int i = 0; i < DMA_PER_WAVE; ++i) {
     dma_row[i] = 4 * (i * NW + w) + (lane >> 4);
-    dma_off[i] = dma_row[i] * sN + (((lane & 15) ^ kv_swz(dma_row[i])) << 3);
+    dma_off[i] = 2 * (dma_row[i] * sN + (((lane & 15) ^ kv_swz(dma_row[i])) << 3));
   }
   auto issue_tile = [&](int k0, bf16_t *__restrict__ Kd, bf16_t *__restrict__ Vd) {
     const bool tail = k0 + kBN > g.N;
-    const bf16_t *kt = kbh + (long long)k0 * sN;
-    const bf16_t *vt = vbh + (long long)k0 * sN;
+    const unsigned soff = unsigned(k0) * unsigned(sN) * 2u;
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       int off = dma_off[i];
-      if (tail) off -= (k0 + dma_row[i] - min(k0 + dma_row[i], g.N - 1)) * sN;
+      if (tail) off -= 2 * (k0 + dma_row[i] - min(k0 + dma_row[i], g.N - 1)) * sN;
       lds_void *kd = (lds_void *)(Kd + (4 * (i * NW + w)) * kD);
       lds_void *vd = (lds_void *)(Vd + (4 * (i * NW + w)) * kD);
-      __builtin_amdgcn_global_load_lds((const void *)(kt + off), kd, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(vt + off), vd, 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, unsigned(off), soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, unsigned(off), soff, 0, 0);
     }
   };
 
@@ -294,9 +299,13 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
         }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    // rescale only when some lane's max moved (the common case late in a row is no change)
-    if (__any(m_new > m_run)) {
+    // The running offset m_run only has to bound the row's scores loosely:
+    // O and l share it, so the final O / l is exact whatever its value.  It
+    // is raised (and O, l rescaled) only when a score exceeds it by more
+    // than 8 in log2 units, so later probabilities stay below 2^8 (no
+    // overflow in fp32 sums or in bf16) while the rescale runs on few tiles.
+    if (__any((mx - m_run) * c2 > 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
       const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       l_run *= alpha;
 #pragma unroll
