@@ -112,8 +112,9 @@ salad_status salad_permute(const salad_problem *p, int apply_rope, int inverse,
  * kb for query block qb = qbar[qb] . kbar[kb] in float64; keep the p->topk
  * highest, equal scores resolved toward the lower block index; write them
  * ascending to idx [B, H, nb, topk] (int32, nb = ceil(N/block)).  Rows of
- * non-Top-K heads are not written.  qbar/kbar (float64 [B,H,nb,d]) receive
- * the means when non-NULL, else they live in the workspace. */
+ * non-Top-K heads are not written.  qbar/kbar (float64 [B,H,nb,d]) also
+ * receive the means when non-NULL.  The workspace (salad_workspace_size)
+ * holds the means and the float64 block scores. */
 salad_status salad_block_select(const salad_problem *p, const void *qw, const void *kw,
                                 int32_t *idx, double *qbar, double *kbar,
                                 void *ws, size_t ws_bytes, hipStream_t stream);

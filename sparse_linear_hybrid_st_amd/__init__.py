@@ -180,7 +180,7 @@ def salad_permute(p: Problem, apply_rope: int, inverse: int, src, dst, stream=No
                                _ptr(src, "src", n, dt), _ptr(dst, "dst", n, dt), _stream(stream)))
 
 
-def salad_block_select(p: Problem, qw, kw, idx, qbar=None, kbar=None, ws=None, stream=None):
+def salad_block_select(p: Problem, qw, kw, idx, ws, qbar=None, kbar=None, stream=None):
     import torch
     n, _ = _sizes(p)
     dt = _io_dtype(p)
@@ -190,7 +190,7 @@ def salad_block_select(p: Problem, qw, kw, idx, qbar=None, kbar=None, ws=None, s
         ctypes.byref(p), _ptr(qw, "qw", n, dt), _ptr(kw, "kw", n, dt),
         _ptr(idx, "idx", p.batch * p.n_heads * nb * p.topk, torch.int32),
         _ptr(qbar, "qbar", means, torch.float64), _ptr(kbar, "kbar", means, torch.float64),
-        _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def salad_sparse_attn(p: Problem, qw, kw, vw, idx, o_s, stream=None):

@@ -123,7 +123,7 @@ salad_status validate(const salad_problem *p, Info *inf) {
 // block selection, Hp and Z; for f32 (staged) working copies of Q/K/V, the
 // selection, O_s, O_l, H and Z.  Both end with the gate values.
 struct Plan {
-  size_t wq, wk, wv, idx, o_s, o_l, h, z, s, hp;
+  size_t wq, wk, wv, idx, o_s, o_l, h, z, s, hp, rope_tab;
   size_t total_stage, total_forward;
 };
 
@@ -134,7 +134,7 @@ Plan plan(const Info &inf) {
   Plan pl = {};
   const size_t BH = size_t(g.B) * g.H;
   const size_t rows = BH * g.N;
-  const size_t means = inf.any_topk ? 2 * up(BH * g.nb * g.D * sizeof(double)) : 0;
+  const size_t means = inf.any_topk ? up(select_ws_bytes(g)) : 0;
   const size_t lin = up(BH * linear_splits(g) * (size_t(g.D) * g.D + g.D) * sizeof(float));
   const size_t gate = up(gate_ws_bytes(g));
   pl.total_stage = means > lin ? (means > gate ? means : gate) : (lin > gate ? lin : gate);
@@ -160,6 +160,7 @@ Plan plan(const Info &inf) {
     pl.z = off; off += up(BH * g.D * sizeof(float));
   }
   pl.s = off; off += up(size_t(g.B) * sizeof(float));
+  pl.rope_tab = off; off += inf.rope ? up(size_t(rope_table_entries(g)) * 16) : 0;
   pl.total_forward = off;
   return pl;
 }
@@ -195,6 +196,15 @@ View boundary_view(const Geom &g, const void *base) {
   v.sN = (long long)g.H * g.D;
   v.perm = 1;
   return v;
+}
+
+// Carve the selection scratch: Q means, K means, scores (see select_ws_bytes).
+void select_regions(const Geom &g, void *ws, double **qm, double **km, double **sc) {
+  const size_t one = up(size_t(g.B) * g.H * g.nb * g.D * sizeof(double));
+  char *w = (char *)ws;
+  *qm = (double *)w;
+  *km = (double *)(w + one);
+  *sc = (double *)(w + 2 * one);
 }
 
 View working_view(const Geom &g, const void *base) {
@@ -284,16 +294,15 @@ salad_status salad_block_select(const salad_problem *p, const void *qw, const vo
   CHECK(need(idx, "idx"));
   if (!inf.any_topk) return fail(SALAD_ERR_SHAPE, "no Top-K head in the problem");
   const Geom &g = inf.g;
-  const size_t one = up(size_t(g.B) * g.H * g.nb * g.D * sizeof(double));
-  const size_t needed = (qbar ? 0 : one) + (kbar ? 0 : one);
-  CHECK(need_ws(ws, ws_bytes, needed));
+  CHECK(need_ws(ws, ws_bytes, up(select_ws_bytes(g))));
   if (qbar) CHECK(need(qbar, "qbar"));
   if (kbar) CHECK(need(kbar, "kbar"));
-  char *w = (char *)ws;
-  double *qm = qbar ? qbar : (double *)w;
-  double *km = kbar ? kbar : (double *)(w + (qbar ? 0 : one));
+  double *qm, *km, *scores;
+  select_regions(g, ws, &qm, &km, &scores);
+  if (qbar) qm = qbar;
+  if (kbar) km = kbar;
   return hip_status(launch_block_select(g, inf.bf16, working_view(g, qw), working_view(g, kw), qm, km,
-                                        idx, stream),
+                                        scores, idx, stream),
                     "salad_block_select");
 }
 
@@ -420,8 +429,10 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
     View qv = boundary_view(g, q), kv_in = boundary_view(g, k);
     bf16_t *k_copy = (bf16_t *)wk;
     if (rope) {
-      if ((e = launch_permute(g, 1, 1, 0, q, wq, stream)) != hipSuccess ||
-          (e = launch_permute(g, 1, 1, 0, k, wk, stream)) != hipSuccess)
+      double2 *tab = (double2 *)(w + pl.rope_tab);
+      if ((e = launch_rope_table(g, tab, stream)) != hipSuccess ||
+          (e = launch_permute(g, 1, 1, 0, q, wq, stream, tab)) != hipSuccess ||
+          (e = launch_permute(g, 1, 1, 0, k, wk, stream, tab)) != hipSuccess)
         return hip_status(e, "salad_attn_forward: rope");
       qv = working_view(g, wq);
       kv_in = working_view(g, wk);
@@ -434,8 +445,9 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
         (e = launch_linear_finalize(g, 1, (const float *)scratch, w_p, s, hm, hp, zv, stream)) != hipSuccess)
       return hip_status(e, "salad_attn_forward: linear state");
     if (inf.any_topk) {
-      const size_t one = up(size_t(g.B) * g.H * g.nb * g.D * sizeof(double));
-      e = launch_block_select(g, 1, qv, kv, (double *)scratch, (double *)(w + one), idx, stream);
+      double *qm, *km, *sc;
+      select_regions(g, scratch, &qm, &km, &sc);
+      e = launch_block_select(g, 1, qv, kv, qm, km, sc, idx, stream);
       if (e != hipSuccess) return hip_status(e, "salad_attn_forward: block select");
     }
     if ((e = prof_mark(0, stream)) != hipSuccess ||
@@ -446,14 +458,18 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
   }
 
   // f32: staged path through working copies
-  if ((e = launch_permute(g, inf.bf16, rope, 0, q, wq, stream)) != hipSuccess ||
-      (e = launch_permute(g, inf.bf16, rope, 0, k, wk, stream)) != hipSuccess ||
+  double2 *tab = rope ? (double2 *)(w + pl.rope_tab) : nullptr;
+  if (rope && (e = launch_rope_table(g, tab, stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_forward: rope");
+  if ((e = launch_permute(g, inf.bf16, rope, 0, q, wq, stream, tab)) != hipSuccess ||
+      (e = launch_permute(g, inf.bf16, rope, 0, k, wk, stream, tab)) != hipSuccess ||
       (e = launch_permute(g, inf.bf16, 0, 0, v, wv, stream)) != hipSuccess)
     return hip_status(e, "salad_attn_forward: permute");
   const View qv = working_view(g, wq), kv = working_view(g, wk), vv = working_view(g, wv);
   if (inf.any_topk) {
-    const size_t one = up(size_t(g.B) * g.H * g.nb * g.D * sizeof(double));
-    e = launch_block_select(g, inf.bf16, qv, kv, (double *)scratch, (double *)(w + one), idx, stream);
+    double *qm, *km, *sc;
+    select_regions(g, scratch, &qm, &km, &sc);
+    e = launch_block_select(g, inf.bf16, qv, kv, qm, km, sc, idx, stream);
     if (e != hipSuccess) return hip_status(e, "salad_attn_forward: block select");
   }
   if ((e = prof_mark(0, stream)) != hipSuccess ||

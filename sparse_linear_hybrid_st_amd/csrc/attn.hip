@@ -138,10 +138,14 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   // objects the compiler can tell that the DMA into one buffer does not
   // feed the reads of the other, so it does not wait for the next tile's
   // DMA before computing on the current one.
+  // Top-K workgroups (2 waves) use one buffer: 32 KB of LDS lets four of
+  // them share a CU (2 waves per SIMD), and the other workgroups cover each
+  // one's DMA wait; window workgroups (4 waves) double-buffer.
+  constexpr bool SINGLE = (NW == 2);
   __shared__ __attribute__((aligned(1024))) bf16_t K0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16_t K1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t K1[SINGLE ? 8 : TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t V0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16_t V1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t V1[SINGLE ? 8 : TILE];
   const Geom &g = a.g;
   // the wave index is uniform per wave; readfirstlane lets the compiler use
   // it as a scalar (the DMA destination in M0 must be wave-uniform)
@@ -356,8 +360,20 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   // Tile starts are read before each DMA is issued and carried along, so no
   // global load (and its wait) sits between a DMA and the LDS reads.
   int k_cur = n_tiles > 0 ? tile_start(0) : 0;
-  if (n_tiles > 0) issue_tile(k_cur, K0, V0);
-  for (int it = 0; it < n_tiles; it += 2) {
+  if constexpr (SINGLE) {
+    // one buffer: DMA, wait, compute; other workgroups on the CU cover the DMA
+    for (int it = 0; it < n_tiles; ++it) {
+      if (it > 0) __syncthreads();  // every wave is done reading the buffer
+      issue_tile(k_cur, K0, V0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const int k_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
+      compute(k_cur, K0, V0);
+      k_cur = k_nxt;
+    }
+  } else {
+    if (n_tiles > 0) issue_tile(k_cur, K0, V0);
+    for (int it = 0; it < n_tiles; it += 2) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     const int k_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
@@ -370,6 +386,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     if (it + 2 < n_tiles) issue_tile(k_nn, K0, V0);
     compute(k_nxt, K1, V1);
     k_cur = k_nn;
+  }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);

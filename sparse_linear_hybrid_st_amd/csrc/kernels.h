@@ -9,11 +9,12 @@
 
 namespace salad {
 
-// Query blocks scored per workgroup by the Top-K selection kernel (bounded
-// by its LDS use: qpb * (d + nb) doubles).
-inline int topk_queries_per_group(int nb, int d) {
-  int q = int((64 * 1024) / (size_t(d + nb) * sizeof(double)));
-  return q < 1 ? 1 : (q > 8 ? 8 : q);
+// Workspace of the Top-K selection: block means of Q and K (fp64
+// [B*H][nb][d] each) and the block scores (fp64 [B*H][nb][nb]).
+inline size_t select_ws_bytes(const Geom &g) {
+  const size_t BH = size_t(g.B) * g.H;
+  return 2 * ((BH * g.nb * g.D * sizeof(double) + 255) & ~size_t(255)) +
+         ((BH * g.nb * g.nb * sizeof(double) + 255) & ~size_t(255));
 }
 
 // Token chunks per (b, h) used by the split-N linear-state reduction.
@@ -32,10 +33,14 @@ inline int gate_splits(const Geom &g) {
 // Workspace bytes of the gate: one double per (sample, row chunk).
 inline size_t gate_ws_bytes(const Geom &g) { return size_t(g.B) * gate_splits(g) * sizeof(double); }
 
+// RoPE (cos, sin) table in fp64: rope_table_entries(g) double2 entries.
+int rope_table_entries(const Geom &g);
+hipError_t launch_rope_table(const Geom &g, double2 *table, hipStream_t st);
+// table: optional RoPE table (NULL: angles computed per element; same values).
 hipError_t launch_permute(const Geom &g, int bf16, int rope, int inverse, const void *src,
-                          void *dst, hipStream_t st);
+                          void *dst, hipStream_t st, const double2 *table = nullptr);
 hipError_t launch_block_select(const Geom &g, int bf16, View qv, View kv, double *qbar,
-                               double *kbar, int32_t *idx, hipStream_t st);
+                               double *kbar, double *scores, int32_t *idx, hipStream_t st);
 // partial: [B*H][S][D*D + D] floats of workspace (S = linear_splits).
 hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float *partial,
                                float *h, float *z, hipStream_t st);

@@ -14,9 +14,34 @@
 
 namespace salad {
 
+// Entry (axis, pos, i) of the RoPE table: (cos, sin) of pos * base^(-2i/D_axis),
+// computed by rope_cs, stored at rope_index(axis, pos, i).
+__device__ __forceinline__ int rope_index(const Geom &g, int axis, int pos, int i) {
+  const int off1 = g.F * (g.rope_dims[0] >> 1);
+  const int off2 = off1 + g.Hg * (g.rope_dims[1] >> 1);
+  const int base = axis == 0 ? 0 : (axis == 1 ? off1 : off2);
+  return base + pos * (g.rope_dims[axis] >> 1) + i;
+}
+
+__global__ void __launch_bounds__(256) rope_table_kernel(Geom g, double2 *__restrict__ table) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int n0 = g.F * (g.rope_dims[0] >> 1), n1 = g.Hg * (g.rope_dims[1] >> 1);
+  const int n2 = g.Wg * (g.rope_dims[2] >> 1);
+  int axis, r;
+  if (e < n0) { axis = 0; r = e; }
+  else if (e < n0 + n1) { axis = 1; r = e - n0; }
+  else if (e < n0 + n1 + n2) { axis = 2; r = e - n0 - n1; }
+  else return;
+  const int half = g.rope_dims[axis] >> 1;
+  double c, sn;
+  rope_cs(r / half, r % half, g.rope_dims[axis], double(g.rope_base), &c, &sn);
+  table[e] = make_double2(c, sn);
+}
+
 template <typename T, bool ROPE>
 __global__ void __launch_bounds__(256) permute_kernel(Geom g, const T *__restrict__ src,
-                                                      T *__restrict__ dst, int inverse) {
+                                                      T *__restrict__ dst, int inverse,
+                                                      const double2 *__restrict__ table) {
   constexpr int VEC = 16 / sizeof(T);
   const int per_row = g.D / VEC;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -50,7 +75,13 @@ __global__ void __launch_bounds__(256) permute_kernel(Geom g, const T *__restric
     int e = c + t, axis = 0, off = 0;
     while (axis < 2 && e >= off + g.rope_dims[axis]) { off += g.rope_dims[axis]; ++axis; }
     double cs, sn;
-    rope_cs(pos3[axis], (e - off) >> 1, g.rope_dims[axis], double(g.rope_base), &cs, &sn);
+    if (table) {
+      const double2 v = table[rope_index(g, axis, pos3[axis], (e - off) >> 1)];
+      cs = v.x;
+      sn = v.y;
+    } else {
+      rope_cs(pos3[axis], (e - off) >> 1, g.rope_dims[axis], double(g.rope_base), &cs, &sn);
+    }
     double a = double(io<T>::ld(&in[t])), bb = double(io<T>::ld(&in[t + 1]));
     out[t] = io<T>::from_f64(a * cs - bb * sn);
     out[t + 1] = io<T>::from_f64(a * sn + bb * cs);
@@ -58,21 +89,31 @@ __global__ void __launch_bounds__(256) permute_kernel(Geom g, const T *__restric
   *reinterpret_cast<u32x4 *>(dst + woff) = *reinterpret_cast<const u32x4 *>(out);
 }
 
+int rope_table_entries(const Geom &g) {
+  return g.F * (g.rope_dims[0] / 2) + g.Hg * (g.rope_dims[1] / 2) + g.Wg * (g.rope_dims[2] / 2);
+}
+
+hipError_t launch_rope_table(const Geom &g, double2 *table, hipStream_t st) {
+  const int n = rope_table_entries(g);
+  rope_table_kernel<<<(n + 255) / 256, 256, 0, st>>>(g, table);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const Geom &g, int dtype_bf16, int rope, int inverse, const void *src,
-                          void *dst, hipStream_t st) {
+                          void *dst, hipStream_t st, const double2 *table) {
   const int vec = dtype_bf16 ? 8 : 4;
   const long long threads = (long long)g.B * g.H * g.N * (g.D / vec);
   const unsigned grid = unsigned((threads + 255) / 256);
   if (dtype_bf16) {
     if (rope)
-      permute_kernel<bf16_t, true><<<grid, 256, 0, st>>>(g, (const bf16_t *)src, (bf16_t *)dst, 0);
+      permute_kernel<bf16_t, true><<<grid, 256, 0, st>>>(g, (const bf16_t *)src, (bf16_t *)dst, 0, table);
     else
-      permute_kernel<bf16_t, false><<<grid, 256, 0, st>>>(g, (const bf16_t *)src, (bf16_t *)dst, inverse);
+      permute_kernel<bf16_t, false><<<grid, 256, 0, st>>>(g, (const bf16_t *)src, (bf16_t *)dst, inverse, nullptr);
   } else {
     if (rope)
-      permute_kernel<float, true><<<grid, 256, 0, st>>>(g, (const float *)src, (float *)dst, 0);
+      permute_kernel<float, true><<<grid, 256, 0, st>>>(g, (const float *)src, (float *)dst, 0, table);
     else
-      permute_kernel<float, false><<<grid, 256, 0, st>>>(g, (const float *)src, (float *)dst, inverse);
+      permute_kernel<float, false><<<grid, 256, 0, st>>>(g, (const float *)src, (float *)dst, inverse, nullptr);
   }
   return hipGetLastError();
 }

@@ -1,5 +1,5 @@
 // Top-K block selection: block-mean pooling of Q and K, block scores and
-// the k best key blocks per query block.
+// the k best key blocks per query block (fp64 scores, bitonic sort).
 //
 // Source: ijyty.com/news/870645, section 1.2 -- cut the tokens into blocks,
 // take each block's mean, compare queries with the key-block means and keep
@@ -51,69 +51,119 @@ __global__ void __launch_bounds__(256) block_mean_kernel(Geom g, View qv, View k
   }
 }
 
-// Scores and selection.  One workgroup handles `qpb` query blocks of one
-// (b, h): scores[q][kb] = qbar[q] . kbar[kb] (float64, LDS), then for each
-// query block a candidate kb is kept iff fewer than k candidates beat it
-// (higher score, or equal score and lower index); kept indices are written
-// ascending via a prefix count.
-__global__ void __launch_bounds__(256) topk_select_kernel(Geom g, const double *__restrict__ qbar,
+// Block scores S[qb][kb] = qbar[qb] . kbar[kb] for every Top-K (b, h), as a
+// tiled fp64 product: workgroup (tile_q, tile_k, bh) computes a 32 x 32 tile,
+// staging 32-column slices of both operands in LDS; thread t owns rows
+// 4*(t/32)..+3 at column t%32.  Each product is a plain left-to-right fp64
+// sum over the d features.
+__global__ void __launch_bounds__(256) block_score_kernel(Geom g, const double *__restrict__ qbar,
                                                           const double *__restrict__ kbar,
-                                                          int32_t *__restrict__ idx, int qpb) {
-  extern __shared__ double smem[];
-  const int bh = blockIdx.y;
-  const int h = bh % g.H;
+                                                          double *__restrict__ scores) {
+  const int bh = blockIdx.z, h = bh % g.H;
   if (!bit(g.topk, h)) return;
   const int nb = g.nb, D = g.D, t = threadIdx.x;
-  const int qb0 = blockIdx.x * qpb;
-  const int nq = min(qpb, nb - qb0);
-  double *qs = smem;              // [qpb][D]
-  double *sc = smem + qpb * D;    // [qpb][nb]
-  __shared__ int wave_count[4];
-  for (int i = t; i < nq * D; i += 256) qs[i] = qbar[((long long)bh * nb + qb0) * D + i];
-  __syncthreads();
-  const double *kb_base = kbar + (long long)bh * nb * D;
-  for (int kb = t; kb < nb; kb += 256) {
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const double *kr = kb_base + (long long)kb * D;
-    for (int c = 0; c < D; ++c) {
-      double kvv = kr[c];
-      for (int q = 0; q < nq; ++q) acc[q] = fma(qs[q * D + c], kvv, acc[q]);
+  const int q0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
+  __shared__ double qs[32][33];
+  __shared__ double ks[32][33];
+  const double *qb = qbar + (long long)bh * nb * D;
+  const double *kb = kbar + (long long)bh * nb * D;
+  const int r0 = 4 * (t >> 5), c = t & 31;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int f0 = 0; f0 < D; f0 += 32) {
+    __syncthreads();
+    for (int e = t; e < 32 * 32; e += 256) {
+      const int r = e >> 5, f = e & 31;
+      qs[r][f] = (q0 + r < nb) ? qb[(long long)(q0 + r) * D + f0 + f] : 0.0;
+      ks[r][f] = (k0 + r < nb) ? kb[(long long)(k0 + r) * D + f0 + f] : 0.0;
     }
-    for (int q = 0; q < nq; ++q) sc[q * nb + kb] = acc[q];
+    __syncthreads();
+    for (int f = 0; f < 32; ++f) {
+      const double kv = ks[c][f];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) acc[a] = fma(qs[r0 + a][f], kv, acc[a]);
+    }
   }
-  __syncthreads();
-  const int lane = t & 63, wv = t >> 6;
-  for (int q = 0; q < nq; ++q) {
-    const double *s = sc + q * nb;
-    int32_t *dst = idx + ((long long)bh * nb + qb0 + q) * g.k;
-    int base_count = 0;  // kept candidates with a lower index than this pass
-    for (int j0 = 0; j0 < nb; j0 += 256) {
-      const int j = j0 + t;
-      bool keep = false;
-      if (j < nb) {
-        const double sj = s[j];
-        int beat = 0;
-        for (int i = 0; i < nb; ++i) {
-          const double si = s[i];
-          beat += (si > sj) || (si == sj && i < j);
-        }
-        keep = beat < g.k;
-      }
-      const uint64_t m = __ballot(keep);
-      if (lane == 0) wave_count[wv] = __popcll(m);
-      __syncthreads();
-      int before = base_count;
-      for (int w = 0; w < wv; ++w) before += wave_count[w];
-      before += __popcll(m & ((1ull << lane) - 1ull));
-      if (keep && before < g.k) dst[before] = j;  // NaN scores cannot overrun the row
-      base_count += wave_count[0] + wave_count[1] + wave_count[2] + wave_count[3];
-      __syncthreads();
-    }
+  if (k0 + c < nb) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      if (q0 + r0 + a < nb) scores[((long long)bh * nb + q0 + r0 + a) * nb + k0 + c] = acc[a];
   }
 }
 
+// Selection for one query block per workgroup: bitonic sort of the P =
+// next_pow2(nb) (score, block) pairs in LDS into the order "higher score
+// first, equal scores lower block first" (padding sorts last), flag the
+// first k blocks, then write the flagged block indices ascending with a
+// ballot prefix count.  The order is total, so the result does not depend on
+// the sort's internal schedule.
+__device__ __forceinline__ bool sel_before(double sa, int ia, double sb, int ib) {
+  return sa > sb || (sa == sb && ia < ib);
+}
+
+__global__ void __launch_bounds__(256) topk_sort_kernel(Geom g, const double *__restrict__ scores,
+                                                        int32_t *__restrict__ idx, int P) {
+  extern __shared__ double sel_smem[];
+  const int bh = blockIdx.y, h = bh % g.H;
+  if (!bit(g.topk, h)) return;
+  const int nb = g.nb, qb = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  double *key = sel_smem;                       // [P]
+  int *id = (int *)(sel_smem + P);              // [P]
+  unsigned char *flag = (unsigned char *)(id + P);  // [P]
+  __shared__ int wave_count[4];
+  const double *row = scores + ((long long)bh * nb + qb) * nb;
+  for (int j = t; j < P; j += 256) {
+    key[j] = j < nb ? row[j] : -INFINITY;
+    id[j] = j < nb ? j : 0x7fffffff;
+    flag[j] = 0;
+  }
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int p = t; p < (P >> 1); p += 256) {
+        const int i = 2 * p - (p & (stride - 1));
+        const int j = i + stride;
+        const double ki = key[i], kj = key[j];
+        const int ii = id[i], ij = id[j];
+        // ascending runs (i & size == 0) put the "before" element first
+        const bool first_i = ((i & size) == 0);
+        const bool swap = first_i ? sel_before(kj, ij, ki, ii) : sel_before(ki, ii, kj, ij);
+        if (swap) {
+          key[i] = kj;
+          key[j] = ki;
+          id[i] = ij;
+          id[j] = ii;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = t; r < g.k; r += 256) flag[id[r]] = 1;
+  __syncthreads();
+  int32_t *dst = idx + ((long long)bh * nb + qb) * g.k;
+  int base_count = 0;
+  for (int j0 = 0; j0 < nb; j0 += 256) {
+    const int j = j0 + t;
+    const bool keep = j < nb && flag[j];
+    const uint64_t m = __ballot(keep);
+    if (lane == 0) wave_count[wv] = __popcll(m);
+    __syncthreads();
+    int before = base_count;
+    for (int w2 = 0; w2 < wv; ++w2) before += wave_count[w2];
+    before += __popcll(m & ((1ull << lane) - 1ull));
+    if (keep && before < g.k) dst[before] = j;
+    base_count += wave_count[0] + wave_count[1] + wave_count[2] + wave_count[3];
+    __syncthreads();
+  }
+}
+
+int select_pow2(int nb) {
+  int P = 2;
+  while (P < nb) P <<= 1;
+  return P;
+}
+
 hipError_t launch_block_select(const Geom &g, int dtype_bf16, View qv, View kv, double *qbar,
-                               double *kbar, int32_t *idx, hipStream_t st) {
+                               double *kbar, double *scores, int32_t *idx, hipStream_t st) {
   dim3 grid1(g.nb, 2, g.B * g.H);
   if (dtype_bf16)
     block_mean_kernel<bf16_t><<<grid1, 256, 0, st>>>(g, qv, kv, qbar, kbar);
@@ -121,10 +171,17 @@ hipError_t launch_block_select(const Geom &g, int dtype_bf16, View qv, View kv, 
     block_mean_kernel<float><<<grid1, 256, 0, st>>>(g, qv, kv, qbar, kbar);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int qpb = topk_queries_per_group(g.nb, g.D);
-  dim3 grid2((g.nb + qpb - 1) / qpb, g.B * g.H);
-  size_t lds = size_t(qpb) * (g.D + g.nb) * sizeof(double);
-  topk_select_kernel<<<grid2, 256, lds, st>>>(g, qbar, kbar, idx, qpb);
+  dim3 grid2((g.nb + 31) / 32, (g.nb + 31) / 32, g.B * g.H);
+  block_score_kernel<<<grid2, 256, 0, st>>>(g, qbar, kbar, scores);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int P = select_pow2(g.nb);
+  const size_t lds = size_t(P) * (sizeof(double) + sizeof(int) + 1);
+  if (lds > 64 * 1024)
+    hipFuncSetAttribute((const void *)topk_sort_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        int(lds));
+  dim3 grid3(g.nb, g.B * g.H);
+  topk_sort_kernel<<<grid3, 256, lds, st>>>(g, scores, idx, P);
   return hipGetLastError();
 }
 

@@ -79,7 +79,8 @@ def test_block_select(name):
     idx = torch.full((w.batch, w.n_heads, nb, w.topk), -1, dtype=torch.int32, device="cuda")
     qbar = torch.zeros((w.batch, w.n_heads, nb, w.head_dim), dtype=torch.float64, device="cuda")
     kbar = torch.zeros_like(qbar)
-    S.salad_block_select(p, _to_dev_storage(qw, w), _to_dev_storage(kw, w), idx, qbar, kbar)
+    S.salad_block_select(p, _to_dev_storage(qw, w), _to_dev_storage(kw, w), idx, S.workspace(p),
+                         qbar, kbar)
     torch.cuda.synchronize()
     idx, qbar, kbar = idx.cpu().numpy(), qbar.cpu().numpy(), kbar.cpu().numpy()
     for b in range(w.batch):
