@@ -108,9 +108,9 @@ salad_status validate(const salad_problem *p, Info *inf) {
     if (sum != p->head_dim) return fail(SALAD_ERR_SHAPE, "rope_dims must sum to head_dim");
     if (!(p->rope_base > 0.f)) return fail(SALAD_ERR_SHAPE, "rope_base must be > 0");
   }
-  g.f_magic = 0;
-  if (g.F > 1 && (unsigned long long)N * g.F < (1ull << 32))
-    g.f_magic = uint32_t(((1ull << 32) + g.F - 1) / g.F);
+  g.fdF = make_fastdiv(uint32_t(g.F));
+  g.fdS = make_fastdiv(uint32_t(g.Hg * g.Wg));
+  g.fdW = make_fastdiv(uint32_t(g.Wg));
   inf->bf16 = p->io_dtype == SALAD_BF16;
   inf->rope = p->rope;
   inf->esize = inf->bf16 ? 2 : 4;

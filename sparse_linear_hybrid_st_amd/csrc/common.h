@@ -65,6 +65,27 @@ template <> struct io<bf16_t> {
 
 // ---- geometry ------------------------------------------------------------
 
+// Division by a runtime constant d >= 1: m = ceil(2^32 / d) (0 when d == 1).
+// q = floor(n * m / 2^32) is floor(n / d) or one more, because m exceeds
+// 2^32 / d by less than 1 and n < 2^32; one multiply-compare fixes the
+// overshoot.  Exact for 0 <= n < 2^31 (then q * d cannot wrap).
+struct FastDiv {
+  uint32_t d, m;
+};
+
+__host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  f.m = d <= 1 ? 0u : uint32_t(((1ull << 32) + d - 1) / d);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(const FastDiv &f, uint32_t n) {
+  if (f.m == 0) return n;
+  uint32_t q = __umulhi(n, f.m);
+  return q * f.d > n ? q - 1 : q;
+}
+
 // Per-layer geometry passed by value to every kernel.
 struct Geom {
   int B, H, D, N;
@@ -77,32 +98,17 @@ struct Geom {
   float eps;             // linear denominator guard
   int rope_dims[3];
   float rope_base;
-  uint32_t f_magic;      // ceil(2^32 / F) when F > 1 and N * F < 2^32, else 0
+  FastDiv fdF, fdS, fdW;  // division by F, Hg*Wg and Wg
 };
 
 __device__ __forceinline__ bool bit(const uint64_t *m, int h) {
   return (m[h >> 6] >> (h & 63)) & 1ull;
 }
 
-// floor(p / F).  With f_magic = ceil(2^32 / F) = (2^32 + e) / F, 0 <= e < F,
-// p * f_magic / 2^32 = p/F + p*e / (F * 2^32), and the excess is below 1/F
-// whenever p * F < 2^32, which cannot lift floor(p/F) since the fractional
-// part of p/F is at most (F-1)/F.  The host sets f_magic only when
-// N * F < 2^32 (else 0: plain division).
-__device__ __forceinline__ int div_f(const Geom &g, int p) {
-  if (g.F == 1) return p;
-  return g.f_magic ? int(__umulhi(uint32_t(p), g.f_magic)) : p / g.F;
-}
-
 // Working position p of a temporal head holds this token.
 __device__ __forceinline__ int st_token(const Geom &g, int p) {
-  const int q = div_f(g, p);
+  const int q = int(fdiv(g.fdF, uint32_t(p)));
   return (p - q * g.F) * (g.Hg * g.Wg) + q;
-}
-// ... and token n sits at this working position.
-__device__ __forceinline__ int st_position(const Geom &g, int n) {
-  int S = g.Hg * g.Wg;
-  return (n % S) * g.F + n / S;
 }
 
 // Row addressing of a [B, *, *, d] tensor.  Element offset of (b, h, row)

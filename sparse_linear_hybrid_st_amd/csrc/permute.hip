@@ -38,23 +38,24 @@ __global__ void __launch_bounds__(256) rope_table_kernel(Geom g, double2 *__rest
   table[e] = make_double2(c, sn);
 }
 
+// Grid (ceil(N / rows_per_wg), B*H): a workgroup moves rows_per_wg
+// consecutive working rows of one (b, h); thread t handles 16-byte chunk
+// t % per_row of row t / per_row.  (b, h) come from the block index and the
+// token decomposition uses multiply-high division, so no per-element
+// integer division remains.
 template <typename T, bool ROPE>
 __global__ void __launch_bounds__(256) permute_kernel(Geom g, const T *__restrict__ src,
                                                       T *__restrict__ dst, int inverse,
                                                       const double2 *__restrict__ table) {
   constexpr int VEC = 16 / sizeof(T);
   const int per_row = g.D / VEC;
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long rows = (long long)g.B * g.H * g.N;
-  const long long row = gid / per_row;  // working row (b*H + h)*N + p
-  const int c = int(gid - row * per_row) * VEC;
-  if (row >= rows) return;
-  const int p = int(row % g.N);
-  const long long bh = row / g.N;
-  const int h = int(bh % g.H);
-  const int b = int(bh / g.H);
+  const int rows_per_wg = 256 / per_row;
+  const int bh = blockIdx.y, h = bh % g.H, b = bh / g.H;
+  const int p = blockIdx.x * rows_per_wg + int(threadIdx.x) / per_row;
+  const int c = (int(threadIdx.x) % per_row) * VEC;
+  if (p >= g.N) return;
   const int tok = bit(g.temporal, h) ? st_token(g, p) : p;
-  const long long woff = row * g.D + c;
+  const long long woff = ((long long)bh * g.N + p) * g.D + c;
   const long long boff = (((long long)b * g.N + tok) * g.H + h) * g.D + c;
 
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -67,8 +68,10 @@ __global__ void __launch_bounds__(256) permute_kernel(Geom g, const T *__restric
   // RoPE (forward only): rotate the VEC/2 pairs held by this thread.
   T in[VEC];
   *reinterpret_cast<u32x4 *>(in) = *reinterpret_cast<const u32x4 *>(src + boff);
-  const int S = g.Hg * g.Wg;
-  const int pos3[3] = {tok / S, (tok / g.Wg) % g.Hg, tok % g.Wg};
+  const int f = int(fdiv(g.fdS, uint32_t(tok)));
+  const int rem = tok - f * g.Hg * g.Wg;
+  const int y = int(fdiv(g.fdW, uint32_t(rem)));
+  const int pos3[3] = {f, y, rem - y * g.Wg};
   T out[VEC];
 #pragma unroll
   for (int t = 0; t < VEC; t += 2) {
@@ -102,8 +105,8 @@ hipError_t launch_rope_table(const Geom &g, double2 *table, hipStream_t st) {
 hipError_t launch_permute(const Geom &g, int dtype_bf16, int rope, int inverse, const void *src,
                           void *dst, hipStream_t st, const double2 *table) {
   const int vec = dtype_bf16 ? 8 : 4;
-  const long long threads = (long long)g.B * g.H * g.N * (g.D / vec);
-  const unsigned grid = unsigned((threads + 255) / 256);
+  const int rows_per_wg = 256 / (g.D / vec);
+  const dim3 grid((g.N + rows_per_wg - 1) / rows_per_wg, g.B * g.H);
   if (dtype_bf16) {
     if (rope)
       permute_kernel<bf16_t, true><<<grid, 256, 0, st>>>(g, (const bf16_t *)src, (bf16_t *)dst, 0, table);
