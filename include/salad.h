@@ -79,7 +79,8 @@ typedef struct {
   int32_t batch;                      /* B >= 1                                   */
   int32_t n_heads;                    /* H in [1, SALAD_MAX_HEADS]                */
   int32_t head_dim;                   /* d in {64, 128}                           */
-  int32_t grid_f, grid_h, grid_w;     /* latent F x Hg x Wg; N = F*Hg*Wg          */
+  int32_t grid_f, grid_h, grid_w;     /* latent F x Hg x Wg; N = F*Hg*Wg <= 2^28,
+                                         B*H*N < 2^31 rows, B*H*N*d <= 2^40      */
   uint8_t head_kind[SALAD_MAX_HEADS]; /* per head: SALAD_HEAD_* (first H used)    */
   int32_t window_radius;              /* window heads keep key j iff |p-j| <= r   */
   int32_t block;                      /* Top-K block size (queries and keys)      */

@@ -56,8 +56,9 @@ salad_status validate(const salad_problem *p, Info *inf) {
     return fail(SALAD_ERR_SHAPE, "grid dims must be >= 1");
   const long long N = (long long)p->grid_f * p->grid_h * p->grid_w;
   if (N > (1ll << 28)) return fail(SALAD_ERR_SHAPE, "N = F*Hg*Wg too large (%lld)", N);
-  if ((long long)p->batch * p->n_heads * N * p->head_dim > (1ll << 40))
-    return fail(SALAD_ERR_SHAPE, "tensor too large");
+  if ((long long)p->batch * p->n_heads * N * p->head_dim > (1ll << 40) ||
+      (long long)p->batch * p->n_heads * N >= (1ll << 31))
+    return fail(SALAD_ERR_SHAPE, "tensor too large (batch*n_heads*N must stay below 2^31 rows)");
   Geom &g = inf->g;
   memset(&g, 0, sizeof g);
   g.B = p->batch;

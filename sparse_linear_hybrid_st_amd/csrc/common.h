@@ -30,25 +30,24 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return bf16_t(u >> 16);
 }
 
-// float64 -> bfloat16 with a single rounding (nearest even).  Rounding to
-// float32 first would round twice.  The integer add carries into the
-// exponent exactly like the float32 trick above, here at bit 45 of the
-// float64 pattern; results outside bf16's normal range fall back to the
-// float32 route, whose extra rounding only matters there.
+// float64 -> bfloat16 with a single rounding (nearest even), branch-free.
+// Rounding to float32 first and then to bf16 would round twice; rounding
+// the first step to odd instead (truncate, then set the last bit when any
+// discarded bit was set) keeps the second rounding correct, because float32
+// carries more than two bits beyond bf16's eight (Boldo and Melquiond,
+// "Emulation of FMA and correctly rounded sums: proved algorithms using
+// rounding to odd", IEEE TC 2008).  The hardware conversion rounds to
+// nearest; when that went away from zero the pattern is stepped back one
+// unit, which is the truncation.  NaN stays NaN, and overflow lands on the
+// largest float32, which bf16 rounding then takes to infinity as it must.
 __device__ __forceinline__ bf16_t f64_to_bf16(double x) {
-  uint64_t u = (uint64_t)__double_as_longlong(x);
-  uint64_t mag = u & 0x7fffffffffffffffull;
-  int e = int(mag >> 52);
-  // bf16 normal range: unbiased exponent in [-126, 127], i.e. e in [897, 1150]
-  if (e < 897 || e > 1150) {
-    if (mag == 0) return bf16_t((u >> 48) & 0x8000u);
-    return f32_to_bf16(float(x));
-  }
-  uint64_t r = (mag + ((1ull << 44) - 1) + ((mag >> 45) & 1ull)) >> 45;  // 11-bit exp, 7-bit mant
-  int e2 = int(r >> 7);
-  if (e2 > 1150) return bf16_t(((u >> 48) & 0x8000u) | 0x7f80u);       // rounded up to inf
-  uint32_t out = uint32_t((e2 - 1023 + 127) << 7) | uint32_t(r & 0x7f);
-  return bf16_t(((u >> 48) & 0x8000u) | out);
+  const float f = float(x);
+  const double back = double(f);
+  uint32_t u = __float_as_uint(f);
+  const bool inexact = back != x;
+  const bool away = fabs(back) > fabs(x);
+  u = (u - (away ? 1u : 0u)) | (inexact ? 1u : 0u);
+  return f32_to_bf16(__uint_as_float(u));
 }
 
 template <typename T> struct io;
