@@ -124,7 +124,7 @@ salad_status validate(const salad_problem *p, Info *inf) {
 // block selection, Hp and Z; for f32 (staged) working copies of Q/K/V, the
 // selection, O_s, O_l, H and Z.  Both end with the gate values.
 struct Plan {
-  size_t wq, wk, wv, idx, o_s, o_l, h, z, s, hp, rope_tab;
+  size_t wq, wk, wv, wkr, idx, o_s, o_l, h, z, s, hp, rope_tab;
   size_t total_stage, total_forward;
 };
 
@@ -144,6 +144,7 @@ Plan plan(const Info &inf) {
   if (inf.bf16) {
     const bool rope = inf.rope != 0;
     pl.wq = off; off += rope ? up(rows * g.D * inf.esize) : 0;
+    pl.wkr = off; off += rope ? up(rows * g.D * inf.esize) : 0;
     pl.wk = off; off += up(rows * g.D * inf.esize);
     pl.wv = off; off += up(rows * g.D * inf.esize);
     pl.idx = off; off += idx_bytes;
@@ -421,38 +422,47 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
   const int rope = p->rope;
 
   if (inf.bf16) {
-    // Fused path.  The linear-state pass reads K and V in each head's
-    // working order (gathered from the boundary layout) and writes the
-    // contiguous working copies the attention kernel streams; Q is gathered
-    // by the attention kernel itself.  With RoPE, Q and K are rotated into
-    // working copies first.  The linear branch, projection, gate and inverse
-    // permutation run in the attention epilogue.
-    View qv = boundary_view(g, q), kv_in = boundary_view(g, k);
-    bf16_t *k_copy = (bf16_t *)wk;
+    // Fused path.  Heads whose working order is the token order (spatial
+    // and Top-K) are read in place: their rows of one (b, h) are already
+    // contiguous and equally spaced in the [B,N,H,d] layout.  The
+    // linear-state pass reads K and V in each head's working order and
+    // writes contiguous working copies for the temporal heads only; Q is
+    // gathered by the attention kernel itself.  With RoPE, Q and K are
+    // rotated first, keeping their layout.  The linear branch, projection,
+    // gate and inverse permutation run in the attention epilogue.
+    View qv = boundary_view(g, q), kb = boundary_view(g, k), vb = boundary_view(g, v);
     if (rope) {
       double2 *tab = (double2 *)(w + pl.rope_tab);
       if ((e = launch_rope_table(g, tab, stream)) != hipSuccess ||
-          (e = launch_permute(g, 1, 1, 0, q, wq, stream, tab)) != hipSuccess ||
-          (e = launch_permute(g, 1, 1, 0, k, wk, stream, tab)) != hipSuccess)
+          (e = launch_rope_rows(g, 1, q, wq, tab, stream)) != hipSuccess ||
+          (e = launch_rope_rows(g, 1, k, w + pl.wkr, tab, stream)) != hipSuccess)
         return hip_status(e, "salad_attn_forward: rope");
-      qv = working_view(g, wq);
-      kv_in = working_view(g, wk);
-      k_copy = nullptr;  // already in working order
+      qv = boundary_view(g, wq);
+      kb = boundary_view(g, w + pl.wkr);
     }
-    const View kv = working_view(g, wk), vv = working_view(g, wv);
+    // in-place rows of non-temporal heads: the boundary views, whose token
+    // gather is the identity for those heads
+    View kd = kb, vd = vb;
+    kd.perm = vd.perm = 0;
+    uint64_t work[4];
+    const bool direct = kv_direct_ok(g, kd, vd);
+    for (int i = 0; i < 4; ++i) work[i] = direct ? g.temporal[i] : ~0ull;
+    const View kw = working_view(g, wk), vw = working_view(g, wv);
     bf16_t *hp = (bf16_t *)(w + pl.hp);
-    if ((e = launch_linear_partials(g, kv_in, boundary_view(g, v), (float *)scratch, k_copy,
-                                    (bf16_t *)wv, stream)) != hipSuccess ||
+    if ((e = launch_linear_partials(g, kb, vb, (float *)scratch, (bf16_t *)wk, (bf16_t *)wv, work,
+                                    stream)) != hipSuccess ||
         (e = launch_linear_finalize(g, 1, (const float *)scratch, w_p, s, hm, hp, zv, stream)) != hipSuccess)
       return hip_status(e, "salad_attn_forward: linear state");
     if (inf.any_topk) {
+      // Top-K heads are never temporal: their working rows are the token rows
       double *qm, *km, *sc;
       select_regions(g, scratch, &qm, &km, &sc);
-      e = launch_block_select(g, 1, qv, kv, qm, km, sc, idx, stream);
+      e = launch_block_select(g, 1, qv, kb, qm, km, sc, idx, stream);
       if (e != hipSuccess) return hip_status(e, "salad_attn_forward: block select");
     }
     if ((e = prof_mark(0, stream)) != hipSuccess ||
-        (e = launch_attn_fused(g, qv, kv, vv, idx, hp, zv, boundary_view(g, out), stream)) != hipSuccess ||
+        (e = launch_attn_fused(g, qv, kw, vw, kd, vd, work, idx, hp, zv, boundary_view(g, out),
+                               stream)) != hipSuccess ||
         (e = prof_mark(1, stream)) != hipSuccess)
       return hip_status(e, "salad_attn_forward: attention");
     return SALAD_OK;

@@ -108,7 +108,10 @@ __device__ __forceinline__ int kv_swz(int j) { return ((j & 3) << 2) | ((j >> 2)
 
 struct AttnArgs {
   Geom g;
-  View q, k, v;
+  View q;
+  View k, v;             // K, V of the heads flagged in `work` (working copies)
+  View kd, vd;           // K, V of the other heads (rows already in working order)
+  uint64_t work[4];
   const int32_t *idx;
   float *o_s;            // staged: working layout fp32 output
   const bf16_t *hp;      // fused: [B*H][128][128] bf16, s_b * (H W_p)^T
@@ -160,9 +163,15 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   const int q0 = qt * BM;
   const int bh = b * g.H + h;
 
+  // K and V of this head: from the working copies, or, for heads whose
+  // working order is the token order, straight from the rows they already
+  // occupy (the two views have the same form; the host checked both)
+  const bool from_work = bit(a.work, h);
   const bf16_t *qbase = (const bf16_t *)a.q.base;
-  const bf16_t *kbase = (const bf16_t *)a.k.base;
-  const bf16_t *vbase = (const bf16_t *)a.v.base;
+  const bf16_t *kbase = (const bf16_t *)(from_work ? a.k.base : a.kd.base);
+  const bf16_t *vbase = (const bf16_t *)(from_work ? a.v.base : a.vd.base);
+  const long long kv_sB = from_work ? a.k.sB : a.kd.sB;
+  const long long kv_sH = from_work ? a.k.sH : a.kd.sH;
 
   // this wave's queries as MFMA B operands: lane -> query q0 + 32w + l32,
   // features 16ks + 8hl + e
@@ -197,20 +206,20 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   };
   // DMA one K and one V tile into a buffer: op i of wave w fills LDS rows
   // 4*(i*NW + w) .. +3; lane l writes physical unit l%16 of row l/16, so it
-  // fetches logical unit (l%16) ^ kv_swz(row).  K and V are in the working
-  // layout (rows of this (b, h) are sN elements apart, checked on the host),
-  // so a lane's address is a per-head base plus a lane-constant offset.
+  // fetches logical unit (l%16) ^ kv_swz(row).  Rows of this (b, h) are in
+  // working order, sN elements apart (checked on the host), so a lane's
+  // address is a per-head base plus a lane-constant offset.
   // Rows past N (only in the last tile) re-read row N-1: finite data whose
   // keys are masked.
   // The DMAs are buffer loads: a descriptor per head (base, byte extent) in
   // SGPRs, the tile start as a scalar offset and a lane-constant byte
   // offset, so issuing a tile costs no per-lane address arithmetic.
-  const int sN = int(a.k.sN);
+  const int sN = int(from_work ? a.k.sN : a.kd.sN);
   const unsigned head_bytes = unsigned((long long)(g.N - 1) * sN * 2 + kD * 2);
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(kbase + (long long)b * a.k.sB + (long long)h * a.k.sH), 0, head_bytes, 0x00020000);
+      (void *)(kbase + (long long)b * kv_sB + (long long)h * kv_sH), 0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(vbase + (long long)b * a.v.sB + (long long)h * a.v.sH), 0, head_bytes, 0x00020000);
+      (void *)(vbase + (long long)b * kv_sB + (long long)h * kv_sH), 0, head_bytes, 0x00020000);
   int dma_row[DMA_PER_WAVE], dma_off[DMA_PER_WAVE];  // row in tile, byte offset
 #pragma unroll
   for (int i = 0; i < DMA_PER_WAVE; ++i) {
@@ -494,13 +503,15 @@ hipError_t launch_bf16(AttnArgs a, hipStream_t st) {
 }
 }  // namespace
 
-// The bf16 kernel streams K and V from a layout whose rows of one (b, h)
-// are contiguous and equally spaced (the working layout), with the same
-// strides for both.
-static bool kv_streamable(const View &kv, const View &vv) {
+// The bf16 kernel streams K and V of one (b, h) as rows sN elements apart,
+// with the same strides for both, and addresses a head's rows with 32-bit
+// byte offsets.
+static bool kv_streamable(const Geom &g, const View &kv, const View &vv) {
   return !kv.perm && !vv.perm && kv.sB == vv.sB && kv.sH == vv.sH && kv.sN == vv.sN &&
-         kv.sN < (1ll << 20);
+         kv.sN > 0 && kv.sN < (1ll << 20) && (long long)(g.N - 1) * kv.sN * 2 + kD * 2 < (1ll << 32);
 }
+
+bool kv_direct_ok(const Geom &g, View kd, View vd) { return kv_streamable(g, kd, vd); }
 
 hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv,
                               const int32_t *idx, float *o_s, hipStream_t st) {
@@ -512,25 +523,37 @@ hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv
       attn_f32_kernel<64><<<grid, 64, 0, st>>>(g, qv, kv, vv, idx, o_s);
     return hipGetLastError();
   }
-  if (!kv_streamable(kv, vv)) return hipErrorInvalidValue;
+  if (!kv_streamable(g, kv, vv)) return hipErrorInvalidValue;
   AttnArgs a = {};
   a.g = g;
   a.q = qv;
-  a.k = kv;
-  a.v = vv;
+  a.k = a.kd = kv;
+  a.v = a.vd = vv;
+  for (int i = 0; i < 4; ++i) a.work[i] = ~0ull;
   a.idx = idx;
   a.o_s = o_s;
   return launch_bf16<false>(a, st);
 }
 
-hipError_t launch_attn_fused(const Geom &g, View qv, View kv, View vv, const int32_t *idx,
-                             const bf16_t *hp, const float *z, View outv, hipStream_t st) {
-  if (!kv_streamable(kv, vv)) return hipErrorInvalidValue;
+hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, View vd,
+                             const uint64_t work[4], const int32_t *idx, const bf16_t *hp,
+                             const float *z, View outv, hipStream_t st) {
+  bool any_work = false, any_direct = false;
+  for (int h = 0; h < g.H; ++h) {
+    const bool w = (work[h >> 6] >> (h & 63)) & 1ull;
+    any_work |= w;
+    any_direct |= !w;
+  }
+  if ((any_work && !kv_streamable(g, kw, vw)) || (any_direct && !kv_streamable(g, kd, vd)))
+    return hipErrorInvalidValue;
   AttnArgs a = {};
   a.g = g;
   a.q = qv;
-  a.k = kv;
-  a.v = vv;
+  a.k = kw;
+  a.v = vw;
+  a.kd = kd;
+  a.vd = vd;
+  for (int i = 0; i < 4; ++i) a.work[i] = work[i];
   a.idx = idx;
   a.hp = hp;
   a.z = z;

@@ -39,6 +39,9 @@ hipError_t launch_rope_table(const Geom &g, double2 *table, hipStream_t st);
 // table: optional RoPE table (NULL: angles computed per element; same values).
 hipError_t launch_permute(const Geom &g, int bf16, int rope, int inverse, const void *src,
                           void *dst, hipStream_t st, const double2 *table = nullptr);
+// RoPE without reordering: src and dst both [B,N,H,d] (bf16 or f32).
+hipError_t launch_rope_rows(const Geom &g, int bf16, const void *src, void *dst,
+                            const double2 *table, hipStream_t st);
 hipError_t launch_block_select(const Geom &g, int bf16, View qv, View kv, double *qbar,
                                double *kbar, double *scores, int32_t *idx, hipStream_t st);
 // partial: [B*H][S][D*D + D] floats of workspace (S = linear_splits).
@@ -46,16 +49,23 @@ hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float 
                                float *h, float *z, hipStream_t st);
 // Fused-layer pieces (bf16, d = 128).
 // Also writes working-layout copies of K / V when kw_out / vw_out are non-null.
+// kw_out / vw_out (working layout) receive the rows of the heads flagged
+// in copy_heads.
 hipError_t launch_linear_partials(const Geom &g, View kv, View vv, float *partial, bf16_t *kw_out,
-                                  bf16_t *vw_out, hipStream_t st);
+                                  bf16_t *vw_out, const uint64_t copy_heads[4], hipStream_t st);
 // h: [B*H][128][128] fp32 state (workspace); hp: [B*H][128][128] bf16 =
 // s_b * (H W_p)^T; z: [B*H][128] fp32.
 hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial, const void *w_p,
                                   const float *s, float *h, bf16_t *hp, float *z, hipStream_t st);
 // Sparse attention with the linear branch, projection, gate and inverse
 // permutation fused into the epilogue; out in the boundary layout.
-hipError_t launch_attn_fused(const Geom &g, View qv, View kv, View vv, const int32_t *idx,
-                             const bf16_t *hp, const float *z, View outv, hipStream_t st);
+// Heads flagged in `work` read K, V through kw, vw (working copies), the
+// others through kd, vd (rows in working order where they already are).
+hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, View vd,
+                             const uint64_t work[4], const int32_t *idx, const bf16_t *hp,
+                             const float *z, View outv, hipStream_t st);
+// Whether the attention kernel can stream K, V rows through these views.
+bool kv_direct_ok(const Geom &g, View kd, View vd);
 hipError_t launch_linear_apply(const Geom &g, int bf16, View qv, const float *h, const float *z,
                                float *o_l, hipStream_t st);
 // ws: gate_ws_bytes of workspace.

@@ -49,9 +49,10 @@ __device__ __forceinline__ u32x4 relu_bf16x8(u32x4 v) {
 // rows [s*chunk, (s+1)*chunk).  Tiles of 64 tokens: thread t loads 16-byte
 // chunk c = t%16 of rows t/16 + 16i (i < 4) of K and V -- each load
 // instruction covers four whole 256-byte rows -- and, when kw_out / vw_out
-// are given, stores them to those working-layout copies (the pass that
-// already reads K and V produces the contiguous per-head copies the
-// attention kernel streams).  relu(K) and V go to LDS row-major; unit u of
+// are given and the head is flagged in `copy`, stores them to those
+// working-layout copies (the pass that already reads K and V produces the
+// contiguous per-head copies the attention kernel streams for heads whose
+// working order differs from the token order).  relu(K) and V go to LDS row-major; unit u of
 // row j sits at u ^ lin_swz(j).  The MFMA operands, which need 4 consecutive
 // tokens of one feature per lane, come from ds_read_b64_tr_b16: each 16-lane
 // group reads 4 rows x 64 bytes, which lin_swz spreads over distinct banks.
@@ -63,11 +64,16 @@ __device__ __forceinline__ int lin_swz(int j) { return ((j & 3) << 2) | ((j >> 2
 typedef __attribute__((ext_vector_type(4))) short s16x4_l;
 typedef __attribute__((address_space(3))) s16x4_l lds_s16x4_l;
 
+struct HeadMask {
+  uint64_t w[4];
+};
+
 __global__ void __launch_bounds__(256, 2) linear_state_bf16_kernel(Geom g, View kv, View vv,
                                                                 float *__restrict__ partial,
                                                                 int S, int chunk,
                                                                 bf16_t *__restrict__ kw_out,
-                                                                bf16_t *__restrict__ vw_out) {
+                                                                bf16_t *__restrict__ vw_out,
+                                                                HeadMask copy) {
   constexpr int D = 128, TT = 64;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[TT * D];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[TT * D];
@@ -78,6 +84,7 @@ __global__ void __launch_bounds__(256, 2) linear_state_bf16_kernel(Geom g, View 
   const bf16_t *kb = (const bf16_t *)kv.base;
   const bf16_t *vb = (const bf16_t *)vv.base;
   const long long wbase = (long long)bh * g.N * D;  // working-layout copy of this (b, h)
+  if (!bit(copy.w, h)) kw_out = vw_out = nullptr;
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -299,11 +306,14 @@ hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial,
 // Partial states only (the fused layer finalizes them itself), optionally
 // writing working-layout copies of K and V.
 hipError_t launch_linear_partials(const Geom &g, View kv, View vv, float *partial, bf16_t *kw_out,
-                                  bf16_t *vw_out, hipStream_t st) {
+                                  bf16_t *vw_out, const uint64_t copy_heads[4], hipStream_t st) {
   const int S = linear_splits(g);
   int chunk = (g.N + S - 1) / S;
   chunk = (chunk + 127) / 128 * 128;
-  linear_state_bf16_kernel<<<dim3(S, g.B * g.H), 256, 0, st>>>(g, kv, vv, partial, S, chunk, kw_out, vw_out);
+  HeadMask m;
+  for (int i = 0; i < 4; ++i) m.w[i] = copy_heads[i];
+  linear_state_bf16_kernel<<<dim3(S, g.B * g.H), 256, 0, st>>>(g, kv, vv, partial, S, chunk, kw_out,
+                                                              vw_out, m);
   return hipGetLastError();
 }
 
@@ -314,7 +324,8 @@ hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float 
   chunk = (chunk + 127) / 128 * 128;
   dim3 grid(S, g.B * g.H);
   if (bf16) {
-    linear_state_bf16_kernel<<<grid, 256, 0, st>>>(g, kv, vv, partial, S, chunk, nullptr, nullptr);
+    linear_state_bf16_kernel<<<grid, 256, 0, st>>>(g, kv, vv, partial, S, chunk, nullptr, nullptr,
+                                                   HeadMask{});
   } else if (g.D == 128) {
     linear_state_f32_kernel<128><<<grid, 256, 0, st>>>(g, kv, vv, partial, S, chunk);
   } else {

@@ -42,11 +42,14 @@ __global__ void __launch_bounds__(256) rope_table_kernel(Geom g, double2 *__rest
 // inverse of st_token), found with multiply-high division.  B*H*N < 2^31
 // rows (checked at the boundary) keeps row indices in 32 bits.  MODE 0
 // copies (forward or inverse), MODE 1 rotates with the (cos, sin) table,
-// MODE 2 rotates computing (cos, sin) in place (no table).
+// MODE 2 rotates computing (cos, sin) in place (no table).  keep_layout = 1
+// (rotation only) writes each row back to its own place in a [B,N,H,d]
+// destination.
 template <typename T, int MODE, int D>
 __global__ void __launch_bounds__(256) permute_kernel(Geom g, const T *__restrict__ src,
                                                       T *__restrict__ dst, int inverse,
-                                                      const double2 *__restrict__ table) {
+                                                      const double2 *__restrict__ table,
+                                                      int keep_layout) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int PER_ROW = D / VEC;
   constexpr int TOK = 256 / PER_ROW;
@@ -94,8 +97,9 @@ __global__ void __launch_bounds__(256) permute_kernel(Geom g, const T *__restric
 #pragma unroll 4
   for (int h = 0; h < g.H; ++h) {
     const int p = bit(g.temporal, h) ? p_temporal : tok;
-    const uint64_t woff = uint64_t(uint32_t(b * g.H + h) * uint32_t(g.N) + uint32_t(p)) * D + c;
     const uint64_t boff = brow + uint32_t(h * D);
+    const uint64_t woff =
+        keep_layout ? boff : uint64_t(uint32_t(b * g.H + h) * uint32_t(g.N) + uint32_t(p)) * D + c;
     if (MODE == 0) {
       const uint64_t from = inverse ? woff : boff;
       const uint64_t to = inverse ? boff : woff;
@@ -117,14 +121,14 @@ __global__ void __launch_bounds__(256) permute_kernel(Geom g, const T *__restric
 
 template <typename T, int D>
 static void permute_launch(const Geom &g, int mode, int inverse, const void *src, void *dst,
-                           hipStream_t st, const double2 *table) {
+                           hipStream_t st, const double2 *table, int keep_layout = 0) {
   constexpr int TOK = 256 / (D / (16 / sizeof(T)));
   const dim3 grid(((g.N + TOK - 1) / TOK) * g.B);
   const T *s = (const T *)src;
   T *d = (T *)dst;
-  if (mode == 1) permute_kernel<T, 1, D><<<grid, 256, 0, st>>>(g, s, d, 0, table);
-  else if (mode == 2) permute_kernel<T, 2, D><<<grid, 256, 0, st>>>(g, s, d, 0, nullptr);
-  else permute_kernel<T, 0, D><<<grid, 256, 0, st>>>(g, s, d, inverse, nullptr);
+  if (mode == 1) permute_kernel<T, 1, D><<<grid, 256, 0, st>>>(g, s, d, 0, table, keep_layout);
+  else if (mode == 2) permute_kernel<T, 2, D><<<grid, 256, 0, st>>>(g, s, d, 0, nullptr, keep_layout);
+  else permute_kernel<T, 0, D><<<grid, 256, 0, st>>>(g, s, d, inverse, nullptr, 0);
 }
 
 int rope_table_entries(const Geom &g) {
@@ -147,6 +151,22 @@ hipError_t launch_permute(const Geom &g, int dtype_bf16, int rope, int inverse, 
     permute_launch<float, 128>(g, mode, inverse, src, dst, st, table);
   } else if (g.D == 64) {
     permute_launch<float, 64>(g, mode, inverse, src, dst, st, table);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_rows(const Geom &g, int dtype_bf16, const void *src, void *dst,
+                            const double2 *table, hipStream_t st) {
+  if (!table) return hipErrorInvalidValue;
+  if (dtype_bf16) {
+    if (g.D != 128) return hipErrorInvalidValue;
+    permute_launch<bf16_t, 128>(g, 1, 0, src, dst, st, table, 1);
+  } else if (g.D == 128) {
+    permute_launch<float, 128>(g, 1, 0, src, dst, st, table, 1);
+  } else if (g.D == 64) {
+    permute_launch<float, 64>(g, 1, 0, src, dst, st, table, 1);
   } else {
     return hipErrorInvalidValue;
   }
