@@ -117,7 +117,6 @@ struct AttnArgs {
   const bf16_t *hp;      // fused: [B*H][128][128] bf16, s_b * (H W_p)^T
   const float *z;        // fused: [B*H][128] linear normaliser state
   View out;              // fused: output rows (boundary layout, scattered)
-  int topk_mode;         // 0: window heads, 1: Top-K heads
   int n_heads_sel;       // heads handled by this launch
   uint8_t heads[kMaxHeads];
   int tiles_per_head;    // query tiles per (b, head)
@@ -145,6 +144,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   // them share a CU (2 waves per SIMD), and the other workgroups cover each
   // one's DMA wait; window workgroups (4 waves) double-buffer.
   constexpr bool SINGLE = (NW == 2);
+  constexpr bool TOPK = (NW == 2);  // the launcher runs Top-K heads with 2 waves, window heads with 4
   __shared__ __attribute__((aligned(1024))) bf16_t K0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t K1[SINGLE ? 8 : TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t V0[TILE];
@@ -185,7 +185,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
 
   int n_tiles, kt_first = 0;
   const int32_t *sel = nullptr;
-  if (a.topk_mode) {
+  if (TOPK) {
     n_tiles = g.k;
     sel = a.idx + ((long long)bh * g.nb + q0 / g.block) * g.k;
   } else {
@@ -198,11 +198,20 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
 
   // First key row of tile `it`.  An out-of-range block index (only possible
   // if idx was not produced by the selection) maps past the end, where every
-  // row is masked.
+  // row is masked.  Top-K workgroups first copy their block list to LDS, so
+  // reading it inside the tile loop is an LDS read, not a global load whose
+  // wait would also wait for the DMAs in flight.
+  extern __shared__ int32_t sel_lds[];  // Top-K: g.k block start rows
+  if (TOPK) {
+    for (int j = t; j < n_tiles; j += NW * 64) {
+      const int kb = sel[j];
+      sel_lds[j] = (kb >= 0 && kb < g.nb) ? kb * g.block : g.N;
+    }
+    __syncthreads();
+  }
   auto tile_start = [&](int it) -> int {
-    if (!a.topk_mode) return (kt_first + it) * kBN;
-    const int kb = sel[it];
-    return (kb >= 0 && kb < g.nb) ? kb * g.block : g.N;
+    if (!TOPK) return (kt_first + it) * kBN;
+    return sel_lds[it];
   };
   // DMA one K and one V tile into a buffer: op i of wave w fills LDS rows
   // 4*(i*NW + w) .. +3; lane l writes physical unit l%16 of row l/16, so it
@@ -226,6 +235,19 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     dma_row[i] = 4 * (i * NW + w) + (lane >> 4);
     dma_off[i] = 2 * (dma_row[i] * sN + (((lane & 15) ^ kv_swz(dma_row[i])) << 3));
   }
+  // one tensor's DMA of the tile starting at key k0 into buffer Dd
+  // one tensor's DMA of the tile starting at key k0 into buffer Dd
+  auto issue_one = [&](const __amdgpu_buffer_rsrc_t &rs, int k0, bf16_t *__restrict__ Dd) {
+    const bool tail = k0 + kBN > g.N;
+    const unsigned soff = unsigned(k0) * unsigned(sN) * 2u;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      int off = dma_off[i];
+      if (tail) off -= 2 * (k0 + dma_row[i] - min(k0 + dma_row[i], g.N - 1)) * sN;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(Dd + (4 * (i * NW + w)) * kD), 16,
+                                               unsigned(off), soff, 0, 0);
+    }
+  };
   auto issue_tile = [&](int k0, bf16_t *__restrict__ Kd, bf16_t *__restrict__ Vd) {
     const bool tail = k0 + kBN > g.N;
     const unsigned soff = unsigned(k0) * unsigned(sN) * 2u;
@@ -266,20 +288,26 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;  // running max (raw score units), partial row sum
 
-  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto compute = [&](int k0, const bf16_t *__restrict__ Ks, const bf16_t *__restrict__ Vs) {
+  // One key tile: S^T = K Q^T (qk), online softmax (softmax), O^T += V^T
+  // P^T (pv).  classify tells whether the tile holds any key of this wave's
+  // queries and whether it needs no mask.  The phases are separate so the
+  // single-buffered loop can free the K buffer right after qk; each takes
+  // its LDS buffer as a restrict parameter, which lets the compiler tell its
+  // reads apart from DMAs into the other buffers.
+  auto classify = [&](int k0, bool &any, bool &full) {
     const int k1 = min(k0 + kBN, g.N) - 1;
-    bool any, full;
-    if (a.topk_mode) {
+    if (TOPK) {
       any = k0 < g.N;
       full = (k0 + kBN) <= g.N;
     } else {
       any = (k0 <= wq_hi + g.r) && (k1 >= wq_lo - g.r) && (wq_lo <= wq_hi);
       full = (k0 + kBN <= g.N) && (k0 >= wq_hi - g.r) && (k0 + kBN - 1 <= wq_lo + g.r);
     }
-    if (!any) return;
-    // S^T[key][query] = K Q^T, two blocks of 32 keys
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  };
+  // S^T[key][query] = K Q^T, two blocks of 32 keys
+  auto qk = [&](const bf16_t *__restrict__ Ks, f32x16 (&s)[2]) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ks += 2) {
       bf16x8 ka[2][2];
@@ -293,6 +321,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_32x32x16(ka[u][kb], qf[ks + u], s[kb]);
     }
+  };
+  auto softmax = [&](int k0, bool full, f32x16 (&s)[2], bf16x8 (&pb)[4]) {
     float mx = -INFINITY;
     if (full) {
 #pragma unroll
@@ -306,7 +336,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
           // bitwise, not short-circuit: keeps the mask a select, not a branch
-          const bool keep = (j < g.N) & (bool(a.topk_mode) | (abs(pq - j) <= g.r));
+          const bool keep = (j < g.N) & (TOPK | (abs(pq - j) <= g.r));
           s[kb][r] = keep ? s[kb][r] : -INFINITY;
           mx = fmaxf(mx, s[kb][r]);
         }
@@ -328,7 +358,6 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
       m_run = m_new;
     }
     const float moff = m_run == -INFINITY ? 0.f : m_run * c2;
-    bf16x8 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -343,6 +372,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
         }
         pb[2 * kb + half] = pv;
       }
+  };
+  auto pv = [&](const bf16_t *__restrict__ Vs, const bf16x8 (&pb)[4]) {
     // O^T[d][q] += V^T[d][keys] P^T[keys][q].  k-step kk, half hl, element
     // e = 4r + e' covers key 32*(kk/2) + 8*(2*(kk%2) + r) + 4*hl + e'; the
     // matching V^T operand comes from two transposing reads (r = 0, 1).
@@ -361,41 +392,85 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
       for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(*(const bf16x8 *)&va[db], pb[kk], o[db]);
     }
   };
+  auto compute = [&](int k0, const bf16_t *__restrict__ Ks, const bf16_t *__restrict__ Vs) {
+    bool any, full;
+    classify(k0, any, full);
+    if (!any) return;
+    f32x16 s[2];
+    bf16x8 pb[4];
+    qk(Ks, s);
+    softmax(k0, full, s, pb);
+    pv(Vs, pb);
+  };
 
-  // Double-buffered tile loop, unrolled by two so each half names its
-  // buffers statically.  Before computing tile it: wait for this wave's DMA
-  // of tile it (vmcnt 0), barrier (every wave's DMA landed and every wave is
-  // done with the other buffer), then start the DMA of tile it+1.
   // Tile starts are read before each DMA is issued and carried along, so no
-  // global load (and its wait) sits between a DMA and the LDS reads.
+  // global load (and its wait) sits between a DMA and the LDS reads.  Each
+  // wave's DMAs complete in issue order, so "vmcnt <= n" means all but the
+  // last n issued have landed; a barrier after such a wait makes every
+  // wave's share visible.
   int k_cur = n_tiles > 0 ? tile_start(0) : 0;
   if constexpr (SINGLE) {
-    // one buffer: DMA, wait, compute; other workgroups on the CU cover the DMA
+    // One buffer per tensor, split phases: the K buffer is refilled with
+    // tile it+1 as soon as every wave has finished QK of tile it, and the V
+    // buffer once PV of tile it is done, so K(it+1) lands during softmax and
+    // PV of tile it.  (The compiler makes the K reads of QK wait for V(it)
+    // too, as it cannot tell the two buffers apart there; issuing the DMAs
+    // out of its sight to overlap V as well measured no faster.)  Issue
+    // order per wave: K(0) V(0) K(1) V(1) ...
+    // The barriers here are bare s_barrier: __syncthreads() also fences,
+    // which waits for every DMA in flight.  The counts are handled by the
+    // explicit waits, and each barrier that frees a buffer follows the
+    // MFMAs that consumed that buffer's LDS reads.
+    constexpr int VM_ONE = DMA_PER_WAVE;  // DMA ops of one tensor per wave
+    static_assert(VM_ONE < 16, "vmcnt immediate below");
+    if (n_tiles > 0) {
+      issue_one(krs, k_cur, K0);
+      issue_one(vrs, k_cur, V0);
+    }
     for (int it = 0; it < n_tiles; ++it) {
-      if (it > 0) __syncthreads();  // every wave is done reading the buffer
-      issue_tile(k_cur, K0, V0);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-      const int k_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
-      compute(k_cur, K0, V0);
+      const bool more = it + 1 < n_tiles;
+      const int k_nxt = more ? tile_start(it + 1) : 0;
+      // Top-K tiles are never skipped: a block past the end (only from an
+      // invalid index) has every key masked and adds nothing
+      bool any, full;
+      classify(k_cur, any, full);
+      (void)any;
+      f32x16 s[2];
+      bf16x8 pb[4];
+      __builtin_amdgcn_s_waitcnt(0x0F70 | VM_ONE);  // K(it) landed, V(it) may be in flight
+      __builtin_amdgcn_s_barrier();
+      qk(K0, s);
+      __builtin_amdgcn_s_barrier();  // every wave is done reading K(it)
+      if (more) issue_one(krs, k_nxt, K0);
+      softmax(k_cur, full, s, pb);
+      if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | VM_ONE);  // V(it) landed, K(it+1) may not
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+      __builtin_amdgcn_s_barrier();
+      pv(V0, pb);
+      __builtin_amdgcn_s_barrier();  // every wave is done reading V(it)
+      if (more) issue_one(vrs, k_nxt, V0);
       k_cur = k_nxt;
     }
   } else {
+    // Double-buffered, unrolled by two so each half names its buffers
+    // statically.  Before computing tile it: wait for this wave's DMA of
+    // tile it (vmcnt 0), barrier (every wave's DMA landed and every wave is
+    // done with the other buffer), then start the DMA of tile it+1.
     if (n_tiles > 0) issue_tile(k_cur, K0, V0);
     for (int it = 0; it < n_tiles; it += 2) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    const int k_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
-    if (it + 1 < n_tiles) issue_tile(k_nxt, K1, V1);
-    compute(k_cur, K0, V0);
-    if (it + 1 >= n_tiles) break;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    const int k_nn = it + 2 < n_tiles ? tile_start(it + 2) : 0;
-    if (it + 2 < n_tiles) issue_tile(k_nn, K0, V0);
-    compute(k_nxt, K1, V1);
-    k_cur = k_nn;
-  }
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const int k_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
+      if (it + 1 < n_tiles) issue_tile(k_nxt, K1, V1);
+      compute(k_cur, K0, V0);
+      if (it + 1 >= n_tiles) break;
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const int k_nn = it + 2 < n_tiles ? tile_start(it + 2) : 0;
+      if (it + 2 < n_tiles) issue_tile(k_nn, K0, V0);
+      compute(k_nxt, K1, V1);
+      k_cur = k_nn;
+    }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -481,7 +556,6 @@ template <bool FUSED>
 hipError_t launch_bf16(AttnArgs a, hipStream_t st) {
   const Geom &g = a.g;
   for (int mode = 0; mode < 2; ++mode) {
-    a.topk_mode = mode;
     a.n_heads_sel = 0;
     for (int h = 0; h < g.H; ++h) {
       const bool is_topk = (g.topk[h >> 6] >> (h & 63)) & 1ull;
@@ -493,7 +567,7 @@ hipError_t launch_bf16(AttnArgs a, hipStream_t st) {
     const unsigned grid = unsigned(a.tiles_per_head) * a.n_heads_sel * g.B;
     a.n_blocks = int(grid);
     if (mode)
-      attn_bf16_kernel<2, FUSED><<<grid, 128, 0, st>>>(a);
+      attn_bf16_kernel<2, FUSED><<<grid, 128, size_t(g.k) * sizeof(int32_t), st>>>(a);
     else
       attn_bf16_kernel<4, FUSED><<<grid, 256, 0, st>>>(a);
     hipError_t e = hipGetLastError();

@@ -1,5 +1,5 @@
 // Top-K block selection: block-mean pooling of Q and K, block scores and
-// the k best key blocks per query block (fp64 scores, bitonic sort).
+// the k best key blocks per query block (fp64 scores, radix select).
 //
 // Source: ijyty.com/news/870645, section 1.2 -- cut the tokens into blocks,
 // take each block's mean, compare queries with the key-block means and keep
@@ -15,30 +15,47 @@
 
 namespace salad {
 
-// One workgroup per (b, h, block) of one tensor (blockIdx.y: 0 = Q, 1 = K).
-// 256 threads: 16 row groups x 16 column chunks of 8 elements.
+// One workgroup per (b, h, block) of one tensor (blockIdx.z: 0 = Q, 1 = K),
+// with (b, h) varying fastest so that workgroups in flight together read
+// every head of the same tokens (whole [B,N,H,d] records).  256 threads:
+// 16 row groups x 16 column chunks of 8 elements; a thread issues all of
+// its rows' loads before it adds.
 template <typename T>
 __global__ void __launch_bounds__(256) block_mean_kernel(Geom g, View qv, View kv,
                                                          double *__restrict__ qbar,
                                                          double *__restrict__ kbar) {
-  const int blk = blockIdx.x;
-  const int bh = blockIdx.z;
+  const int bh = blockIdx.x;
+  const int blk = blockIdx.y;
   const int h = bh % g.H, b = bh / g.H;
   if (!bit(g.topk, h)) return;
-  const View v = blockIdx.y ? kv : qv;
-  double *out = (blockIdx.y ? kbar : qbar) + ((long long)bh * g.nb + blk) * g.D;
+  const View v = blockIdx.z ? kv : qv;
+  double *out = (blockIdx.z ? kbar : qbar) + ((long long)bh * g.nb + blk) * g.D;
   const T *base = (const T *)v.base;
   const int t = threadIdx.x, rg = t >> 4, ch = t & 15;
   const int row0 = blk * g.block;
   const int rows = min(g.block, g.N - row0);
   __shared__ double part[16][128];
   const int cols = g.D / 8;  // column chunks in use (8 or 16)
+  typedef T chunk8 __attribute__((ext_vector_type(8)));  // 16 B (bf16) or 32 B (f32)
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (ch < cols) {
-    for (int r = rg; r < rows; r += 16) {
-      const T *src = base + row_offset(g, v, b, h, row0 + r) + ch * 8;
+    for (int r0 = rg; r0 < rows; r0 += 64) {
+      // up to four rows in flight: rows r0, r0+16, r0+32, r0+48
+      chunk8 raw[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += double(io<T>::ld(src + e));
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + 16 * u;
+        if (r < rows) raw[u] = *(const chunk8 *)(base + row_offset(g, v, b, h, row0 + r) + ch * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (r0 + 16 * u >= rows) break;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const T x = raw[u][e];
+          acc[e] += double(io<T>::ld(&x));
+        }
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) part[rg][ch * 8 + e] = acc[e];
@@ -52,136 +69,178 @@ __global__ void __launch_bounds__(256) block_mean_kernel(Geom g, View qv, View k
 }
 
 // Block scores S[qb][kb] = qbar[qb] . kbar[kb] for every Top-K (b, h), as a
-// tiled fp64 product: workgroup (tile_q, tile_k, bh) computes a 32 x 32 tile,
-// staging 32-column slices of both operands in LDS; thread t owns rows
-// 4*(t/32)..+3 at column t%32.  Each product is a plain left-to-right fp64
-// sum over the d features.
+// tiled fp64 product: workgroup (tile_q, tile_k, bh) computes a 128 x 128
+// tile from 16-feature slices of both operands staged in LDS
+// (feature-major); thread t owns query rows 8*(t/16)..+7 and key columns
+// 8*(t%16)..+7, so each feature step is 16 LDS values for 64 FMAs.  Each
+// product is a plain left-to-right fp64 sum over the d features.
+constexpr int kScoreTile = 128;
+
 __global__ void __launch_bounds__(256) block_score_kernel(Geom g, const double *__restrict__ qbar,
                                                           const double *__restrict__ kbar,
                                                           double *__restrict__ scores) {
+  constexpr int TS = kScoreTile, LD = TS + 2;  // +2: the feature-major stores spread over banks
   const int bh = blockIdx.z, h = bh % g.H;
   if (!bit(g.topk, h)) return;
   const int nb = g.nb, D = g.D, t = threadIdx.x;
-  const int q0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
-  __shared__ double qs[32][33];
-  __shared__ double ks[32][33];
+  const int q0 = blockIdx.x * TS, k0 = blockIdx.y * TS;
+  __shared__ __attribute__((aligned(16))) double qs[16 * LD];
+  __shared__ __attribute__((aligned(16))) double ks[16 * LD];
   const double *qb = qbar + (long long)bh * nb * D;
   const double *kb = kbar + (long long)bh * nb * D;
-  const int r0 = 4 * (t >> 5), c = t & 31;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int f0 = 0; f0 < D; f0 += 32) {
-    __syncthreads();
-    for (int e = t; e < 32 * 32; e += 256) {
-      const int r = e >> 5, f = e & 31;
-      qs[r][f] = (q0 + r < nb) ? qb[(long long)(q0 + r) * D + f0 + f] : 0.0;
-      ks[r][f] = (k0 + r < nb) ? kb[(long long)(k0 + r) * D + f0 + f] : 0.0;
+  const int ti = 8 * (t >> 4), tj = 8 * (t & 15);
+  // staging: thread t loads features f8..f8+7 of row r (64 contiguous bytes)
+  const int lr = t >> 1, f8 = 8 * (t & 1);
+  double acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+  for (int f0 = 0; f0 < D; f0 += 16) {
+    double qv[8], kv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[e] = (q0 + lr < nb) ? qb[(long long)(q0 + lr) * D + f0 + f8 + e] : 0.0;
+      kv[e] = (k0 + lr < nb) ? kb[(long long)(k0 + lr) * D + f0 + f8 + e] : 0.0;
+    }
+    __syncthreads();  // previous slice's reads are done
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qs[(f8 + e) * LD + lr] = qv[e];
+      ks[(f8 + e) * LD + lr] = kv[e];
     }
     __syncthreads();
-    for (int f = 0; f < 32; ++f) {
-      const double kv = ks[c][f];
+#pragma unroll 4
+    for (int f = 0; f < 16; ++f) {
+      double a[8], bv[8];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) acc[a] = fma(qs[r0 + a][f], kv, acc[a]);
+      for (int i = 0; i < 8; ++i) a[i] = qs[f * LD + ti + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bv[j] = ks[f * LD + tj + j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], bv[j], acc[i][j]);
     }
   }
-  if (k0 + c < nb) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-      if (q0 + r0 + a < nb) scores[((long long)bh * nb + q0 + r0 + a) * nb + k0 + c] = acc[a];
+  for (int i = 0; i < 8; ++i) {
+    if (q0 + ti + i >= nb) continue;
+    double *dst = scores + ((long long)bh * nb + q0 + ti + i) * nb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + tj + j < nb) dst[k0 + tj + j] = acc[i][j];
   }
 }
 
-// Selection for one query block per workgroup: bitonic sort of the P =
-// next_pow2(nb) (score, block) pairs in LDS into the order "higher score
-// first, equal scores lower block first" (padding sorts last), flag the
-// first k blocks, then write the flagged block indices ascending with a
-// ballot prefix count.  The order is total, so the result does not depend on
-// the sort's internal schedule.
-__device__ __forceinline__ bool sel_before(double sa, int ia, double sb, int ib) {
-  return sa > sb || (sa == sb && ia < ib);
+// Selection, one wave per query block (4 per workgroup): the k best key
+// blocks under the order "higher score first, equal scores lower block
+// first", written ascending.
+//
+// Radix select on an order-preserving 64-bit key of the score (sign bit
+// flipped for non-negative values, all bits flipped for negative ones; -0
+// is first turned into +0 so that it ties with +0): eight passes over 8-bit
+// digits from the top, each counting in an LDS histogram the digits of the
+// keys that still match the prefix found so far and picking the digit where
+// the running count from the top reaches the number still to be chosen.
+// After the last pass the prefix is T, the k-th largest key, and `rem` of
+// the keys equal to T are to be kept; a last sweep in index order keeps the
+// keys above T and the first `rem` keys equal to T, and compacts them with
+// ballot prefix counts.  Exact, and independent of the schedule.
+__device__ __forceinline__ unsigned long long score_key(double s) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(s + 0.0);
+  return (u >> 63) ? ~u : (u | (1ull << 63));
 }
 
-__global__ void __launch_bounds__(256) topk_sort_kernel(Geom g, const double *__restrict__ scores,
-                                                        int32_t *__restrict__ idx, int P) {
-  extern __shared__ double sel_smem[];
+__global__ void __launch_bounds__(256) topk_select_kernel(Geom g, const double *__restrict__ scores,
+                                                          int32_t *__restrict__ idx) {
+  extern __shared__ unsigned long long sel_keys[];  // [4][nb]
+  __shared__ unsigned hist_all[4][256];
   const int bh = blockIdx.y, h = bh % g.H;
   if (!bit(g.topk, h)) return;
-  const int nb = g.nb, qb = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  double *key = sel_smem;                       // [P]
-  int *id = (int *)(sel_smem + P);              // [P]
-  unsigned char *flag = (unsigned char *)(id + P);  // [P]
-  __shared__ int wave_count[4];
-  const double *row = scores + ((long long)bh * nb + qb) * nb;
-  for (int j = t; j < P; j += 256) {
-    key[j] = j < nb ? row[j] : -INFINITY;
-    id[j] = j < nb ? j : 0x7fffffff;
-    flag[j] = 0;
-  }
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int p = t; p < (P >> 1); p += 256) {
-        const int i = 2 * p - (p & (stride - 1));
-        const int j = i + stride;
-        const double ki = key[i], kj = key[j];
-        const int ii = id[i], ij = id[j];
-        // ascending runs (i & size == 0) put the "before" element first
-        const bool first_i = ((i & size) == 0);
-        const bool swap = first_i ? sel_before(kj, ij, ki, ii) : sel_before(ki, ii, kj, ij);
-        if (swap) {
-          key[i] = kj;
-          key[j] = ki;
-          id[i] = ij;
-          id[j] = ii;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int r = t; r < g.k; r += 256) flag[id[r]] = 1;
-  __syncthreads();
-  int32_t *dst = idx + ((long long)bh * nb + qb) * g.k;
-  int base_count = 0;
-  for (int j0 = 0; j0 < nb; j0 += 256) {
-    const int j = j0 + t;
-    const bool keep = j < nb && flag[j];
-    const uint64_t m = __ballot(keep);
-    if (lane == 0) wave_count[wv] = __popcll(m);
-    __syncthreads();
-    int before = base_count;
-    for (int w2 = 0; w2 < wv; ++w2) before += wave_count[w2];
-    before += __popcll(m & ((1ull << lane) - 1ull));
-    if (keep && before < g.k) dst[before] = j;
-    base_count += wave_count[0] + wave_count[1] + wave_count[2] + wave_count[3];
-    __syncthreads();
-  }
-}
+  const int nb = g.nb, k = g.k, lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const int qb = blockIdx.x * 4 + wv;
+  const bool live = qb < nb;  // dead waves still take part in the barriers
+  unsigned long long *key = sel_keys + (long long)wv * nb;
+  unsigned *hist = hist_all[wv];
+  const double *row = scores + ((long long)bh * nb + (live ? qb : 0)) * nb;
+  for (int j = lane; j < nb; j += 64) key[j] = score_key(row[j]);
 
-int select_pow2(int nb) {
-  int P = 2;
-  while (P < nb) P <<= 1;
-  return P;
+  unsigned long long prefix = 0, mask = 0;
+  int rem = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[lane + 64 * i] = 0;
+    __syncthreads();
+    for (int j = lane; j < nb; j += 64) {
+      const unsigned long long kk = key[j];
+      if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255], 1u);
+    }
+    __syncthreads();
+    // lane L owns bins 4L..4L+3; suf = number of matching keys with digit >= 4L
+    const unsigned c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
+                   c3 = hist[4 * lane + 3];
+    const unsigned c = c0 + c1 + c2 + c3;
+    unsigned suf = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned v = __shfl_down(suf, o);
+      if (lane + o < 64) suf += v;
+    }
+    const unsigned need = unsigned(rem);
+    const bool mine = suf >= need && suf - c < need;  // exactly one lane
+    int d;
+    unsigned greater;
+    if (suf - c0 - c1 - c2 >= need) { d = 4 * lane + 3; greater = suf - c; }
+    else if (suf - c0 - c1 >= need) { d = 4 * lane + 2; greater = suf - c0 - c1 - c2; }
+    else if (suf - c0 >= need) { d = 4 * lane + 1; greater = suf - c0 - c1; }
+    else { d = 4 * lane; greater = suf - c0; }
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+    d = __shfl(d, src);
+    greater = __shfl(greater, src);
+    prefix |= (unsigned long long)d << shift;
+    mask |= 255ull << shift;
+    rem -= int(greater);
+    __syncthreads();  // histogram reads done before the next clear
+  }
+
+  int32_t *dst = idx + ((long long)bh * nb + qb) * k;
+  int taken = 0, eq_seen = 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int j0 = 0; j0 < nb; j0 += 64) {
+    const int j = j0 + lane;
+    const unsigned long long kk = j < nb ? key[j] : 0ull;
+    const bool gt = j < nb && kk > prefix;
+    const bool eq = j < nb && kk == prefix;
+    const unsigned long long beq = __ballot(eq);
+    const bool keep = gt || (eq && eq_seen + __popcll(beq & below) < rem);
+    const unsigned long long bk = __ballot(keep);
+    if (live && keep) dst[taken + __popcll(bk & below)] = j;
+    taken += __popcll(bk);
+    eq_seen += __popcll(beq);
+  }
 }
 
 hipError_t launch_block_select(const Geom &g, int dtype_bf16, View qv, View kv, double *qbar,
                                double *kbar, double *scores, int32_t *idx, hipStream_t st) {
-  dim3 grid1(g.nb, 2, g.B * g.H);
+  dim3 grid1(g.B * g.H, g.nb, 2);
   if (dtype_bf16)
     block_mean_kernel<bf16_t><<<grid1, 256, 0, st>>>(g, qv, kv, qbar, kbar);
   else
     block_mean_kernel<float><<<grid1, 256, 0, st>>>(g, qv, kv, qbar, kbar);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid2((g.nb + 31) / 32, (g.nb + 31) / 32, g.B * g.H);
+  dim3 grid2((g.nb + kScoreTile - 1) / kScoreTile, (g.nb + kScoreTile - 1) / kScoreTile, g.B * g.H);
   block_score_kernel<<<grid2, 256, 0, st>>>(g, qbar, kbar, scores);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int P = select_pow2(g.nb);
-  const size_t lds = size_t(P) * (sizeof(double) + sizeof(int) + 1);
-  if (lds > 64 * 1024)
-    hipFuncSetAttribute((const void *)topk_sort_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        int(lds));
-  dim3 grid3(g.nb, g.B * g.H);
-  topk_sort_kernel<<<grid3, 256, lds, st>>>(g, scores, idx, P);
+  const size_t lds = size_t(4) * g.nb * sizeof(unsigned long long);
+  if (lds > 48 * 1024)
+    hipFuncSetAttribute((const void *)topk_select_kernel,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  dim3 grid3((g.nb + 3) / 4, g.B * g.H);
+  topk_select_kernel<<<grid3, 256, lds, st>>>(g, scores, idx);
   return hipGetLastError();
 }
 
