@@ -97,6 +97,20 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Workgroup barrier without the memory fence of __syncthreads(), whose
+// release half waits for every DMA in flight.  The barrier intrinsic by
+// itself does not order memory accesses in the compiler, so the empty asm
+// statements with a memory clobber pin every access (LDS reads, DMA issues)
+// to its side of the barrier, and the lgkmcnt wait makes this wave's LDS
+// reads complete before any wave passes.  DMA completion is waited for
+// explicitly (vmcnt) by the callers.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt: no wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // K and V tiles are stored row-major ([key][d], 256-byte rows) in LDS.  The
 // 16-byte unit u of row j sits at u ^ kv_swz(j).  kv_swz is a bijection on
 // the low 4 bits of j that swaps its two 2-bit halves, so
@@ -417,10 +431,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     // too, as it cannot tell the two buffers apart there; issuing the DMAs
     // out of its sight to overlap V as well measured no faster.)  Issue
     // order per wave: K(0) V(0) K(1) V(1) ...
-    // The barriers here are bare s_barrier: __syncthreads() also fences,
-    // which waits for every DMA in flight.  The counts are handled by the
-    // explicit waits, and each barrier that frees a buffer follows the
-    // MFMAs that consumed that buffer's LDS reads.
+    // The barriers here are wg_barrier (no fence, so no wait for the DMAs
+    // in flight); DMA completion is handled by the explicit vmcnt waits.
     constexpr int VM_ONE = DMA_PER_WAVE;  // DMA ops of one tensor per wave
     static_assert(VM_ONE < 16, "vmcnt immediate below");
     if (n_tiles > 0) {
@@ -438,16 +450,16 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
       f32x16 s[2];
       bf16x8 pb[4];
       __builtin_amdgcn_s_waitcnt(0x0F70 | VM_ONE);  // K(it) landed, V(it) may be in flight
-      __builtin_amdgcn_s_barrier();
+      wg_barrier();
       qk(K0, s);
-      __builtin_amdgcn_s_barrier();  // every wave is done reading K(it)
+      wg_barrier();  // every wave is done reading K(it)
       if (more) issue_one(krs, k_nxt, K0);
       softmax(k_cur, full, s, pb);
       if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | VM_ONE);  // V(it) landed, K(it+1) may not
       else __builtin_amdgcn_s_waitcnt(0x0F70);
-      __builtin_amdgcn_s_barrier();
+      wg_barrier();
       pv(V0, pb);
-      __builtin_amdgcn_s_barrier();  // every wave is done reading V(it)
+      wg_barrier();  // every wave is done reading V(it)
       if (more) issue_one(vrs, k_nxt, V0);
       k_cur = k_nxt;
     }
