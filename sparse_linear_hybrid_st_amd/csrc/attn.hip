@@ -300,7 +300,10 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;  // running max (raw score units), partial row sum
+  float m_run = -INFINITY, l_run = 0.f;  // running offset (raw score units), partial row sum
+  float m_off = 0.f;                       // m_run * c2 (0 while m_run is -inf)
+  const float thr_gap = 8.f / c2;          // raise the offset past m_run + thr_gap
+  float m_thr = -INFINITY;                 // m_run + thr_gap
 
   // One key tile: S^T = K Q^T (qk), online softmax (softmax), O^T += V^T
   // P^T (pv).  classify tells whether the tile holds any key of this wave's
@@ -336,33 +339,44 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_32x32x16(ka[u][kb], qf[ks + u], s[kb]);
     }
   };
+  // Softmax of one tile, in place.  Edge tiles mask first: key j is kept
+  // iff j < N and, for window heads, |pq - j| <= r, i.e. the unsigned value
+  // pq - j + r is at most 2r (one subtract and one compare per score).
+  // The running offset m_run only has to bound the row's scores loosely: O
+  // and l share it, so the final O / l is exact whatever its value.  It is
+  // raised (and O, l rescaled) only when a score exceeds it by more than 8
+  // in log2 units, so probabilities stay below 2^8 (no overflow in fp32
+  // sums or in bf16).  Each lane tests its own 32 scores against that
+  // threshold; only when some lane of the wave crosses it is the row max
+  // combined across the two half-waves (which hold the other 32 keys of the
+  // same query), so both halves always share one offset.  The row sum l
+  // adds the bf16-rounded probabilities in pairs (v_dot2 with (1, 1)): the
+  // same values the PV product weighs V with.
   auto softmax = [&](int k0, bool full, f32x16 (&s)[2], bf16x8 (&pb)[4]) {
-    float mx = -INFINITY;
-    if (full) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    } else {
+    if (!full) {
+      const int jl = k0 + 4 * hl;                        // j = jl + c below
+      const unsigned wb = unsigned(pq - jl + g.r);        // pq - j + r = wb - c
+      const int lim = g.N - jl;                          // j < N  <=>  c < lim
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
           // bitwise, not short-circuit: keeps the mask a select, not a branch
-          const bool keep = (j < g.N) & (TOPK | (abs(pq - j) <= g.r));
+          const bool keep = (c < lim) & (TOPK | (wb - unsigned(c) <= unsigned(2 * g.r)));
           s[kb][r] = keep ? s[kb][r] : -INFINITY;
-          mx = fmaxf(mx, s[kb][r]);
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // The running offset m_run only has to bound the row's scores loosely:
-    // O and l share it, so the final O / l is exact whatever its value.  It
-    // is raised (and O, l rescaled) only when a score exceeds it by more
-    // than 8 in log2 units, so later probabilities stay below 2^8 (no
-    // overflow in fp32 sums or in bf16) while the rescale runs on few tiles.
-    if (__any((mx - m_run) * c2 > 8.f)) {
-      const float m_new = fmaxf(m_run, mx);
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    if (__any(mx > m_thr)) {
+      const unsigned um = __float_as_uint(mx);
+      const auto sw = __builtin_amdgcn_permlane32_swap(um, um, false, false);
+      const float mxa = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const float m_new = fmaxf(m_run, mxa);
       const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       l_run *= alpha;
 #pragma unroll
@@ -370,20 +384,23 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       m_run = m_new;
+      m_off = m_run == -INFINITY ? 0.f : m_run * c2;
+      m_thr = m_run + thr_gap;
     }
-    const float moff = m_run == -INFINITY ? 0.f : m_run * c2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         bf16x8 pv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // v_exp_f32 directly: arguments are <= 0, tiny results flush to 0
-          const float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e], c2, -moff));
-          l_run += pe;
-          pv[e] = (__bf16)pe;
-        }
+        for (int e = 0; e < 8; ++e)
+          // v_exp_f32 directly: arguments are <= 8, tiny results flush to 0
+          pv[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e], c2, -m_off));
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, l_run, false);
         pb[2 * kb + half] = pv;
       }
   };
