@@ -68,13 +68,18 @@ __global__ void __launch_bounds__(256) block_mean_kernel(Geom g, View qv, View k
   }
 }
 
-// Block scores S[qb][kb] = qbar[qb] . kbar[kb] for every Top-K (b, h), as a
-// tiled fp64 product: workgroup (tile_q, tile_k, bh) computes a 128 x 128
+// Block scores S[qb][kb] = qbar[qb] . kbar[kb] for every Top-K (b, h), on
+// the fp64 matrix cores (v_mfma_f64_16x16x4_f64; a dot product of 128
+// terms has no room for a third operand per FMA in the vector units'
+// register banks).  Workgroup (tile_q, tile_k, bh) computes a 128 x 128
 // tile from 16-feature slices of both operands staged in LDS
-// (feature-major); thread t owns query rows 8*(t/16)..+7 and key columns
-// 8*(t%16)..+7, so each feature step is 16 LDS values for 64 FMAs.  Each
-// product is a plain left-to-right fp64 sum over the d features.
+// (feature-major); wave w owns the 64 x 64 quadrant (64*(w/2), 64*(w%2)) as
+// 4 x 4 blocks of 16 x 16.  MFMA layout: lane l supplies A[i = l%16][k =
+// l/16] and B[k = l/16][j = l%16]; its four results are D[i = 4r + l/16][j
+// = l%16], r = 0..3.  Each product is an fp64 sum over the d features (the
+// matrix unit's own order inside each step of 4).
 constexpr int kScoreTile = 128;
+typedef __attribute__((ext_vector_type(4))) double f64x4;
 
 __global__ void __launch_bounds__(256) block_score_kernel(Geom g, const double *__restrict__ qbar,
                                                           const double *__restrict__ kbar,
@@ -82,27 +87,33 @@ __global__ void __launch_bounds__(256) block_score_kernel(Geom g, const double *
   constexpr int TS = kScoreTile, LD = TS + 2;  // +2: the feature-major stores spread over banks
   const int bh = blockIdx.z, h = bh % g.H;
   if (!bit(g.topk, h)) return;
-  const int nb = g.nb, D = g.D, t = threadIdx.x;
+  const int nb = g.nb, D = g.D, t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int q0 = blockIdx.x * TS, k0 = blockIdx.y * TS;
   __shared__ __attribute__((aligned(16))) double qs[16 * LD];
   __shared__ __attribute__((aligned(16))) double ks[16 * LD];
   const double *qb = qbar + (long long)bh * nb * D;
   const double *kb = kbar + (long long)bh * nb * D;
-  const int ti = 8 * (t >> 4), tj = 8 * (t & 15);
+  const int wq = 64 * (w >> 1), wk = 64 * (w & 1);
+  const int li = lane & 15, lk = lane >> 4;
   // staging: thread t loads features f8..f8+7 of row r (64 contiguous bytes)
   const int lr = t >> 1, f8 = 8 * (t & 1);
-  double acc[8][8];
+  f64x4 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
-  for (int f0 = 0; f0 < D; f0 += 16) {
-    double qv[8], kv[8];
+    for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // the next slice is fetched into registers while the current one computes
+  double qv[8], kv[8];
+  auto fetch = [&](int f0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       qv[e] = (q0 + lr < nb) ? qb[(long long)(q0 + lr) * D + f0 + f8 + e] : 0.0;
       kv[e] = (k0 + lr < nb) ? kb[(long long)(k0 + lr) * D + f0 + f8 + e] : 0.0;
     }
+  };
+  fetch(0);
+  for (int f0 = 0; f0 < D; f0 += 16) {
     __syncthreads();  // previous slice's reads are done
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -110,27 +121,34 @@ __global__ void __launch_bounds__(256) block_score_kernel(Geom g, const double *
       ks[(f8 + e) * LD + lr] = kv[e];
     }
     __syncthreads();
-#pragma unroll 4
-    for (int f = 0; f < 16; ++f) {
-      double a[8], bv[8];
+    if (f0 + 16 < D) fetch(f0 + 16);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a[i] = qs[f * LD + ti + i];
+    for (int s4 = 0; s4 < 16; s4 += 4) {
+      double a[4], bv[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) bv[j] = ks[f * LD + tj + j];
+      for (int i = 0; i < 4; ++i) a[i] = qs[(s4 + lk) * LD + wq + 16 * i + li];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int j = 0; j < 4; ++j) bv[j] = ks[(s4 + lk) * LD + wk + 16 * j + li];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], bv[j], acc[i][j]);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bv[j], acc[i][j], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (q0 + ti + i >= nb) continue;
-    double *dst = scores + ((long long)bh * nb + q0 + ti + i) * nb;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (k0 + tj + j < nb) dst[k0 + tj + j] = acc[i][j];
-  }
+    for (int r = 0; r < 4; ++r) {
+      const int row = q0 + wq + 16 * i + 4 * r + lk;
+      if (row >= nb) continue;
+      double *dst = scores + ((long long)bh * nb + row) * nb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = k0 + wk + 16 * j + li;
+        if (col < nb) dst[col] = acc[i][j][r];
+      }
+    }
 }
 
 // Selection, one wave per query block (4 per workgroup): the k best key

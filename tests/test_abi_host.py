@@ -74,6 +74,20 @@ def test_bad_topk_and_rope_and_kind():
     assert _status(p)[0] == 3
 
 
+def test_size_limits():
+    """Row indices are 32-bit inside the kernels: B*H*N must stay below 2^31
+    (and N below 2^28); the largest accepted sizes pass."""
+    p = S.problem_from_workload(configs.swa_480p())
+    p.grid_f, p.grid_h, p.grid_w = 1 << 10, 1 << 9, 1 << 9      # N = 2^28
+    p.n_heads, p.batch = 4, 2                                    # B*H*N = 2^31
+    p.window_radius = 64
+    assert _status(p)[0] == 2 and b"2^31" in S.lib().salad_last_error()
+    p.batch = 1                                                  # B*H*N = 2^30
+    assert _status(p)[0] == 0, S.lib().salad_last_error()
+    p.grid_f = (1 << 10) + 1                                     # N > 2^28
+    assert _status(p)[0] == 2
+
+
 def test_null_and_misaligned_pointers_fail_before_launch():
     L = S.lib()
     p = S.problem_from_workload(configs.tiny_f32())
