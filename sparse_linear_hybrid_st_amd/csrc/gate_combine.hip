@@ -34,6 +34,8 @@ __global__ void __launch_bounds__(256) gate_partial_kernel(Geom g, const T *__re
     float wv[8], cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < 8; ++e) wv[e] = io<T>::ld(w + cg * 8 + e);
+    // unrolled so that several rows' loads are in flight per thread
+#pragma unroll 8
     for (int n = n0; n < n1; ++n) {
       const T *src = x + ((long long)b * g.N + n) * C + cg * 8;
       T v[8];

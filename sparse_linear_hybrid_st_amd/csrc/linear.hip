@@ -245,6 +245,7 @@ __global__ void linear_reduce_kernel(int D, int S, const float *__restrict__ par
   if (e >= per) return;
   const float *p = partial + (long long)bh * S * per + e;
   float acc = 0.f;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) acc += p[(long long)s * per];
   if (e < D * D)
     h[(long long)bh * D * D + e] = acc;
@@ -253,53 +254,79 @@ __global__ void linear_reduce_kernel(int D, int S, const float *__restrict__ par
 }
 
 // ---------------------------------------------------------------------------
-// Projection for the fused layer (bf16, d = 128): fold the static projection
-// and the gate into the summed state,
-//   Hp = s_b * H W_p,   so that   s_b * (O_l W_p) = relu(q) Hp / (relu(q) . Z + eps)
-// (the normaliser is one scalar per token, so it commutes with W_p).  Hp is
-// written transposed, as bf16 rows [d_out][d_in] (the MFMA A operand of the
-// fused epilogue).  Grid (16, B*H): workgroup (blk, bh) computes rows
-// i = 8*blk .. +7 of H W_p; thread t owns row 8*blk + t/32 and columns
-// (t%32) + 32m.  W_p is staged in LDS as fp32.
+// Finalize, d = 128 (fused layer): sum the split-N partial states of 8 rows
+// of H (and, in block 0, of Z) in a fixed order, keep them in LDS and fold
+// the projection and the gate in: Hp[j][i] = bf16(s_b * (H W_p)[i][j]).
+// Grid (16, B*H); block blk owns rows 8*blk..+7.  W_p is staged once per
+// block as bf16 (16-byte loads); thread t computes row t/32 at columns
+// (t%32) + 32m, m < 4.  H and Z are also written out in fp32.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ void __launch_bounds__(256) linear_project_kernel(Geom g, const float *__restrict__ hm,
-                                                             const T *__restrict__ w_p,
-                                                             const float *__restrict__ s_gate,
-                                                             bf16_t *__restrict__ hp) {
-  constexpr int D = 128;
-  __shared__ float Ws[D * D];
-  __shared__ float Hs[8][D];
+__global__ void __launch_bounds__(256) linear_finalize_kernel(Geom g, int S,
+                                                              const float *__restrict__ partial,
+                                                              const T *__restrict__ w_p,
+                                                              const float *__restrict__ s_gate,
+                                                              float *__restrict__ hm,
+                                                              float *__restrict__ zv,
+                                                              bf16_t *__restrict__ hp) {
+  constexpr int D = 128, per = D * D + D;
+  __shared__ __attribute__((aligned(16))) T Ws[D * D];
+  __shared__ float Hs[8 * D];
   const int blk = blockIdx.x, bh = blockIdx.y, b = bh / g.H, t = threadIdx.x;
-  for (int e = t; e < D * D; e += 256) Ws[e] = io<T>::ld(w_p + e);
-  for (int e = t; e < 8 * D; e += 256) Hs[e / D][e % D] = hm[((long long)bh * D + 8 * blk) * D + e];
+  // stage W_p (16-byte chunks)
+  constexpr int VEC = 16 / sizeof(T);
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  for (int e = t * VEC; e < D * D; e += 256 * VEC)
+    *(u32x4 *)(Ws + e) = *(const u32x4 *)(w_p + e);
+  // reduce this block's 8 rows (elements t, t + 256, .. of the 1024), fixed order
+  const float *p = partial + (long long)bh * S * per + 8 * blk * D;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  // unrolled so that several splits' loads are in flight; the adds keep
+  // their order
+#pragma unroll 8
+  for (int s = 0; s < S; ++s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += p[(long long)s * per + t + 256 * i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    Hs[t + 256 * i] = acc[i];
+    hm[((long long)bh * D + 8 * blk) * D + t + 256 * i] = acc[i];
+  }
+  if (blk == 0 && t < D) {
+    const float *pz = partial + (long long)bh * S * per + D * D + t;
+    float az = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) az += pz[(long long)s * per];
+    zv[(long long)bh * D + t] = az;
+  }
   __syncthreads();
   const int ii = t >> 5, jg = t & 31;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
   for (int k = 0; k < D; ++k) {
-    const float hv = Hs[ii][k];
+    const float hv = Hs[ii * D + k];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc[m] = fmaf(hv, Ws[k * D + jg + 32 * m], acc[m]);
+    for (int m = 0; m < 4; ++m) o[m] = fmaf(hv, io<T>::ld(Ws + k * D + jg + 32 * m), o[m]);
   }
   const float sb = s_gate[b];
   bf16_t *dst = hp + (long long)bh * D * D;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const __bf16 v = (__bf16)(sb * acc[m]);
+    const __bf16 v = (__bf16)(sb * o[m]);
     dst[(jg + 32 * m) * D + 8 * blk + ii] = *(const bf16_t *)&v;
   }
 }
 
 hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial, const void *w_p,
                                   const float *s, float *h, bf16_t *hp, float *z, hipStream_t st) {
+  if (g.D != 128) return hipErrorInvalidValue;
   const int S = linear_splits(g);
-  dim3 grid1((g.D * g.D + g.D + 255) / 256, g.B * g.H);
-  linear_reduce_kernel<<<grid1, 256, 0, st>>>(g.D, S, partial, h, z);
-  dim3 grid2(16, g.B * g.H);
+  dim3 grid(16, g.B * g.H);
   if (bf16)
-    linear_project_kernel<bf16_t><<<grid2, 256, 0, st>>>(g, h, (const bf16_t *)w_p, s, hp);
+    linear_finalize_kernel<bf16_t><<<grid, 256, 0, st>>>(g, S, partial, (const bf16_t *)w_p, s, h, z, hp);
   else
-    linear_project_kernel<float><<<grid2, 256, 0, st>>>(g, h, (const float *)w_p, s, hp);
+    linear_finalize_kernel<float><<<grid, 256, 0, st>>>(g, S, partial, (const float *)w_p, s, h, z, hp);
   return hipGetLastError();
 }
 
