@@ -41,7 +41,7 @@ __all__ = [
     "to_working", "block_means", "block_scores", "topk_blocks", "topk_gap",
     "swa_keys", "topk_keys", "sparse_attention", "sparse_attention_head",
     "linear_state", "linear_apply", "gate", "combine",
-    "swa_pair_count", "topk_pair_count", "attn_forward",
+    "swa_pair_count", "topk_pair_count", "branch_kept", "attn_forward",
 ]
 
 HEAD_SPATIAL = 0
@@ -333,16 +333,26 @@ def combine(o_s: np.ndarray, o_l: np.ndarray, w_p: np.ndarray, s: float) -> np.n
 # Whole layer
 # --------------------------------------------------------------------------
 
+def branch_kept(s: float, tau: float) -> bool:
+    """Post-tuning branch dropping ([G] 2 C; [S] step 8): at inference the
+    linear branch of a sample is switched off when its dynamic scale s is
+    below a threshold tau (the pages calibrate one per timestep; it is an
+    input here).  Reading: s < tau drops, so tau <= 0 never drops (s > 0)."""
+    return not (s < tau)
+
+
 def attn_forward(q, k, v, x, w_p, gate_w, gate_b, *, grid, head_kinds,
                  window_radius, block, topk, io_dtype="bf16", rope=False,
                  rope_dims=(44, 42, 42), rope_base=10000.0, softmax_scale=None,
-                 linear_eps=1e-6, s_override=None, rows=None):
+                 linear_eps=1e-6, s_override=None, rows=None, drop_tau=0.0):
     """Hybrid attention layer output for Q, K, V [B, N, H, d] and X [B, N, C].
 
     Steps ([S] steps 2-6): optional 3D RoPE on Q and K (materialised in the
     storage type ``io_dtype``); per-head working order ([I] 1.1); sparse
     branch per head (window or Top-K); linear branch on the same Q, K, V;
     gate per sample; O = O_s + s * (O_l W_p) written back in token order.
+    With ``drop_tau`` a sample whose gate value is below it keeps only the
+    sparse branch, O = O_s ([G] 2 C; see ``branch_kept``).
 
     Everything but the gate is per (sample, head), so each head's inputs
     are prepared only when that head is needed.  ``rows`` (optional, a list
@@ -395,8 +405,11 @@ def attn_forward(q, k, v, x, w_p, gate_w, gate_b, *, grid, head_kinds,
             o_s, _ = sparse_attention_head(int(head_kinds[h]), c["qw"], c["kw"], c["vw"],
                                            r=window_radius, bs=block, k=topk, scale=scale,
                                            rows=[int(inv[h][n])], idx=c["idx"])
-            o_l = linear_apply(c["q"][n:n + 1], c["H"], c["Z"], linear_eps)
-            result[(b, n, h)] = combine(o_s, o_l, w_p, s[b])[0]
+            if branch_kept(s[b], drop_tau):
+                o_l = linear_apply(c["q"][n:n + 1], c["H"], c["Z"], linear_eps)
+                result[(b, n, h)] = combine(o_s, o_l, w_p, s[b])[0]
+            else:
+                result[(b, n, h)] = o_s[0]
         return result
 
     out = np.empty((B, N, H, v.shape[3]))
@@ -419,7 +432,7 @@ def attn_forward(q, k, v, x, w_p, gate_w, gate_b, *, grid, head_kinds,
             o_l = linear_apply(c["q"], c["H"], c["Z"], linear_eps)
             o_s_all[b, :, h] = o_s
             o_l_all[b, :, h] = o_l
-            out[b, :, h] = combine(o_s, o_l, w_p, s[b])
+            out[b, :, h] = combine(o_s, o_l, w_p, s[b]) if branch_kept(s[b], drop_tau) else o_s
             Hs[b, h], Zs[b, h] = c["H"], c["Z"]
             q_used[b, :, h], k_used[b, :, h] = c["q"], c["k"]
             del cache[(b, h)]

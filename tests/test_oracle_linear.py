@@ -136,6 +136,37 @@ def test_layer_combine_and_gate_override():
         np.testing.assert_allclose(part[key], res["out"][key], atol=1e-14)
 
 
+def test_layer_branch_dropping():
+    """[G] 2 C: a sample whose gate value is below the threshold keeps only
+    the sparse branch.  Pinned against the zero-projection layer (which has
+    no linear term by construction) and against the undropped layer."""
+    grid, H, d = (2, 3, 4), 2, 4
+    q, k, v, x, wp, gw = _layer_inputs(2, grid, H, d, 23)
+    x[1] += 3.0                                  # a second, different gate value
+    kw = dict(grid=grid, head_kinds=[0, 1], window_radius=3, block=8, topk=1, io_dtype="f32")
+    full = O.attn_forward(q, k, v, x, wp, gw, 0.1, **kw)
+    sparse_only = O.attn_forward(q, k, v, x, np.zeros_like(wp), gw, 0.1, **kw)
+    s0, s1 = full["s"]
+    assert s0 != s1
+    lo, hi = (0, 1) if s0 < s1 else (1, 0)
+    tau = 0.5 * (s0 + s1)
+    mixed = O.attn_forward(q, k, v, x, wp, gw, 0.1, drop_tau=tau, **kw)
+    np.testing.assert_array_equal(mixed["out"][lo], sparse_only["out"][lo])
+    np.testing.assert_array_equal(mixed["out"][hi], full["out"][hi])
+    np.testing.assert_array_equal(mixed["s"], full["s"])          # s reports the gate value
+    for t, ref in ((0.0, full), (1.0, sparse_only)):
+        np.testing.assert_array_equal(O.attn_forward(q, k, v, x, wp, gw, 0.1, drop_tau=t, **kw)["out"],
+                                      ref["out"])
+    # a gate value equal to the threshold is kept (strict comparison)
+    eq = O.attn_forward(q, k, v, x, wp, gw, 0.1, drop_tau=full["s"][lo], **kw)
+    np.testing.assert_array_equal(eq["out"][lo], full["out"][lo])
+    # the rows form agrees
+    rows = [(lo, 0, 0), (lo, 17, 1), (hi, 5, 0)]
+    part = O.attn_forward(q, k, v, x, wp, gw, 0.1, drop_tau=tau, rows=rows, **kw)
+    for key in rows:
+        np.testing.assert_allclose(part[key], mixed["out"][key], atol=1e-14)
+
+
 def test_layer_temporal_head_is_window_on_regrouped_sequence():
     # a temporal head's output for token n equals a plain window attention on
     # the regrouped sequence, read back at n's working position

@@ -96,6 +96,14 @@ def _bf16_truncate(x):                 # rounds toward zero instead of to neares
     return np.trunc(x / sp) * sp
 
 
+def _drop_inverted(s, tau):            # drops the samples above the threshold
+    return s < tau
+
+
+def _drop_at_equality(s, tau):         # drops a gate value equal to the threshold
+    return s > tau
+
+
 CASES = [
     ("st_permutation", _perm_inverse, lambda: TO.test_st_permutation_matches_sort_construction((4, 8, 8))),
     ("swa_keys", _swa_keys_short, lambda: TA.test_window_matches_masked_dense(64, 5)),
@@ -110,6 +118,8 @@ CASES = [
     ("gate", _gate_sum, TL.test_gate_values),
     ("combine", _combine_transposed, TL.test_combine_special_cases),
     ("round_to_bf16", _bf16_truncate, TO.test_round_to_bf16_exact_on_float64_values),
+    ("branch_kept", _drop_inverted, TL.test_layer_branch_dropping),
+    ("branch_kept", _drop_at_equality, TL.test_layer_branch_dropping),
 ]
 
 
