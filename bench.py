@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--workload", default="480p-stswa-h12")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--branch-drop-tau", type=float, default=0.0,
+                    help="post-tuning branch dropping threshold (samples whose gate value is "
+                         "below it keep only the sparse branch); 0 never drops")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size reference for the HBM byte counters)")
@@ -140,7 +143,7 @@ def main():
     w = C.all_workloads()[args.workload]
     print(f"[bench] workload {w.name}: {w.description}", file=sys.stderr, flush=True)
     inp = I.make_inputs(w)
-    p = S.problem_from_workload(w)
+    p = S.problem_from_workload(w, branch_drop_tau=args.branch_drop_tau)
     dev = {n: inp[n].cuda() for n in ("q", "k", "v", "x", "w_p", "gate_w")}
     out = torch.empty_like(dev["q"])
     s_out = torch.empty(w.batch, dtype=torch.float32, device="cuda")
@@ -196,7 +199,9 @@ def main():
                    "heads": w.n_heads, "head_dim": w.head_dim,
                    "head_kinds": "".join("STK"[k] for k in w.head_kinds),
                    "window_radius": w.window_radius, "block": w.block, "topk": w.topk,
-                   "rope": w.rope, "computed_pairs": pairs,
+                   "rope": w.rope, "branch_drop_tau": args.branch_drop_tau,
+                   "samples_dropped": int((s_out.cpu() < args.branch_drop_tau).sum()),
+                   "computed_pairs": pairs,
                    "density": pairs / (w.batch * w.n_heads * w.N * w.N)},
         "roofline": {"bound": "mfma", "kernel": "sparse attention (attn_bf16_kernel)",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

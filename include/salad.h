@@ -91,6 +91,11 @@ typedef struct {
   int32_t rope_dims[3];               /* frame/height/width segment sizes, even, sum d */
   float rope_base;                    /* rotary base (10000)                      */
   int32_t io_dtype;                   /* salad_dtype                              */
+  float branch_drop_tau;              /* post-tuning branch dropping ([G] 2 C, [S]
+                                         step 8): a sample whose gate value s_b is
+                                         below it keeps only the sparse branch
+                                         (out = O_s) and its linear-branch work is
+                                         skipped; 0 never drops (s_b > 0); finite */
 } salad_problem;
 
 /* Bytes of workspace that any entry point below may need for problem *p
@@ -153,15 +158,19 @@ salad_status salad_gate(const salad_problem *p, const void *x, const void *w, fl
 /* Combine ([S] steps 4 and 6): out[b, pi_h(p), h, :] =
  * o_s[b,h,p,:] + s[b] * (o_l[b,h,p,:] W_p), W_p [d_in, d_out] row-major in
  * io_dtype, shared by all heads, no bias.  o_s, o_l float32 working layout;
- * s float32 [B] device; out boundary layout in io_dtype. */
+ * s float32 [B] device; out boundary layout in io_dtype.  A sample with
+ * s_b < p->branch_drop_tau gets out = O_s (branch dropping, [G] 2 C). */
 salad_status salad_combine(const salad_problem *p, const float *o_s, const float *o_l,
                            const void *w_p, const float *s, void *out, hipStream_t stream);
 
-/* Whole layer ([S] steps 2-6): q, k, v [B,N,H,d], x [B,N,C], w_p [d,d],
- * gate_w [C] in io_dtype -> out [B,N,H,d] in io_dtype.  s_override (device
- * float [B]) replaces the gate when non-NULL; s_out (device float [B]) and
- * idx_out ([B,H,nb,topk] int32, Top-K heads only) receive the gate values
- * and the block selection when non-NULL.  Workspace: salad_workspace_size. */
+/* Whole layer ([S] steps 2-6, and step 8 through p->branch_drop_tau): q, k,
+ * v [B,N,H,d], x [B,N,C], w_p [d,d], gate_w [C] in io_dtype -> out [B,N,H,d]
+ * in io_dtype.  s_override (device float [B]) replaces the gate when
+ * non-NULL; s_out (device float [B]) and idx_out ([B,H,nb,topk] int32,
+ * Top-K heads only) receive the gate values (before any dropping) and the
+ * block selection when non-NULL.  A sample with s_b < branch_drop_tau gets
+ * out = O_s; the decision is taken on the device, so nothing synchronises.
+ * Workspace: salad_workspace_size. */
 salad_status salad_attn_forward(const salad_problem *p, const void *q, const void *k,
                                 const void *v, const void *x, const void *w_p,
                                 const void *gate_w, float gate_b, const float *s_override,

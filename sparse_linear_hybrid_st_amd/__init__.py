@@ -41,7 +41,7 @@ class Problem(ctypes.Structure):
         ("window_radius", ctypes.c_int32), ("block", ctypes.c_int32), ("topk", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("linear_eps", ctypes.c_float),
         ("rope", ctypes.c_int32), ("rope_dims", ctypes.c_int32 * 3), ("rope_base", ctypes.c_float),
-        ("io_dtype", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32), ("branch_drop_tau", ctypes.c_float),
     ]
 
     @property
@@ -108,7 +108,7 @@ def _check(status: int):
 
 def make_problem(*, batch, n_heads, head_dim, grid, head_kinds, window_radius=0, block=64,
                  topk=1, softmax_scale=0.0, linear_eps=1e-6, rope=False, rope_dims=(0, 0, 0),
-                 rope_base=10000.0, io_dtype="bf16") -> Problem:
+                 rope_base=10000.0, io_dtype="bf16", branch_drop_tau=0.0) -> Problem:
     p = Problem()
     p.batch, p.n_heads, p.head_dim = batch, n_heads, head_dim
     p.grid_f, p.grid_h, p.grid_w = grid
@@ -121,14 +121,15 @@ def make_problem(*, batch, n_heads, head_dim, grid, head_kinds, window_radius=0,
         p.rope_dims[i] = int(rope_dims[i])
     p.rope_base = rope_base
     p.io_dtype = SALAD_BF16 if io_dtype == "bf16" else SALAD_F32
+    p.branch_drop_tau = branch_drop_tau
     return p
 
 
-def problem_from_workload(w) -> Problem:
+def problem_from_workload(w, branch_drop_tau=0.0) -> Problem:
     return make_problem(batch=w.batch, n_heads=w.n_heads, head_dim=w.head_dim, grid=w.grid,
                         head_kinds=w.head_kinds, window_radius=w.window_radius, block=w.block,
                         topk=w.topk, rope=w.rope, rope_dims=w.rope_dims, rope_base=w.rope_base,
-                        io_dtype=w.io_dtype)
+                        io_dtype=w.io_dtype, branch_drop_tau=branch_drop_tau)
 
 
 # ---- marshalling helpers --------------------------------------------------

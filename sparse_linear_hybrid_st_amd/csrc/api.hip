@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
 #include <string>
 
 #include "../../include/salad.h"
@@ -96,6 +97,9 @@ salad_status validate(const salad_problem *p, Info *inf) {
   }
   g.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf(float(p->head_dim));
   g.eps = p->linear_eps;
+  if (!std::isfinite(p->branch_drop_tau))
+    return fail(SALAD_ERR_SHAPE, "branch_drop_tau must be finite");
+  g.drop_tau = p->branch_drop_tau;
   g.rope_base = p->rope_base;
   for (int i = 0; i < 3; ++i) g.rope_dims[i] = p->rope_dims[i];
   if (p->rope) {
@@ -449,7 +453,7 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
     for (int i = 0; i < 4; ++i) work[i] = direct ? g.temporal[i] : ~0ull;
     const View kw = working_view(g, wk), vw = working_view(g, wv);
     bf16_t *hp = (bf16_t *)(w + pl.hp);
-    if ((e = launch_linear_partials(g, kb, vb, (float *)scratch, (bf16_t *)wk, (bf16_t *)wv, work,
+    if ((e = launch_linear_partials(g, kb, vb, (float *)scratch, (bf16_t *)wk, (bf16_t *)wv, work, s,
                                     stream)) != hipSuccess ||
         (e = launch_linear_finalize(g, 1, (const float *)scratch, w_p, s, hm, hp, zv, stream)) != hipSuccess)
       return hip_status(e, "salad_attn_forward: linear state");
@@ -461,7 +465,7 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
       if (e != hipSuccess) return hip_status(e, "salad_attn_forward: block select");
     }
     if ((e = prof_mark(0, stream)) != hipSuccess ||
-        (e = launch_attn_fused(g, qv, kw, vw, kd, vd, work, idx, hp, zv, boundary_view(g, out),
+        (e = launch_attn_fused(g, qv, kw, vw, kd, vd, work, idx, hp, zv, s, boundary_view(g, out),
                                stream)) != hipSuccess ||
         (e = prof_mark(1, stream)) != hipSuccess)
       return hip_status(e, "salad_attn_forward: attention");

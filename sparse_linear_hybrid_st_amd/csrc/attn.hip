@@ -130,6 +130,7 @@ struct AttnArgs {
   float *o_s;            // staged: working layout fp32 output
   const bf16_t *hp;      // fused: [B*H][128][128] bf16, s_b * (H W_p)^T
   const float *z;        // fused: [B*H][128] linear normaliser state
+  const float *s_gate;   // fused: [B] gate values (branch dropping below g.drop_tau)
   View out;              // fused: output rows (boundary layout, scattered)
   int n_heads_sel;       // heads handled by this launch
   uint8_t heads[kMaxHeads];
@@ -506,6 +507,22 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   const float inv = 1.f / l_tot;
 
   if constexpr (FUSED) {
+    // Branch dropping ([G] 2 C): a sample whose gate value is below the
+    // threshold keeps only the sparse branch (its state was not computed).
+    if (a.s_gate[b] < g.drop_tau) {
+      if (pq >= g.N) return;
+      bf16_t *orow = (bf16_t *)a.out.base + row_offset(g, a.out, b, h, pq);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * r4 + e] * inv);
+          *(bf16x4 *)(orow + 32 * db + 8 * r4 + 4 * hl) = v;
+        }
+      return;
+    }
     // Linear branch, projection, gate and combine for this wave's queries:
     //   out = O_s + relu(q) Hp / (relu(q) . Z + eps),  Hp = s_b (H W_p)^T
     // Hp rows 0..63 go to K0 and rows 64..127 to V0 (same swizzle as K).
@@ -640,7 +657,7 @@ hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv
 
 hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, View vd,
                              const uint64_t work[4], const int32_t *idx, const bf16_t *hp,
-                             const float *z, View outv, hipStream_t st) {
+                             const float *z, const float *s_gate, View outv, hipStream_t st) {
   bool any_work = false, any_direct = false;
   for (int h = 0; h < g.H; ++h) {
     const bool w = (work[h >> 6] >> (h & 63)) & 1ull;
@@ -660,6 +677,7 @@ hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, 
   a.idx = idx;
   a.hp = hp;
   a.z = z;
+  a.s_gate = s_gate;
   a.out = outv;
   return launch_bf16<true>(a, st);
 }

@@ -95,6 +95,7 @@ struct Geom {
   int block, k, nb;      // Top-K block size, kept blocks, number of blocks
   float scale;           // softmax scale
   float eps;             // linear denominator guard
+  float drop_tau;        // branch dropping: samples with s_b < drop_tau keep only O_s
   int rope_dims[3];
   float rope_base;
   FastDiv fdF, fdS, fdW;  // division by F, Hg*Wg and Wg

@@ -131,6 +131,7 @@ __global__ void __launch_bounds__(256) combine_kernel(Geom g, const float *__res
       for (int m = 0; m < NC; ++m) acc[a][m] = fmaf(ol[a], wv[m], acc[a][m]);
   }
   const float sb = s[b];
+  const bool dropped = sb < g.drop_tau;  // branch dropping ([G] 2 C): out = O_s
   const bool temporal = bit(g.temporal, h);
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -142,7 +143,7 @@ __global__ void __launch_bounds__(256) combine_kernel(Geom g, const float *__res
 #pragma unroll
     for (int m = 0; m < NC; ++m) {
       const int c = cg + 16 * m;
-      io<T>::st(dst + c, os[c] + sb * acc[a][m]);
+      io<T>::st(dst + c, dropped ? os[c] : os[c] + sb * acc[a][m]);
     }
   }
 }

@@ -51,8 +51,11 @@ hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float 
 // Also writes working-layout copies of K / V when kw_out / vw_out are non-null.
 // kw_out / vw_out (working layout) receive the rows of the heads flagged
 // in copy_heads.
+// s_gate (device, nullable): samples with s_b < g.drop_tau skip the state
+// and only write their copies.
 hipError_t launch_linear_partials(const Geom &g, View kv, View vv, float *partial, bf16_t *kw_out,
-                                  bf16_t *vw_out, const uint64_t copy_heads[4], hipStream_t st);
+                                  bf16_t *vw_out, const uint64_t copy_heads[4], const float *s_gate,
+                                  hipStream_t st);
 // h: [B*H][128][128] fp32 state (workspace); hp: [B*H][128][128] bf16 =
 // s_b * (H W_p)^T; z: [B*H][128] fp32.
 hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial, const void *w_p,
@@ -61,9 +64,10 @@ hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial,
 // permutation fused into the epilogue; out in the boundary layout.
 // Heads flagged in `work` read K, V through kw, vw (working copies), the
 // others through kd, vd (rows in working order where they already are).
+// s_gate: samples with s_b < g.drop_tau skip the linear term (out = O_s).
 hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, View vd,
                              const uint64_t work[4], const int32_t *idx, const bf16_t *hp,
-                             const float *z, View outv, hipStream_t st);
+                             const float *z, const float *s_gate, View outv, hipStream_t st);
 // Whether the attention kernel can stream K, V rows through these views.
 bool kv_direct_ok(const Geom &g, View kd, View vd);
 hipError_t launch_linear_apply(const Geom &g, int bf16, View qv, const float *h, const float *z,

@@ -73,7 +73,8 @@ __global__ void __launch_bounds__(256, 2) linear_state_bf16_kernel(Geom g, View 
                                                                 int S, int chunk,
                                                                 bf16_t *__restrict__ kw_out,
                                                                 bf16_t *__restrict__ vw_out,
-                                                                HeadMask copy) {
+                                                                HeadMask copy,
+                                                                const float *__restrict__ s_gate) {
   constexpr int D = 128, TT = 64;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[TT * D];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[TT * D];
@@ -85,6 +86,22 @@ __global__ void __launch_bounds__(256, 2) linear_state_bf16_kernel(Geom g, View 
   const bf16_t *vb = (const bf16_t *)vv.base;
   const long long wbase = (long long)bh * g.N * D;  // working-layout copy of this (b, h)
   if (!bit(copy.w, h)) kw_out = vw_out = nullptr;
+  // Branch dropping: a dropped sample needs no linear state, only the
+  // working copies of its temporal heads (the sparse branch reads them).
+  if (s_gate && s_gate[b] < g.drop_tau) {
+    if (!kw_out && !vw_out) return;
+    for (int base = n0; base < n1; base += TT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = base + rg + 16 * i;
+        if (n >= n1) continue;
+        const long long w_at = wbase + (long long)n * D + c * 8;
+        if (kw_out) *(u32x4 *)(kw_out + w_at) = *(const u32x4 *)(kb + row_offset(g, kv, b, h, n) + c * 8);
+        if (vw_out) *(u32x4 *)(vw_out + w_at) = *(const u32x4 *)(vb + row_offset(g, vv, b, h, n) + c * 8);
+      }
+    }
+    return;
+  }
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -257,6 +274,7 @@ __global__ void linear_reduce_kernel(int D, int S, const float *__restrict__ par
 // Finalize, d = 128 (fused layer): sum the split-N partial states of 8 rows
 // of H (and, in block 0, of Z) in a fixed order, keep them in LDS and fold
 // the projection and the gate in: Hp[j][i] = bf16(s_b * (H W_p)[i][j]).
+// Samples dropped by the branch threshold (s_b < drop_tau) are skipped.
 // Grid (16, B*H); block blk owns rows 8*blk..+7.  W_p is staged once per
 // block as bf16 (16-byte loads); thread t computes row t/32 at columns
 // (t%32) + 32m, m < 4.  H and Z are also written out in fp32.
@@ -273,6 +291,7 @@ __global__ void __launch_bounds__(256) linear_finalize_kernel(Geom g, int S,
   __shared__ __attribute__((aligned(16))) T Ws[D * D];
   __shared__ float Hs[8 * D];
   const int blk = blockIdx.x, bh = blockIdx.y, b = bh / g.H, t = threadIdx.x;
+  if (s_gate[b] < g.drop_tau) return;  // dropped sample: no linear branch (its state was skipped)
   // stage W_p (16-byte chunks)
   constexpr int VEC = 16 / sizeof(T);
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -333,14 +352,15 @@ hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial,
 // Partial states only (the fused layer finalizes them itself), optionally
 // writing working-layout copies of K and V.
 hipError_t launch_linear_partials(const Geom &g, View kv, View vv, float *partial, bf16_t *kw_out,
-                                  bf16_t *vw_out, const uint64_t copy_heads[4], hipStream_t st) {
+                                  bf16_t *vw_out, const uint64_t copy_heads[4], const float *s_gate,
+                                  hipStream_t st) {
   const int S = linear_splits(g);
   int chunk = (g.N + S - 1) / S;
   chunk = (chunk + 127) / 128 * 128;
   HeadMask m;
   for (int i = 0; i < 4; ++i) m.w[i] = copy_heads[i];
   linear_state_bf16_kernel<<<dim3(S, g.B * g.H), 256, 0, st>>>(g, kv, vv, partial, S, chunk, kw_out,
-                                                              vw_out, m);
+                                                              vw_out, m, s_gate);
   return hipGetLastError();
 }
 
@@ -352,7 +372,7 @@ hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float 
   dim3 grid(S, g.B * g.H);
   if (bf16) {
     linear_state_bf16_kernel<<<grid, 256, 0, st>>>(g, kv, vv, partial, S, chunk, nullptr, nullptr,
-                                                   HeadMask{});
+                                                   HeadMask{}, nullptr);
   } else if (g.D == 128) {
     linear_state_f32_kernel<128><<<grid, 256, 0, st>>>(g, kv, vv, partial, S, chunk);
   } else {

@@ -97,3 +97,41 @@ def test_forward_is_deterministic():
     a, sa, ia = run_forward(w, inp)
     b, sb, ib = run_forward(w, inp)
     assert torch.equal(a, b) and np.array_equal(sa, sb) and np.array_equal(ia, ib)
+
+
+# ---- post-tuning branch dropping ([G] 2 C) ---------------------------------
+
+DROP_CASES = [
+    C.small("drop-bf16", (4, 6, 10), 4, 128, "bf16", [0, 1, 2, 2], 25, 64, 2, batch=2,
+            x_sample_shift=True),
+    C.small("drop-f32", (3, 4, 8), 3, 64, "f32", [0, 1, 2], 9, 16, 2, batch=2,
+            x_sample_shift=True, qk_channel_scale=False),
+]
+
+
+@pytest.mark.parametrize("w", DROP_CASES, ids=[w.name for w in DROP_CASES])
+def test_branch_dropping(w):
+    """A sample whose gate value is below the threshold keeps only the
+    sparse branch; the other sample is untouched.  Against the oracle, and
+    bitwise against the same layer with the dropped sample's gate forced
+    to 0 (no linear term) and the kept sample's gate left alone."""
+    inp = I.make_inputs(w)
+    full, s, _ = run_forward(w, inp)
+    assert s[0] != s[1]
+    lo, hi = (0, 1) if s[0] < s[1] else (1, 0)
+    tau = float(0.5 * (s[0] + s[1]))
+    out, s_d, _ = run_forward(w, inp, branch_drop_tau=tau)
+    np.testing.assert_array_equal(s_d, s)                      # s_out reports the gate value
+    assert torch.equal(out[hi], full[hi]), "kept sample changed"
+    forced = [float(v) for v in s]
+    forced[lo] = 0.0
+    ref0, _, _ = run_forward(w, inp, s_override=forced)
+    assert torch.equal(out[lo], ref0[lo]), "dropped sample is not the sparse branch alone"
+    ref = O.attn_forward(*(I.as_f64(inp[n]) for n in ("q", "k", "v", "x", "w_p", "gate_w")),
+                         inp["gate_b"], drop_tau=tau, **oracle_kwargs(w))
+    mx, mn = assert_close(host64(out), ref["out"], w.io_dtype, f"{w.name}: dropped layer")
+    print(f"{w.name}: tau {tau:.4f} (s = {s}), out max {mx:.3g} mean {mn:.3g}")
+    # every sample dropped
+    out_all, _, _ = run_forward(w, inp, branch_drop_tau=1.0)
+    ref_all, _, _ = run_forward(w, inp, s_override=[0.0, 0.0])
+    assert torch.equal(out_all, ref_all)
