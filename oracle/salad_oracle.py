@@ -40,7 +40,7 @@ __all__ = [
     "rope_3d", "round_to_bf16", "round_to_io",
     "to_working", "block_means", "block_scores", "topk_blocks", "topk_gap",
     "swa_keys", "topk_keys", "sparse_attention", "sparse_attention_head",
-    "linear_state", "linear_apply", "gate", "combine",
+    "linear_state", "linear_apply", "gate", "combine", "combine_full", "output_projection",
     "swa_pair_count", "topk_pair_count", "branch_kept", "attn_forward",
 ]
 
@@ -329,6 +329,21 @@ def combine(o_s: np.ndarray, o_l: np.ndarray, w_p: np.ndarray, s: float) -> np.n
     return np.asarray(o_s, np.float64) + s * (np.asarray(o_l, np.float64) @ np.asarray(w_p, np.float64))
 
 
+def combine_full(o_s: np.ndarray, o_l: np.ndarray, w_p: np.ndarray, s: float) -> np.ndarray:
+    """Full-width reading of the static projection ([S] step 4; the extra
+    parameter count of about 5 % that [S] reports fits one [C, C] matrix per
+    layer): the linear outputs of all heads of a token, concatenated in head
+    order (C = H*d), pass through one projection.  o_s, o_l: [N, C] token
+    rows; w_p [C, C]; O = O_s + s * (O_l W_p)."""
+    return np.asarray(o_s, np.float64) + s * (np.asarray(o_l, np.float64) @ np.asarray(w_p, np.float64))
+
+
+def output_projection(o: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """[S] step 7: the combined output's token rows (length C) times W^O
+    [C, C] (row vector times matrix, no bias)."""
+    return np.asarray(o, np.float64) @ np.asarray(w_o, np.float64)
+
+
 # --------------------------------------------------------------------------
 # Whole layer
 # --------------------------------------------------------------------------
@@ -344,7 +359,8 @@ def branch_kept(s: float, tau: float) -> bool:
 def attn_forward(q, k, v, x, w_p, gate_w, gate_b, *, grid, head_kinds,
                  window_radius, block, topk, io_dtype="bf16", rope=False,
                  rope_dims=(44, 42, 42), rope_base=10000.0, softmax_scale=None,
-                 linear_eps=1e-6, s_override=None, rows=None, drop_tau=0.0):
+                 linear_eps=1e-6, s_override=None, rows=None, drop_tau=0.0,
+                 proj="head", w_o=None):
     """Hybrid attention layer output for Q, K, V [B, N, H, d] and X [B, N, C].
 
     Steps ([S] steps 2-6): optional 3D RoPE on Q and K (materialised in the
@@ -352,7 +368,10 @@ def attn_forward(q, k, v, x, w_p, gate_w, gate_b, *, grid, head_kinds,
     branch per head (window or Top-K); linear branch on the same Q, K, V;
     gate per sample; O = O_s + s * (O_l W_p) written back in token order.
     With ``drop_tau`` a sample whose gate value is below it keeps only the
-    sparse branch, O = O_s ([G] 2 C; see ``branch_kept``).
+    sparse branch, O = O_s ([G] 2 C; see ``branch_kept``).  ``proj="full"``
+    takes W_p as one [C, C] projection of each token's concatenated linear
+    outputs (``combine_full``); ``w_o`` (optional, [C, C]) applies the output
+    projection of [S] step 7 to each token's combined row.
 
     Everything but the gate is per (sample, head), so each head's inputs
     are prepared only when that head is needed.  ``rows`` (optional, a list
@@ -398,18 +417,38 @@ def attn_forward(q, k, v, x, w_p, gate_w, gate_b, *, grid, head_kinds,
                 c["idx"] = topk_blocks(block_means(c["qw"], block), block_means(c["kw"], block), topk)
         return cache[key]
 
+    def row_parts(b, n, h):
+        """O_s and O_l of one (sample, token, head), token order."""
+        c = head(b, h)
+        o_s, _ = sparse_attention_head(int(head_kinds[h]), c["qw"], c["kw"], c["vw"],
+                                       r=window_radius, bs=block, k=topk, scale=scale,
+                                       rows=[int(inv[h][n])], idx=c["idx"])
+        return o_s[0], linear_apply(c["q"][n:n + 1], c["H"], c["Z"], linear_eps)[0]
+
     if rows is not None:
         result = {}
+        token_rows = {}
         for (b, n, h) in rows:
-            c = head(b, h)
-            o_s, _ = sparse_attention_head(int(head_kinds[h]), c["qw"], c["kw"], c["vw"],
-                                           r=window_radius, bs=block, k=topk, scale=scale,
-                                           rows=[int(inv[h][n])], idx=c["idx"])
-            if branch_kept(s[b], drop_tau):
-                o_l = linear_apply(c["q"][n:n + 1], c["H"], c["Z"], linear_eps)
-                result[(b, n, h)] = combine(o_s, o_l, w_p, s[b])[0]
-            else:
-                result[(b, n, h)] = o_s[0]
+            if proj == "head" and w_o is None:
+                o_s, o_l = row_parts(b, n, h)
+                result[(b, n, h)] = combine(o_s[None], o_l[None], w_p, s[b])[0] \
+                    if branch_kept(s[b], drop_tau) else o_s
+                continue
+            # cross-head projections need the token's whole row
+            if (b, n) not in token_rows:
+                parts = [row_parts(b, n, hh) for hh in range(H)]
+                os_row = np.concatenate([p_[0] for p_ in parts])
+                ol_row = np.concatenate([p_[1] for p_ in parts])
+                if not branch_kept(s[b], drop_tau):
+                    row = os_row
+                elif proj == "full":
+                    row = combine_full(os_row[None], ol_row[None], w_p, s[b])[0]
+                else:
+                    row = np.concatenate([combine(parts[hh][0][None], parts[hh][1][None], w_p,
+                                                  s[b])[0] for hh in range(H)])
+                token_rows[(b, n)] = output_projection(row[None], w_o)[0] if w_o is not None else row
+            dv = v.shape[3]
+            result[(b, n, h)] = token_rows[(b, n)][h * dv:(h + 1) * dv]
         return result
 
     out = np.empty((B, N, H, v.shape[3]))
@@ -432,9 +471,17 @@ def attn_forward(q, k, v, x, w_p, gate_w, gate_b, *, grid, head_kinds,
             o_l = linear_apply(c["q"], c["H"], c["Z"], linear_eps)
             o_s_all[b, :, h] = o_s
             o_l_all[b, :, h] = o_l
-            out[b, :, h] = combine(o_s, o_l, w_p, s[b]) if branch_kept(s[b], drop_tau) else o_s
+            if proj == "head":
+                out[b, :, h] = combine(o_s, o_l, w_p, s[b]) if branch_kept(s[b], drop_tau) else o_s
             Hs[b, h], Zs[b, h] = c["H"], c["Z"]
             q_used[b, :, h], k_used[b, :, h] = c["q"], c["k"]
             del cache[(b, h)]
+        dv = v.shape[3]
+        if proj == "full":
+            os_tok = o_s_all[b].reshape(N, H * dv)
+            out[b] = (combine_full(os_tok, o_l_all[b].reshape(N, H * dv), w_p, s[b])
+                      if branch_kept(s[b], drop_tau) else os_tok).reshape(N, H, dv)
+        if w_o is not None:
+            out[b] = output_projection(out[b].reshape(N, H * dv), w_o).reshape(N, H, dv)
     return {"out": out, "o_s": o_s_all, "o_l": o_l_all, "H": Hs, "Z": Zs, "s": s,
             "idx": idx_all, "orders": orders, "q_used": q_used, "k_used": k_used}

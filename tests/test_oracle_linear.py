@@ -167,6 +167,44 @@ def test_layer_branch_dropping():
         np.testing.assert_allclose(part[key], mixed["out"][key], atol=1e-14)
 
 
+def test_layer_full_width_projection_and_output_projection():
+    """[C, C] reading of the static projection and the W^O step: a
+    block-diagonal W_p with equal blocks is the per-head reading; one
+    off-diagonal block moves head 0's linear output into head 1's columns
+    (head-major concatenation); W_p = 0 leaves O_s; W^O = I changes nothing
+    and a permutation W^O permutes the output columns."""
+    grid, H, d = (2, 3, 4), 3, 4
+    C = H * d
+    q, k, v, x, wp, gw = _layer_inputs(1, grid, H, d, 24)
+    kw = dict(grid=grid, head_kinds=[0, 1, 2], window_radius=3, block=8, topk=2, io_dtype="f32")
+    head = O.attn_forward(q, k, v, x, wp, gw, 0.1, **kw)
+    full = O.attn_forward(q, k, v, x, np.kron(np.eye(H), wp), gw, 0.1, proj="full", **kw)
+    np.testing.assert_allclose(full["out"], head["out"], atol=1e-13)
+    s = head["s"][0]
+    off = np.zeros((C, C))
+    off[0:d, d:2 * d] = wp                        # head 0's O_l -> head 1's columns
+    cross = O.attn_forward(q, k, v, x, off, gw, 0.1, proj="full", **kw)
+    np.testing.assert_allclose(cross["out"][0, :, 1],
+                               head["o_s"][0, :, 1] + s * (head["o_l"][0, :, 0] @ wp), atol=1e-13)
+    np.testing.assert_array_equal(cross["out"][0, :, 0], head["o_s"][0, :, 0])
+    zero = O.attn_forward(q, k, v, x, np.zeros((C, C)), gw, 0.1, proj="full", **kw)
+    np.testing.assert_array_equal(zero["out"], zero["o_s"])
+    ident = O.attn_forward(q, k, v, x, wp, gw, 0.1, w_o=np.eye(C), **kw)
+    np.testing.assert_array_equal(ident["out"], head["out"])
+    perm = np.random.default_rng(5).permutation(C)
+    P = np.eye(C)[:, perm]                        # column c of the result = column perm[c]
+    moved = O.attn_forward(q, k, v, x, wp, gw, 0.1, w_o=P, **kw)
+    np.testing.assert_array_equal(moved["out"][0].reshape(-1, C), head["out"][0].reshape(-1, C)[:, perm])
+    # rows form with both cross-head steps
+    w_o = np.random.default_rng(6).standard_normal((C, C)) * 0.2
+    both = O.attn_forward(q, k, v, x, off + np.kron(np.eye(H), wp), gw, 0.1, proj="full", w_o=w_o, **kw)
+    rows = [(0, 0, 0), (0, 13, 2), (0, 23, 1)]
+    part = O.attn_forward(q, k, v, x, off + np.kron(np.eye(H), wp), gw, 0.1, proj="full", w_o=w_o,
+                          rows=rows, **kw)
+    for key in rows:
+        np.testing.assert_allclose(part[key], both["out"][key], atol=1e-13)
+
+
 def test_layer_temporal_head_is_window_on_regrouped_sequence():
     # a temporal head's output for token n equals a plain window attention on
     # the regrouped sequence, read back at n's working position

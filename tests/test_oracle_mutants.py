@@ -104,6 +104,14 @@ def _drop_at_equality(s, tau):         # drops a gate value equal to the thresho
     return s > tau
 
 
+def _combine_full_transposed(o_s, o_l, w_p, s):   # W_p applied as its transpose
+    return np.asarray(o_s, np.float64) + s * (np.asarray(o_l, np.float64) @ np.asarray(w_p, np.float64).T)
+
+
+def _output_projection_transposed(o, w_o):          # W^O applied as its transpose
+    return np.asarray(o, np.float64) @ np.asarray(w_o, np.float64).T
+
+
 CASES = [
     ("st_permutation", _perm_inverse, lambda: TO.test_st_permutation_matches_sort_construction((4, 8, 8))),
     ("swa_keys", _swa_keys_short, lambda: TA.test_window_matches_masked_dense(64, 5)),
@@ -120,6 +128,9 @@ CASES = [
     ("round_to_bf16", _bf16_truncate, TO.test_round_to_bf16_exact_on_float64_values),
     ("branch_kept", _drop_inverted, TL.test_layer_branch_dropping),
     ("branch_kept", _drop_at_equality, TL.test_layer_branch_dropping),
+    ("combine_full", _combine_full_transposed, TL.test_layer_full_width_projection_and_output_projection),
+    ("output_projection", _output_projection_transposed,
+     TL.test_layer_full_width_projection_and_output_projection),
 ]
 
 
