@@ -62,14 +62,15 @@ def source_sha() -> str:
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def cpu_baseline(w, inp, flops_total: float, target_s: float = 15.0):
+def cpu_baseline(w, inp, flops_total: float, target_s: float = 15.0, proj: str = "head"):
     """Time the fp64 oracle on a bounded sample of the layer and extrapolate.
 
     The oracle computes each head's per-layer work (RoPE, working order,
     linear state, Top-K selection) once per call, on first use, and then
     one output row at a time.  A call with one row per (sample, head) pays
     all of the per-layer work; further calls add random rows on top, and the
-    difference gives the per-row cost."""
+    difference gives the per-row cost.  With the full-width projection a
+    unit is a whole token row (all heads), so rows are drawn per token."""
     import numpy as np
     import threadpoolctl
 
@@ -79,19 +80,20 @@ def cpu_baseline(w, inp, flops_total: float, target_s: float = 15.0):
     args = [I.as_f64(inp[n]) for n in ("q", "k", "v", "x", "w_p", "gate_w")]
     kw = dict(grid=w.grid, head_kinds=w.head_kinds, window_radius=w.window_radius,
               block=w.block, topk=w.topk, io_dtype=w.io_dtype, rope=w.rope,
-              rope_dims=w.rope_dims, rope_base=w.rope_base)
+              rope_dims=w.rope_dims, rope_base=w.rope_base, proj=proj)
+    heads = 1 if proj == "full" else w.n_heads     # output units per token
     threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
         if threadpoolctl.threadpool_info() else 1
     rng = np.random.default_rng(0)
-    base_rows = [(b, int(rng.integers(w.N)), h) for b in range(w.batch) for h in range(w.n_heads)]
+    base_rows = [(b, int(rng.integers(w.N)), h) for b in range(w.batch) for h in range(heads)]
     t0 = time.perf_counter()
     O.attn_forward(*args, inp["gate_b"], rows=base_rows, **kw)
     t_fixed = time.perf_counter() - t0
-    total_rows = w.batch * w.N * w.n_heads
+    total_rows = w.batch * w.N * heads
     n_rows, t_rows = min(64, total_rows), 0.0
     while True:                                                  # grow the sample to ~target_s
         rows = base_rows + [(int(rng.integers(w.batch)), int(rng.integers(w.N)),
-                             int(rng.integers(w.n_heads))) for _ in range(n_rows)]
+                             int(rng.integers(heads))) for _ in range(n_rows)]
         t0 = time.perf_counter()
         O.attn_forward(*args, inp["gate_b"], rows=rows, **kw)
         t_rows = max(time.perf_counter() - t0 - t_fixed, 1e-9)
@@ -103,11 +105,12 @@ def cpu_baseline(w, inp, flops_total: float, target_s: float = 15.0):
     return {
         "value": flops_total / t_layer / 1e12, "unit": "TFLOP/s", "cores": int(threads),
         "kind": "oracle", "ms_per_layer_extrapolated": t_layer * 1e3,
-        "sample": (f"fp64 numpy oracle: one output row per (sample, head), which includes every "
+        "sample": (f"fp64 numpy oracle ({proj} projection): one output row per (sample, head), "
+                   f"which includes every "
                    f"head's per-layer work (gate, RoPE, working order, linear state, Top-K "
                    f"selection), in {t_fixed:.2f} s; then {n_rows} more random rows (sparse "
                    f"attention, linear apply, combine) in {t_rows:.2f} s beyond that; "
-                   f"extrapolated to all {total_rows} rows"),
+                   f"extrapolated to all {total_rows} " + ("token rows" if proj == "full" else "rows")),
     }
 
 
@@ -122,6 +125,10 @@ def main():
     ap.add_argument("--branch-drop-tau", type=float, default=0.0,
                     help="post-tuning branch dropping threshold (samples whose gate value is "
                          "below it keep only the sparse branch); 0 never drops")
+    ap.add_argument("--proj", choices=("head", "full"), default="head",
+                    help="static projection W_p: one [d, d] matrix per head (default) or one "
+                         "[C, C] matrix over each token's concatenated heads (a GEMM after the "
+                         "attention kernel)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size reference for the HBM byte counters)")
@@ -142,8 +149,8 @@ def main():
 
     w = C.all_workloads()[args.workload]
     print(f"[bench] workload {w.name}: {w.description}", file=sys.stderr, flush=True)
-    inp = I.make_inputs(w)
-    p = S.problem_from_workload(w, branch_drop_tau=args.branch_drop_tau)
+    inp = I.make_inputs(w, proj=args.proj)
+    p = S.problem_from_workload(w, branch_drop_tau=args.branch_drop_tau, proj=args.proj)
     dev = {n: inp[n].cuda() for n in ("q", "k", "v", "x", "w_p", "gate_w")}
     out = torch.empty_like(dev["q"])
     s_out = torch.empty(w.batch, dtype=torch.float32, device="cuda")
@@ -199,7 +206,10 @@ def main():
                    "heads": w.n_heads, "head_dim": w.head_dim,
                    "head_kinds": "".join("STK"[k] for k in w.head_kinds),
                    "window_radius": w.window_radius, "block": w.block, "topk": w.topk,
-                   "rope": w.rope, "branch_drop_tau": args.branch_drop_tau,
+                   "rope": w.rope, "proj": args.proj,
+                   "projection_gemm_flop": (2.0 * w.batch * w.N * (w.n_heads * w.head_dim) ** 2
+                                            if args.proj == "full" else None),
+                   "branch_drop_tau": args.branch_drop_tau,
                    "samples_dropped": int((s_out.cpu() < args.branch_drop_tau).sum()),
                    "computed_pairs": pairs,
                    "density": pairs / (w.batch * w.n_heads * w.N * w.N)},
@@ -212,7 +222,7 @@ def main():
         rec["dtype"] = "f32"
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, inp, flops, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(w, inp, flops, args.cpu_seconds, args.proj)
     print(json.dumps(rec), flush=True)
 
 

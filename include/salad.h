@@ -35,8 +35,12 @@
  *  Ownership: every buffer is allocated and freed by the caller.  Device
  *  pointers must be 16-byte aligned and contiguous in the stated layout.
  *  Scratch memory comes only from the caller's workspace (ws, ws_bytes),
- *  sized by salad_workspace_size; the library allocates no device memory
- *  and keeps no pointer after a call returns.
+ *  sized by salad_workspace_size, and the library keeps no pointer after a
+ *  call returns.  The library's own kernels allocate no device memory; the
+ *  two calls that run a GEMM (SALAD_PROJ_FULL forwards and
+ *  salad_output_projection) use one hipBLASLt handle per device, created on
+ *  first use and kept until the process ends, with GEMM algorithms that
+ *  need no workspace (those calls are serialised by a lock around it).
  *
  *  Execution: calls enqueue kernels on `stream` and return without
  *  synchronising.  Results are deterministic (no floating-point atomics).
@@ -72,6 +76,13 @@ typedef enum { SALAD_F32 = 0, SALAD_BF16 = 1 } salad_dtype;
 
 enum { SALAD_HEAD_SPATIAL = 0, SALAD_HEAD_TEMPORAL = 1, SALAD_HEAD_TOPK = 2 };
 
+/* Shape of the static projection W_p of the linear branch ([S] step 4):
+ * one [d, d] matrix shared by the heads (each head's linear output row times
+ * W_p), or one [C, C] matrix over a token's linear outputs concatenated in
+ * head order (the reading that matches the extra parameter count of about
+ * 5 % that [S] reports). */
+enum { SALAD_PROJ_HEAD = 0, SALAD_PROJ_FULL = 1 };
+
 #define SALAD_MAX_HEADS 256
 
 /* The layer's problem statement ([S] method steps 2-6, [I] 1.1-1.2). */
@@ -96,6 +107,7 @@ typedef struct {
                                          below it keeps only the sparse branch
                                          (out = O_s) and its linear-branch work is
                                          skipped; 0 never drops (s_b > 0); finite */
+  int32_t proj_mode;                  /* SALAD_PROJ_HEAD or SALAD_PROJ_FULL        */
 } salad_problem;
 
 /* Bytes of workspace that any entry point below may need for problem *p
@@ -159,16 +171,24 @@ salad_status salad_gate(const salad_problem *p, const void *x, const void *w, fl
  * o_s[b,h,p,:] + s[b] * (o_l[b,h,p,:] W_p), W_p [d_in, d_out] row-major in
  * io_dtype, shared by all heads, no bias.  o_s, o_l float32 working layout;
  * s float32 [B] device; out boundary layout in io_dtype.  A sample with
- * s_b < p->branch_drop_tau gets out = O_s (branch dropping, [G] 2 C). */
+ * s_b < p->branch_drop_tau gets out = O_s (branch dropping, [G] 2 C).
+ * SALAD_PROJ_HEAD only (the full-width projection mixes heads and runs
+ * inside salad_attn_forward); SALAD_ERR_UNSUPPORTED otherwise. */
 salad_status salad_combine(const salad_problem *p, const float *o_s, const float *o_l,
                            const void *w_p, const float *s, void *out, hipStream_t stream);
 
 /* Whole layer ([S] steps 2-6, and step 8 through p->branch_drop_tau): q, k,
- * v [B,N,H,d], x [B,N,C], w_p [d,d], gate_w [C] in io_dtype -> out [B,N,H,d]
- * in io_dtype.  s_override (device float [B]) replaces the gate when
- * non-NULL; s_out (device float [B]) and idx_out ([B,H,nb,topk] int32,
- * Top-K heads only) receive the gate values (before any dropping) and the
- * block selection when non-NULL.  A sample with s_b < branch_drop_tau gets
+ * v [B,N,H,d], x [B,N,C], w_p ([d,d] for SALAD_PROJ_HEAD, [C,C] for
+ * SALAD_PROJ_FULL), gate_w [C] in io_dtype -> out [B,N,H,d] in io_dtype.
+ * With SALAD_PROJ_FULL, out[b,n,:] = O_s[b,n,:] + s_b * (O_l[b,n,:] W_p) over
+ * the token's C-wide rows; the [B*N, C] x [C, C] product runs as one hipBLASLt
+ * GEMM (float32 accumulation) on `stream`, accumulating into out; the
+ * workspace then also holds s_b * O_l in token rows (B*N*C io_dtype
+ * elements, zero for dropped samples).
+ * s_override (device float [B]) replaces the gate when non-NULL; s_out
+ * (device float [B]) and idx_out ([B,H,nb,topk] int32, Top-K heads only)
+ * receive the gate values (before any dropping) and the block selection
+ * when non-NULL.  A sample with s_b < branch_drop_tau gets
  * out = O_s; the decision is taken on the device, so nothing synchronises.
  * Workspace: salad_workspace_size. */
 salad_status salad_attn_forward(const salad_problem *p, const void *q, const void *k,
@@ -176,6 +196,13 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
                                 const void *gate_w, float gate_b, const float *s_override,
                                 void *out, float *s_out, int32_t *idx_out, void *ws,
                                 size_t ws_bytes, hipStream_t stream);
+
+/* Output projection ([S] step 7): out[b,n,:] = in[b,n,:] W_o, a row vector
+ * times W_o [C, C] row-major, no bias; in, out [B, N, C] (equivalently
+ * [B,N,H,d]) and W_o in io_dtype.  One hipBLASLt GEMM, float32 accumulation.
+ * in and out must not overlap.  Errors: NULL, ALIGN, SHAPE, HIP. */
+salad_status salad_output_projection(const salad_problem *p, const void *in, const void *w_o,
+                                     void *out, hipStream_t stream);
 
 /* Measurement hook.  While enabled (on != 0), salad_attn_forward records a
  * pair of HIP events around its sparse-attention kernel launch(es) on the

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libsalad.so")
 
 SALAD_F32, SALAD_BF16 = 0, 1
 HEAD_SPATIAL, HEAD_TEMPORAL, HEAD_TOPK = 0, 1, 2
+PROJ_HEAD, PROJ_FULL = 0, 1
 MAX_HEADS = 256
 
 STATUS = {0: "SALAD_OK", 1: "SALAD_ERR_NULL", 2: "SALAD_ERR_SHAPE", 3: "SALAD_ERR_UNSUPPORTED",
@@ -29,8 +30,8 @@ STATUS = {0: "SALAD_OK", 1: "SALAD_ERR_NULL", 2: "SALAD_ERR_SHAPE", 3: "SALAD_ER
 
 EXPORTS = ("salad_workspace_size", "salad_permute", "salad_block_select", "salad_sparse_attn",
            "salad_linear_state", "salad_linear_apply", "salad_gate", "salad_combine",
-           "salad_attn_forward", "salad_profile_enable", "salad_profile_read",
-           "salad_last_error")
+           "salad_attn_forward", "salad_output_projection", "salad_profile_enable",
+           "salad_profile_read", "salad_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -42,6 +43,7 @@ class Problem(ctypes.Structure):
         ("softmax_scale", ctypes.c_float), ("linear_eps", ctypes.c_float),
         ("rope", ctypes.c_int32), ("rope_dims", ctypes.c_int32 * 3), ("rope_base", ctypes.c_float),
         ("io_dtype", ctypes.c_int32), ("branch_drop_tau", ctypes.c_float),
+        ("proj_mode", ctypes.c_int32),
     ]
 
     @property
@@ -51,6 +53,15 @@ class Problem(ctypes.Structure):
     @property
     def n_blocks(self) -> int:
         return -(-self.N // self.block) if self.block > 0 else 0
+
+    @property
+    def C(self) -> int:
+        return self.n_heads * self.head_dim
+
+    @property
+    def w_p_numel(self) -> int:
+        """Elements of W_p: [d, d] per head, or [C, C] full width."""
+        return self.C ** 2 if self.proj_mode == PROJ_FULL else self.head_dim ** 2
 
     @property
     def kinds(self):
@@ -86,6 +97,7 @@ def lib() -> ctypes.CDLL:
             "salad_gate": [P, vp, vp, f32, vp, vp, sz, vp],
             "salad_combine": [P, vp, vp, vp, vp, vp, vp],
             "salad_attn_forward": [P, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp],
+            "salad_output_projection": [P, vp, vp, vp, vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -108,7 +120,7 @@ def _check(status: int):
 
 def make_problem(*, batch, n_heads, head_dim, grid, head_kinds, window_radius=0, block=64,
                  topk=1, softmax_scale=0.0, linear_eps=1e-6, rope=False, rope_dims=(0, 0, 0),
-                 rope_base=10000.0, io_dtype="bf16", branch_drop_tau=0.0) -> Problem:
+                 rope_base=10000.0, io_dtype="bf16", branch_drop_tau=0.0, proj="head") -> Problem:
     p = Problem()
     p.batch, p.n_heads, p.head_dim = batch, n_heads, head_dim
     p.grid_f, p.grid_h, p.grid_w = grid
@@ -122,14 +134,17 @@ def make_problem(*, batch, n_heads, head_dim, grid, head_kinds, window_radius=0,
     p.rope_base = rope_base
     p.io_dtype = SALAD_BF16 if io_dtype == "bf16" else SALAD_F32
     p.branch_drop_tau = branch_drop_tau
+    if proj not in ("head", "full"):
+        raise ValueError(f"proj must be 'head' or 'full' (got {proj!r})")
+    p.proj_mode = PROJ_FULL if proj == "full" else PROJ_HEAD
     return p
 
 
-def problem_from_workload(w, branch_drop_tau=0.0) -> Problem:
+def problem_from_workload(w, branch_drop_tau=0.0, proj="head") -> Problem:
     return make_problem(batch=w.batch, n_heads=w.n_heads, head_dim=w.head_dim, grid=w.grid,
                         head_kinds=w.head_kinds, window_radius=w.window_radius, block=w.block,
                         topk=w.topk, rope=w.rope, rope_dims=w.rope_dims, rope_base=w.rope_base,
-                        io_dtype=w.io_dtype, branch_drop_tau=branch_drop_tau)
+                        io_dtype=w.io_dtype, branch_drop_tau=branch_drop_tau, proj=proj)
 
 
 # ---- marshalling helpers --------------------------------------------------
@@ -254,11 +269,20 @@ def salad_attn_forward(p: Problem, q, k, v, x, w_p, gate_w, gate_b: float, out, 
     nidx = p.batch * p.n_heads * p.n_blocks * p.topk
     _check(lib().salad_attn_forward(
         ctypes.byref(p), _ptr(q, "q", n, dt), _ptr(k, "k", n, dt), _ptr(v, "v", n, dt),
-        _ptr(x, "x", p.batch * p.N * C, dt), _ptr(w_p, "w_p", p.head_dim ** 2, dt),
+        _ptr(x, "x", p.batch * p.N * C, dt), _ptr(w_p, "w_p", p.w_p_numel, dt),
         _ptr(gate_w, "gate_w", C, dt), float(gate_b),
         _ptr(s_override, "s_override", p.batch, torch.float32), _ptr(out, "out", n, dt),
         _ptr(s_out, "s_out", p.batch, torch.float32), _ptr(idx_out, "idx_out", nidx, torch.int32),
         _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def salad_output_projection(p: Problem, x, w_o, out, stream=None):
+    """out [B, N, C] = x [B, N, C] @ w_o [C, C] (storage type of p)."""
+    n, _ = _sizes(p)
+    dt = _io_dtype(p)
+    _check(lib().salad_output_projection(
+        ctypes.byref(p), _ptr(x, "in", n, dt), _ptr(w_o, "w_o", p.C ** 2, dt), _ptr(out, "out", n, dt),
+        _stream(stream)))
 
 
 def workspace(p: Problem, device="cuda"):

@@ -37,7 +37,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Info {
   Geom g;
-  int bf16, rope;
+  int bf16, rope, full;
   int any_topk, any_window;
   size_t esize;
 };
@@ -99,6 +99,9 @@ salad_status validate(const salad_problem *p, Info *inf) {
   g.eps = p->linear_eps;
   if (!std::isfinite(p->branch_drop_tau))
     return fail(SALAD_ERR_SHAPE, "branch_drop_tau must be finite");
+  if (p->proj_mode != SALAD_PROJ_HEAD && p->proj_mode != SALAD_PROJ_FULL)
+    return fail(SALAD_ERR_SHAPE, "proj_mode must be SALAD_PROJ_HEAD or SALAD_PROJ_FULL (got %d)", p->proj_mode);
+  inf->full = p->proj_mode == SALAD_PROJ_FULL;
   g.drop_tau = p->branch_drop_tau;
   g.rope_base = p->rope_base;
   for (int i = 0; i < 3; ++i) g.rope_dims[i] = p->rope_dims[i];
@@ -126,9 +129,10 @@ salad_status validate(const salad_problem *p, Info *inf) {
 // the first total_stage bytes.  salad_attn_forward adds, after that shared
 // scratch: for bf16 (fused) the RoPE'd working Q/K (only with rope), the
 // block selection, Hp and Z; for f32 (staged) working copies of Q/K/V, the
-// selection, O_s, O_l, H and Z.  Both end with the gate values.
+// selection, O_s, O_l, H and Z.  Both end with the gate values, the RoPE
+// table and, for the full-width projection, s_b * O_l in token rows.
 struct Plan {
-  size_t wq, wk, wv, wkr, idx, o_s, o_l, h, z, s, hp, rope_tab;
+  size_t wq, wk, wv, wkr, idx, o_s, o_l, h, z, s, hp, rope_tab, olt;
   size_t total_stage, total_forward;
 };
 
@@ -167,6 +171,7 @@ Plan plan(const Info &inf) {
   }
   pl.s = off; off += up(size_t(g.B) * sizeof(float));
   pl.rope_tab = off; off += inf.rope ? up(size_t(rope_table_entries(g)) * 16) : 0;
+  pl.olt = off; off += inf.full ? up(rows * g.D * inf.esize) : 0;
   pl.total_forward = off;
   return pl;
 }
@@ -211,6 +216,15 @@ void select_regions(const Geom &g, void *ws, double **qm, double **km, double **
   *qm = (double *)w;
   *km = (double *)(w + one);
   *sc = (double *)(w + 2 * one);
+}
+
+// Full-width projection ([S] step 4, [C, C] reading): out += olt W_p over
+// the B*N token rows, where olt already holds s_b * O_l.
+salad_status project_full(const Info &inf, const void *olt, const void *w_p, void *out, hipStream_t st) {
+  const Geom &g = inf.g;
+  if (const char *m = gemm_rows(inf.bf16, (long long)g.B * g.N, g.H * g.D, olt, w_p, 1.f, out, st))
+    return fail(SALAD_ERR_HIP, "salad_attn_forward: projection GEMM: %s", m);
+  return SALAD_OK;
 }
 
 View working_view(const Geom &g, const void *base) {
@@ -378,6 +392,10 @@ salad_status salad_combine(const salad_problem *p, const float *o_s, const float
   CHECK(need(w_p, "w_p"));
   CHECK(need(s, "s"));
   CHECK(need(out, "out"));
+  if (inf.full)
+    return fail(SALAD_ERR_UNSUPPORTED,
+                "salad_combine applies the per-head projection only; the full-width projection runs in "
+                "salad_attn_forward");
   return hip_status(launch_combine(inf.g, inf.bf16, o_s, o_l, w_p, s, out, stream), "salad_combine");
 }
 
@@ -453,9 +471,11 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
     for (int i = 0; i < 4; ++i) work[i] = direct ? g.temporal[i] : ~0ull;
     const View kw = working_view(g, wk), vw = working_view(g, wv);
     bf16_t *hp = (bf16_t *)(w + pl.hp);
+    // full-width projection: the finalize leaves W_p and s to the GEMM below
     if ((e = launch_linear_partials(g, kb, vb, (float *)scratch, (bf16_t *)wk, (bf16_t *)wv, work, s,
                                     stream)) != hipSuccess ||
-        (e = launch_linear_finalize(g, 1, (const float *)scratch, w_p, s, hm, hp, zv, stream)) != hipSuccess)
+        (e = launch_linear_finalize(g, 1, (const float *)scratch, inf.full ? nullptr : w_p, s, hm, hp, zv,
+                                    stream)) != hipSuccess)
       return hip_status(e, "salad_attn_forward: linear state");
     if (inf.any_topk) {
       // Top-K heads are never temporal: their working rows are the token rows
@@ -464,11 +484,14 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
       e = launch_block_select(g, 1, qv, kb, qm, km, sc, idx, stream);
       if (e != hipSuccess) return hip_status(e, "salad_attn_forward: block select");
     }
+    View outl = boundary_view(g, w + pl.olt);  // s_b * O_l rows (full-width projection only)
+    if (!inf.full) outl.base = nullptr;
     if ((e = prof_mark(0, stream)) != hipSuccess ||
-        (e = launch_attn_fused(g, qv, kw, vw, kd, vd, work, idx, hp, zv, s, boundary_view(g, out),
+        (e = launch_attn_fused(g, qv, kw, vw, kd, vd, work, idx, hp, zv, s, boundary_view(g, out), outl,
                                stream)) != hipSuccess ||
         (e = prof_mark(1, stream)) != hipSuccess)
       return hip_status(e, "salad_attn_forward: attention");
+    if (inf.full) return project_full(inf, w + pl.olt, w_p, out, stream);
     return SALAD_OK;
   }
 
@@ -495,8 +518,30 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
     return hip_status(e, "salad_attn_forward: linear state");
   if ((e = launch_linear_apply(g, inf.bf16, qv, hm, zv, o_l, stream)) != hipSuccess)
     return hip_status(e, "salad_attn_forward: linear apply");
+  if (inf.full) {
+    if ((e = launch_split_full(g, inf.bf16, o_s, o_l, s, out, w + pl.olt, stream)) != hipSuccess)
+      return hip_status(e, "salad_attn_forward: split");
+    return project_full(inf, w + pl.olt, w_p, out, stream);
+  }
   if ((e = launch_combine(g, inf.bf16, o_s, o_l, w_p, s, out, stream)) != hipSuccess)
     return hip_status(e, "salad_attn_forward: combine");
+  return SALAD_OK;
+}
+
+salad_status salad_output_projection(const salad_problem *p, const void *in, const void *w_o, void *out,
+                                     hipStream_t stream) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  CHECK(need(in, "in"));
+  CHECK(need(w_o, "w_o"));
+  CHECK(need(out, "out"));
+  const Geom &g = inf.g;
+  const long long rows = (long long)g.B * g.N;
+  const size_t bytes = size_t(rows) * g.H * g.D * inf.esize;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(in), b0 = reinterpret_cast<uintptr_t>(out);
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(SALAD_ERR_SHAPE, "in and out must not overlap");
+  if (const char *m = gemm_rows(inf.bf16, rows, g.H * g.D, in, w_o, 0.f, out, stream))
+    return fail(SALAD_ERR_HIP, "salad_output_projection: %s", m);
   return SALAD_OK;
 }
 

@@ -128,10 +128,11 @@ struct AttnArgs {
   uint64_t work[4];
   const int32_t *idx;
   float *o_s;            // staged: working layout fp32 output
-  const bf16_t *hp;      // fused: [B*H][128][128] bf16, s_b * (H W_p)^T
+  const bf16_t *hp;      // fused: [B*H][128][128] bf16, s_b * (H W_p)^T (H^T with out_l)
   const float *z;        // fused: [B*H][128] linear normaliser state
   const float *s_gate;   // fused: [B] gate values (branch dropping below g.drop_tau)
   View out;              // fused: output rows (boundary layout, scattered)
+  View out_l;            // fused, full-width projection: s_b * O_l rows (base NULL otherwise)
   int n_heads_sel;       // heads handled by this launch
   uint8_t heads[kMaxHeads];
   int tiles_per_head;    // query tiles per (b, head)
@@ -521,6 +522,13 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
           for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * r4 + e] * inv);
           *(bf16x4 *)(orow + 32 * db + 8 * r4 + 4 * hl) = v;
         }
+      if (a.out_l.base) {  // the projection GEMM then adds nothing to this row
+        bf16_t *lrow = (bf16_t *)a.out_l.base + row_offset(g, a.out_l, b, h, pq);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) *(bf16x4 *)(lrow + 32 * db + 8 * r4 + 4 * hl) = bf16x4{};
+      }
       return;
     }
     // Linear branch, projection, gate and combine for this wave's queries:
@@ -570,6 +578,26 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
       }
     if (pq >= g.N) return;
     bf16_t *orow = (bf16_t *)a.out.base + row_offset(g, a.out, b, h, pq);
+    if (a.out_l.base) {
+      // full-width projection: O_s here, s_b * O_l to its own rows; a GEMM
+      // over whole token rows adds (s_b O_l) W_p afterwards
+      bf16_t *lrow = (bf16_t *)a.out_l.base + row_offset(g, a.out_l, b, h, pq);
+      const float sl = a.s_gate[b] * inv_den;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x4 v, u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = (__bf16)(o[db][4 * r4 + e] * inv);
+            u[e] = (__bf16)(lin[db][4 * r4 + e] * sl);
+          }
+          *(bf16x4 *)(orow + 32 * db + 8 * r4 + 4 * hl) = v;
+          *(bf16x4 *)(lrow + 32 * db + 8 * r4 + 4 * hl) = u;
+        }
+      return;
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -657,7 +685,8 @@ hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv
 
 hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, View vd,
                              const uint64_t work[4], const int32_t *idx, const bf16_t *hp,
-                             const float *z, const float *s_gate, View outv, hipStream_t st) {
+                             const float *z, const float *s_gate, View outv, View outl,
+                             hipStream_t st) {
   bool any_work = false, any_direct = false;
   for (int h = 0; h < g.H; ++h) {
     const bool w = (work[h >> 6] >> (h & 63)) & 1ull;
@@ -679,6 +708,7 @@ hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, 
   a.z = z;
   a.s_gate = s_gate;
   a.out = outv;
+  a.out_l = outl;
   return launch_bf16<true>(a, st);
 }
 

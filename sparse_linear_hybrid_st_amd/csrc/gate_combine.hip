@@ -167,4 +167,41 @@ hipError_t launch_combine(const Geom &g, int bf16, const float *o_s, const float
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Staged full-width projection, first half: O_s and s_b * O_l back to token
+// rows (the GEMM over whole token rows follows).  Grid (ceil(N*D/1024), B*H),
+// thread t moves elements 4t..4t+3 of its workgroup's 1024-element slice of
+// the head's N x D working rows.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) split_full_kernel(Geom g, const float *__restrict__ o_s,
+                                                         const float *__restrict__ o_l,
+                                                         const float *__restrict__ s,
+                                                         T *__restrict__ out, T *__restrict__ olt) {
+  const int bh = blockIdx.y, h = bh % g.H, b = bh / g.H;
+  const long long e = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= (long long)g.N * g.D) return;
+  const int p = int(e / g.D), c = int(e % g.D);
+  const float sb = s[b];
+  const float sl = sb < g.drop_tau ? 0.f : sb;  // branch dropping ([G] 2 C)
+  const int tok = bit(g.temporal, h) ? st_token(g, p) : p;
+  const long long src = (long long)bh * g.N * g.D + e;
+  const long long dst = ((long long)b * g.N + tok) * g.H * g.D + (long long)h * g.D + c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    io<T>::st(out + dst + i, o_s[src + i]);
+    io<T>::st(olt + dst + i, sl * o_l[src + i]);
+  }
+}
+
+hipError_t launch_split_full(const Geom &g, int bf16, const float *o_s, const float *o_l,
+                             const float *s, void *out, void *olt, hipStream_t st) {
+  dim3 grid(unsigned(((long long)g.N * g.D + 1023) / 1024), g.B * g.H);
+  if (bf16)
+    split_full_kernel<bf16_t><<<grid, 256, 0, st>>>(g, o_s, o_l, s, (bf16_t *)out, (bf16_t *)olt);
+  else
+    split_full_kernel<float><<<grid, 256, 0, st>>>(g, o_s, o_l, s, (float *)out, (float *)olt);
+  return hipGetLastError();
+}
+
 }  // namespace salad

@@ -57,7 +57,8 @@ hipError_t launch_linear_partials(const Geom &g, View kv, View vv, float *partia
                                   bf16_t *vw_out, const uint64_t copy_heads[4], const float *s_gate,
                                   hipStream_t st);
 // h: [B*H][128][128] fp32 state (workspace); hp: [B*H][128][128] bf16 =
-// s_b * (H W_p)^T; z: [B*H][128] fp32.
+// s_b * (H W_p)^T, or H^T when w_p is NULL (full-width projection);
+// z: [B*H][128] fp32.
 hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial, const void *w_p,
                                   const float *s, float *h, bf16_t *hp, float *z, hipStream_t st);
 // Sparse attention with the linear branch, projection, gate and inverse
@@ -65,9 +66,12 @@ hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial,
 // Heads flagged in `work` read K, V through kw, vw (working copies), the
 // others through kd, vd (rows in working order where they already are).
 // s_gate: samples with s_b < g.drop_tau skip the linear term (out = O_s).
+// outl.base non-NULL (full-width projection, hp = H^T): out receives O_s
+// and outl receives s_b * O_l (zero rows for dropped samples).
 hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, View vd,
                              const uint64_t work[4], const int32_t *idx, const bf16_t *hp,
-                             const float *z, const float *s_gate, View outv, hipStream_t st);
+                             const float *z, const float *s_gate, View outv, View outl,
+                             hipStream_t st);
 // Whether the attention kernel can stream K, V rows through these views.
 bool kv_direct_ok(const Geom &g, View kd, View vd);
 hipError_t launch_linear_apply(const Geom &g, int bf16, View qv, const float *h, const float *z,
@@ -79,5 +83,14 @@ hipError_t launch_combine(const Geom &g, int bf16, const float *o_s, const float
                           const void *w_p, const float *s, void *out, hipStream_t st);
 hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv,
                               const int32_t *idx, float *o_s, hipStream_t st);
+// Staged full-width projection: out[b, pi_h(p), h, :] = o_s[b,h,p,:] and
+// olt (same layout) = s_b * o_l[b,h,p,:] (zero for dropped samples).
+hipError_t launch_split_full(const Geom &g, int bf16, const float *o_s, const float *o_l,
+                             const float *s, void *out, void *olt, hipStream_t st);
+// Row-major out[rows, C] = a[rows, C] W[C, C] + beta * out (hipBLASLt,
+// float32 accumulation, storage type bf16 or f32).  a must not overlap out.
+// Returns NULL on success, else a message.
+const char *gemm_rows(int bf16, long long rows, int C, const void *a, const void *w, float beta,
+                      void *out, hipStream_t st);
 
 }  // namespace salad

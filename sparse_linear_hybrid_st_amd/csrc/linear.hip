@@ -278,8 +278,10 @@ __global__ void linear_reduce_kernel(int D, int S, const float *__restrict__ par
 // Grid (16, B*H); block blk owns rows 8*blk..+7.  W_p is staged once per
 // block as bf16 (16-byte loads); thread t computes row t/32 at columns
 // (t%32) + 32m, m < 4.  H and Z are also written out in fp32.
+// FULL (full-width [C, C] projection, applied after the attention kernel
+// by a GEMM over whole token rows): Hp = bf16(H^T), no W_p and no gate.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool FULL>
 __global__ void __launch_bounds__(256) linear_finalize_kernel(Geom g, int S,
                                                               const float *__restrict__ partial,
                                                               const T *__restrict__ w_p,
@@ -288,15 +290,16 @@ __global__ void __launch_bounds__(256) linear_finalize_kernel(Geom g, int S,
                                                               float *__restrict__ zv,
                                                               bf16_t *__restrict__ hp) {
   constexpr int D = 128, per = D * D + D;
-  __shared__ __attribute__((aligned(16))) T Ws[D * D];
+  __shared__ __attribute__((aligned(16))) T Ws[FULL ? 8 : D * D];
   __shared__ float Hs[8 * D];
   const int blk = blockIdx.x, bh = blockIdx.y, b = bh / g.H, t = threadIdx.x;
   if (s_gate[b] < g.drop_tau) return;  // dropped sample: no linear branch (its state was skipped)
   // stage W_p (16-byte chunks)
   constexpr int VEC = 16 / sizeof(T);
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-  for (int e = t * VEC; e < D * D; e += 256 * VEC)
-    *(u32x4 *)(Ws + e) = *(const u32x4 *)(w_p + e);
+  if constexpr (!FULL)
+    for (int e = t * VEC; e < D * D; e += 256 * VEC)
+      *(u32x4 *)(Ws + e) = *(const u32x4 *)(w_p + e);
   // reduce this block's 8 rows (elements t, t + 256, .. of the 1024), fixed order
   const float *p = partial + (long long)bh * S * per + 8 * blk * D;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -322,13 +325,18 @@ __global__ void __launch_bounds__(256) linear_finalize_kernel(Geom g, int S,
   __syncthreads();
   const int ii = t >> 5, jg = t & 31;
   float o[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int k = 0; k < D; ++k) {
-    const float hv = Hs[ii * D + k];
+  if constexpr (FULL) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) o[m] = fmaf(hv, io<T>::ld(Ws + k * D + jg + 32 * m), o[m]);
+    for (int m = 0; m < 4; ++m) o[m] = Hs[ii * D + jg + 32 * m];
+  } else {
+#pragma unroll 8
+    for (int k = 0; k < D; ++k) {
+      const float hv = Hs[ii * D + k];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) o[m] = fmaf(hv, io<T>::ld(Ws + k * D + jg + 32 * m), o[m]);
+    }
   }
-  const float sb = s_gate[b];
+  const float sb = FULL ? 1.f : s_gate[b];
   bf16_t *dst = hp + (long long)bh * D * D;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -342,10 +350,12 @@ hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial,
   if (g.D != 128) return hipErrorInvalidValue;
   const int S = linear_splits(g);
   dim3 grid(16, g.B * g.H);
-  if (bf16)
-    linear_finalize_kernel<bf16_t><<<grid, 256, 0, st>>>(g, S, partial, (const bf16_t *)w_p, s, h, z, hp);
+  if (!w_p)  // full-width projection: the GEMM after the attention kernel applies W_p and s
+    linear_finalize_kernel<bf16_t, true><<<grid, 256, 0, st>>>(g, S, partial, nullptr, s, h, z, hp);
+  else if (bf16)
+    linear_finalize_kernel<bf16_t, false><<<grid, 256, 0, st>>>(g, S, partial, (const bf16_t *)w_p, s, h, z, hp);
   else
-    linear_finalize_kernel<float><<<grid, 256, 0, st>>>(g, S, partial, (const float *)w_p, s, h, z, hp);
+    linear_finalize_kernel<float, false><<<grid, 256, 0, st>>>(g, S, partial, (const float *)w_p, s, h, z, hp);
   return hipGetLastError();
 }
 

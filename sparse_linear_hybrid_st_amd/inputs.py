@@ -14,6 +14,8 @@ Recipe (N(mu, sigma) is mean and standard deviation):
   V = N(0,1) [B,N,H,d] (t=2)
   X = N(0,1) [B,N,C] (t=3) plus, if enabled, a per-sample N(0,0.5) shift (t=8)
   W_p = N(0,0.02) [d,d] (t=4), gate w = N(0,0.02) [C] (t=5), gate b = 0
+  full-width W_p = N(0,0.02) [C,C] (t=9); output projection
+  W^O = N(0, 1/sqrt(C)) [C,C] (t=10)
 """
 
 from __future__ import annotations
@@ -21,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-T_Q, T_K, T_V, T_X, T_WP, T_W, T_CQ, T_CK, T_SHIFT = range(9)
+T_Q, T_K, T_V, T_X, T_WP, T_W, T_CQ, T_CK, T_SHIFT, T_WPF, T_WO = range(11)
 
 
 def _rng(seed: int, t: int) -> np.random.Generator:
@@ -41,9 +43,10 @@ def to_storage(a: np.ndarray, io_dtype: str) -> torch.Tensor:
     return t.to(torch.bfloat16) if io_dtype == "bf16" else t
 
 
-def make_inputs(w, wp_std: float = 0.02, wp_zero: bool = False) -> dict:
-    """CPU storage-type tensors q, k, v [B,N,H,d], x [B,N,C], w_p [d,d],
-    gate_w [C] and the float gate_b, for workload ``w``."""
+def make_inputs(w, wp_std: float = 0.02, wp_zero: bool = False, proj: str = "head") -> dict:
+    """CPU storage-type tensors q, k, v [B,N,H,d], x [B,N,C], w_p ([d,d], or
+    [C,C] with proj="full"), gate_w [C] and the float gate_b, for workload
+    ``w``."""
     B, N, H, d = w.batch, w.N, w.n_heads, w.head_dim
     C = H * d
     s = w.seed
@@ -61,11 +64,18 @@ def make_inputs(w, wp_std: float = 0.02, wp_zero: bool = False) -> dict:
         x += _normal(s, T_SHIFT, (B,), 0.5)[:, None, None]
     out["x"] = to_storage(x, w.io_dtype)
     del x
-    wp = np.zeros((d, d), np.float32) if wp_zero else _normal(s, T_WP, (d, d), wp_std)
+    shape, t_wp = ((C, C), T_WPF) if proj == "full" else ((d, d), T_WP)
+    wp = np.zeros(shape, np.float32) if wp_zero else _normal(s, t_wp, shape, wp_std)
     out["w_p"] = to_storage(wp, w.io_dtype)
     out["gate_w"] = to_storage(_normal(s, T_W, (C,), 0.02), w.io_dtype)
     out["gate_b"] = 0.0
     return out
+
+
+def make_w_o(w) -> torch.Tensor:
+    """Output projection W^O [C, C] in the storage type of workload ``w``."""
+    C = w.n_heads * w.head_dim
+    return to_storage(_normal(w.seed, T_WO, (C, C), 1.0 / np.sqrt(C)), w.io_dtype)
 
 
 def as_f64(t: torch.Tensor) -> np.ndarray:

@@ -75,9 +75,9 @@ def check_selection(gpu_idx, qbar, kbar, k, what=""):
     return differ
 
 
-def run_forward(w, inp, s_override=None, stream=None, branch_drop_tau=0.0):
+def run_forward(w, inp, s_override=None, stream=None, branch_drop_tau=0.0, proj="head"):
     """salad_attn_forward on the device; returns (out, s, idx) on the host."""
-    p = S.problem_from_workload(w, branch_drop_tau=branch_drop_tau)
+    p = S.problem_from_workload(w, branch_drop_tau=branch_drop_tau, proj=proj)
     q, k, v, x = (dev(inp[n]) for n in ("q", "k", "v", "x"))
     wp, gw = dev(inp["w_p"]), dev(inp["gate_w"])
     out = torch.empty_like(q)

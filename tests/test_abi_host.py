@@ -103,3 +103,31 @@ def test_null_and_misaligned_pointers_fail_before_launch():
                                 a, 16, None) == 5
     assert b"workspace" in L.salad_last_error()
     assert L.salad_workspace_size(None, None) == 1
+
+
+def test_projection_mode_checks():
+    """proj_mode must be one of the two readings; the full-width mode grows
+    the workspace by the s_b * O_l token rows; salad_combine (per-head only)
+    and salad_output_projection reject bad arguments before any launch."""
+    L = S.lib()
+    w = configs.swa_480p()
+    p = S.problem_from_workload(w)
+    st, head_ws = _status(p)
+    assert st == 0
+    p.proj_mode = 2
+    assert _status(p)[0] == 2 and b"proj_mode" in L.salad_last_error()
+    p = S.problem_from_workload(w, proj="full")
+    st, full_ws = _status(p)
+    assert st == 0
+    rows = w.batch * w.N * w.n_heads * w.head_dim
+    assert full_ws - head_ws >= rows * 2
+    assert p.w_p_numel == (w.n_heads * w.head_dim) ** 2
+    a = ctypes.c_void_p(0x10000)
+    assert L.salad_combine(ctypes.byref(p), a, a, a, a, a, None) == 3
+    assert b"full-width" in L.salad_last_error()
+    assert L.salad_output_projection(ctypes.byref(p), None, a, a, None) == 1
+    assert L.salad_output_projection(ctypes.byref(p), a, ctypes.c_void_p(0x10008), a, None) == 4
+    assert L.salad_output_projection(ctypes.byref(p), a, a, a, None) == 2     # in == out
+    assert b"overlap" in L.salad_last_error()
+    with pytest.raises(ValueError):
+        S.problem_from_workload(w, proj="rows")
