@@ -100,11 +100,15 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
 
 def round_to_io(x: np.ndarray, io_dtype: str) -> np.ndarray:
     """Round a materialised tensor to the layer's storage type ("bf16" or
-    "f32"); the result stays float64."""
+    "f32"); the result stays float64.  "f64" keeps every value (no storage
+    rounding anywhere: the layer as a smooth function, for derivative
+    checks)."""
     if io_dtype == "bf16":
         return round_to_bf16(x)
     if io_dtype == "f32":
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if io_dtype == "f64":
+        return np.array(x, dtype=np.float64)
     raise ValueError(io_dtype)
 
 

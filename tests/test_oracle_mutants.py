@@ -9,16 +9,19 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.salad_backward as sb
 import oracle.salad_oracle as so
 from tests import test_oracle_attention as TA
+from tests import test_oracle_backward as TB
 from tests import test_oracle_linear as TL
 from tests import test_oracle_order as TO
 from tests import test_oracle_rope as TR
 
 
 def _patch(monkeypatch, name, fn):
-    monkeypatch.setattr(so, name, fn)
-    monkeypatch.setattr(oracle, name, fn)
+    for mod in (so, sb, oracle):
+        if hasattr(mod, name):
+            monkeypatch.setattr(mod, name, fn)
 
 
 def _perm_inverse(F, Hg, Wg):          # frame-major read as site-major (the inverse map)
@@ -112,6 +115,40 @@ def _output_projection_transposed(o, w_o):          # W^O applied as its transpo
     return np.asarray(o, np.float64) @ np.asarray(w_o, np.float64).T
 
 
+def _sparse_bwd_uncentred(qw, kw, vw, keys_of, scale, gw):   # softmax Jacobian without - P.dP
+    qw, kw, vw, gw = (np.asarray(t, np.float64) for t in (qw, kw, vw, gw))
+    dq, dk, dv = np.zeros_like(qw), np.zeros_like(kw), np.zeros_like(vw)
+    for p in range(qw.shape[0]):
+        J = keys_of(p)
+        lg = scale * (kw[J] @ qw[p])
+        P = np.exp(lg - lg.max())
+        P /= P.sum()
+        dv[J] += np.outer(P, gw[p])
+        dl = P * (vw[J] @ gw[p])
+        dq[p] = scale * (dl @ kw[J])
+        dk[J] += scale * np.outer(dl, qw[p])
+    return dq, dk, dv
+
+
+def _rope_t_as_forward(g, F, Hg, Wg, dims=(44, 42, 42), base=10000.0):   # rotation, not its transpose
+    return so.rope_3d(g, F, Hg, Wg, dims, base)
+
+
+def _linear_bwd_no_den(q, k, v, g, eps=1e-6):      # the normaliser's gradient dropped
+    H, Z = so.linear_state(k, v)
+    a = np.maximum(q, 0.0)
+    den = a @ Z + eps
+    dnum = g / den[:, None]
+    dH = a.T @ dnum
+    return (dnum @ H.T) * (q > 0), (v @ dH.T) * (k > 0), np.maximum(k, 0.0) @ dH
+
+
+def _gate_bwd_no_one_minus_s(x, w, b, ds):         # sigmoid derivative taken as s
+    x, w = np.asarray(x, np.float64), np.asarray(w, np.float64)
+    dt = ds * so.gate(x, w, b)
+    return np.broadcast_to(dt * w / x.shape[0], x.shape).copy(), dt * x.mean(axis=0), dt
+
+
 CASES = [
     ("st_permutation", _perm_inverse, lambda: TO.test_st_permutation_matches_sort_construction((4, 8, 8))),
     ("swa_keys", _swa_keys_short, lambda: TA.test_window_matches_masked_dense(64, 5)),
@@ -131,6 +168,10 @@ CASES = [
     ("combine_full", _combine_full_transposed, TL.test_layer_full_width_projection_and_output_projection),
     ("output_projection", _output_projection_transposed,
      TL.test_layer_full_width_projection_and_output_projection),
+    ("sparse_attention_backward", _sparse_bwd_uncentred, lambda: TB.test_backward_matches_finite_differences(False)),
+    ("rope_3d_transpose", _rope_t_as_forward, lambda: TB.test_backward_matches_finite_differences(True)),
+    ("linear_backward", _linear_bwd_no_den, lambda: TB.test_backward_matches_finite_differences(False)),
+    ("gate_backward", _gate_bwd_no_one_minus_s, lambda: TB.test_backward_matches_finite_differences(False)),
 ]
 
 
