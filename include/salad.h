@@ -110,8 +110,9 @@ typedef struct {
   int32_t proj_mode;                  /* SALAD_PROJ_HEAD or SALAD_PROJ_FULL        */
 } salad_problem;
 
-/* Bytes of workspace that any entry point below may need for problem *p
- * (the largest over all of them).  Errors: NULL, SHAPE, UNSUPPORTED. */
+/* Bytes of workspace that any entry point below except salad_attn_backward
+ * may need for problem *p (the largest over them); the backward has its own
+ * size, salad_backward_workspace_size.  Errors: NULL, SHAPE, UNSUPPORTED. */
 salad_status salad_workspace_size(const salad_problem *p, size_t *bytes);
 
 /* Head-wise token permutation ([I] 1.1), optionally with 3D RoPE ([S] step 3,
@@ -197,6 +198,32 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
                                 void *out, float *s_out, int32_t *idx_out, void *ws,
                                 size_t ws_bytes, hipStream_t stream);
 
+/* Backward of salad_attn_forward (head-wise projection, bf16 storage,
+ * d = 128): the gradients of L = sum(dout * out) that fine-tuning the
+ * layer needs ([S] steps 4-5 and the training configuration under
+ * 复现评估; [G] 2 A-B).  The pages print no backward; it is the forward's
+ * derivative, with these readings: the storage rounding of the rotated Q
+ * and K passes gradients unchanged; relu'(0) = 0; the Top-K selection is
+ * held fixed (recomputed from Q and K exactly as the forward does); a
+ * sample with s_b < branch_drop_tau gets no gradient through its linear
+ * branch, W_p or the gate; with s_override the gate is not differentiated.
+ *
+ * Inputs as for salad_attn_forward, plus dout [B,N,H,d] (bf16).  Outputs:
+ * dq, dk, dv [B,N,H,d] bf16 (w.r.t. the unrotated Q, K); dw_p [d,d] float32;
+ * when the gate is computed (s_override NULL): dx [B,N,C] bf16, dgate_w [C]
+ * and dgate_b [1] float32, each optional (NULL: not written); ds_out [B]
+ * float32 (optional): dL/ds_b.  Sums over rows and heads run in a fixed
+ * order (no atomics): results are deterministic.  Workspace:
+ * salad_backward_workspace_size.  Errors as above; SALAD_ERR_UNSUPPORTED for
+ * f32 storage or SALAD_PROJ_FULL. */
+salad_status salad_backward_workspace_size(const salad_problem *p, size_t *bytes);
+salad_status salad_attn_backward(const salad_problem *p, const void *q, const void *k,
+                                 const void *v, const void *x, const void *w_p,
+                                 const void *gate_w, float gate_b, const float *s_override,
+                                 const void *dout, void *dq, void *dk, void *dv, float *dw_p,
+                                 void *dx, float *dgate_w, float *dgate_b, float *ds_out,
+                                 void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Output projection ([S] step 7): out[b,n,:] = in[b,n,:] W_o, a row vector
  * times W_o [C, C] row-major, no bias; in, out [B, N, C] (equivalently
  * [B,N,H,d]) and W_o in io_dtype.  One hipBLASLt GEMM, float32 accumulation.
@@ -206,7 +233,9 @@ salad_status salad_output_projection(const salad_problem *p, const void *in, con
 
 /* Measurement hook.  While enabled (on != 0), salad_attn_forward records a
  * pair of HIP events around its sparse-attention kernel launch(es) on the
- * caller's stream (the first 4096 calls after enabling are recorded).
+ * caller's stream, and salad_attn_backward around its sparse-branch
+ * gradient kernels (dQ, then dK and dV); the first 4096 calls after
+ * enabling are recorded.
  * salad_profile_read waits for the recorded events, returns the number of
  * timed calls and their summed duration in milliseconds, and clears the
  * record.  Process-wide state; not thread-safe; not for use under graph

@@ -30,8 +30,8 @@ STATUS = {0: "SALAD_OK", 1: "SALAD_ERR_NULL", 2: "SALAD_ERR_SHAPE", 3: "SALAD_ER
 
 EXPORTS = ("salad_workspace_size", "salad_permute", "salad_block_select", "salad_sparse_attn",
            "salad_linear_state", "salad_linear_apply", "salad_gate", "salad_combine",
-           "salad_attn_forward", "salad_output_projection", "salad_profile_enable",
-           "salad_profile_read", "salad_last_error")
+           "salad_attn_forward", "salad_output_projection", "salad_backward_workspace_size",
+           "salad_attn_backward", "salad_profile_enable", "salad_profile_read", "salad_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
             "salad_combine": [P, vp, vp, vp, vp, vp, vp],
             "salad_attn_forward": [P, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp],
             "salad_output_projection": [P, vp, vp, vp, vp],
+            "salad_backward_workspace_size": [P, ctypes.POINTER(sz)],
+            "salad_attn_backward": [P, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    vp, sz, vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -283,6 +286,39 @@ def salad_output_projection(p: Problem, x, w_o, out, stream=None):
     _check(lib().salad_output_projection(
         ctypes.byref(p), _ptr(x, "in", n, dt), _ptr(w_o, "w_o", p.C ** 2, dt), _ptr(out, "out", n, dt),
         _stream(stream)))
+
+
+def salad_backward_workspace_size(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().salad_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def salad_attn_backward(p: Problem, q, k, v, x, w_p, gate_w, gate_b: float, dout, dq, dk, dv, dw_p, ws,
+                        dx=None, dgate_w=None, dgate_b=None, ds=None, s_override=None, stream=None):
+    """Gradients of sum(dout * salad_attn_forward(...)): dq, dk, dv [B,N,H,d]
+    and dx [B,N,C] in bf16; dw_p [d,d], dgate_w [C], dgate_b [1], ds [B] in
+    float32 (dx, dgate_w, dgate_b, ds optional)."""
+    import torch
+    n, _ = _sizes(p)
+    dt = _io_dtype(p)
+    C = p.n_heads * p.head_dim
+    _check(lib().salad_attn_backward(
+        ctypes.byref(p), _ptr(q, "q", n, dt), _ptr(k, "k", n, dt), _ptr(v, "v", n, dt),
+        _ptr(x, "x", p.batch * p.N * C, dt), _ptr(w_p, "w_p", p.w_p_numel, dt),
+        _ptr(gate_w, "gate_w", C, dt), float(gate_b),
+        _ptr(s_override, "s_override", p.batch, torch.float32), _ptr(dout, "dout", n, dt),
+        _ptr(dq, "dq", n, dt), _ptr(dk, "dk", n, dt), _ptr(dv, "dv", n, dt),
+        _ptr(dw_p, "dw_p", p.head_dim ** 2, torch.float32), _ptr(dx, "dx", p.batch * p.N * C, dt),
+        _ptr(dgate_w, "dgate_w", C, torch.float32), _ptr(dgate_b, "dgate_b", 1, torch.float32),
+        _ptr(ds, "ds", p.batch, torch.float32), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def backward_workspace(p: Problem, device="cuda"):
+    """A device workspace of salad_backward_workspace_size(p) bytes."""
+    import torch
+    return torch.empty(max(salad_backward_workspace_size(p), 16), dtype=torch.uint8, device=device)
 
 
 def workspace(p: Problem, device="cuda"):

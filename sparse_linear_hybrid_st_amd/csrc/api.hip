@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 #include <string>
 
@@ -542,6 +543,194 @@ salad_status salad_output_projection(const salad_problem *p, const void *in, con
   if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(SALAD_ERR_SHAPE, "in and out must not overlap");
   if (const char *m = gemm_rows(inf.bf16, rows, g.H * g.D, in, w_o, 0.f, out, stream))
     return fail(SALAD_ERR_HIP, "salad_output_projection: %s", m);
+  return SALAD_OK;
+}
+
+// ---- backward -----------------------------------------------------------------
+
+namespace {
+
+// Backward workspace (bf16, d = 128).  Regions 256-byte aligned: a shared
+// scratch (gate partials, then the linear-state and linear-backward split
+// partials, and the Top-K means and scores in between), working copies of
+// Q, K (rotated), V and dO, lse2 / D, the selection and its inverse lists,
+// fp32 dQ, dK, dV, the per-head linear state and backward matrices, the
+// gate's column sums and values, and the RoPE table.
+struct BwdPlan {
+  size_t wq, wk, wv, wg, lse, dsum, idx, inv_off, inv_list, dq, dk, dv, h, z;
+  size_t mf, mb, a_red, bz, dhb, dhtb, dwp_h, ds_part, colsum, s, dt, rope_tab;
+  int Np;
+  size_t total;
+};
+
+BwdPlan bwd_plan(const Info &inf) {
+  const Geom &g = inf.g;
+  BwdPlan pl = {};
+  const size_t BH = size_t(g.B) * g.H, D = size_t(g.D);
+  const size_t rows = BH * g.N;
+  pl.Np = (g.N + 63) / 64 * 64;
+  const size_t means = inf.any_topk ? up(select_ws_bytes(g)) : 0;
+  const size_t lin = up(BH * linear_splits(g) * (D * D + D) * sizeof(float));
+  const size_t gate = up(gate_ws_bytes(g));
+  size_t off = std::max(means, std::max(lin, gate));
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += up(bytes);
+    return at;
+  };
+  pl.wq = take(rows * D * 2);
+  pl.wk = take(rows * D * 2);
+  pl.wv = take(rows * D * 2);
+  pl.wg = take(rows * D * 2);
+  pl.lse = take(BH * pl.Np * sizeof(float));
+  pl.dsum = take(BH * pl.Np * sizeof(float));
+  pl.idx = take(inf.any_topk ? BH * g.nb * g.k * sizeof(int32_t) : 0);
+  pl.inv_off = take(inf.any_topk ? BH * (g.nb + 1) * sizeof(int32_t) : 0);
+  pl.inv_list = take(inf.any_topk ? BH * g.nb * g.k * sizeof(int32_t) : 0);
+  pl.dq = take(rows * D * sizeof(float));
+  pl.dk = take(rows * D * sizeof(float));
+  pl.dv = take(rows * D * sizeof(float));
+  pl.h = take(BH * D * D * sizeof(float));
+  pl.z = take(BH * D * sizeof(float));
+  pl.mf = take(BH * D * D * sizeof(float));
+  pl.mb = take(BH * D * D * 2);
+  pl.a_red = take(BH * D * D * sizeof(float));
+  pl.bz = take(BH * D * sizeof(float));
+  pl.dhb = take(BH * D * D * 2);
+  pl.dhtb = take(BH * D * D * 2);
+  pl.dwp_h = take(BH * D * D * sizeof(float));
+  pl.ds_part = take(BH * 16 * sizeof(float));
+  pl.colsum = take(size_t(g.B) * gate_bwd_splits(g) * g.H * D * sizeof(float));
+  pl.s = take(size_t(g.B) * sizeof(float));
+  pl.dt = take(size_t(g.B) * sizeof(float));
+  pl.rope_tab = take(inf.rope ? size_t(rope_table_entries(g)) * 16 : 0);
+  pl.total = off;
+  return pl;
+}
+
+salad_status validate_backward(const salad_problem *p, Info *inf) {
+  CHECK(validate(p, inf));
+  if (!inf->bf16)
+    return fail(SALAD_ERR_UNSUPPORTED, "salad_attn_backward is built for bf16 storage (d = 128) only");
+  if (inf->full)
+    return fail(SALAD_ERR_UNSUPPORTED, "salad_attn_backward supports the per-head projection (SALAD_PROJ_HEAD) only");
+  return SALAD_OK;
+}
+
+}  // namespace
+
+salad_status salad_backward_workspace_size(const salad_problem *p, size_t *bytes) {
+  Info inf;
+  CHECK(validate_backward(p, &inf));
+  if (!bytes) return fail(SALAD_ERR_NULL, "bytes is NULL");
+  *bytes = bwd_plan(inf).total;
+  return SALAD_OK;
+}
+
+salad_status salad_attn_backward(const salad_problem *p, const void *q, const void *k, const void *v,
+                                 const void *x, const void *w_p, const void *gate_w, float gate_b,
+                                 const float *s_override, const void *dout, void *dq, void *dk, void *dv,
+                                 float *dw_p, void *dx, float *dgate_w, float *dgate_b, float *ds_out,
+                                 void *ws, size_t ws_bytes, hipStream_t stream) {
+  Info inf;
+  CHECK(validate_backward(p, &inf));
+  CHECK(need(q, "q"));
+  CHECK(need(k, "k"));
+  CHECK(need(v, "v"));
+  CHECK(need(w_p, "w_p"));
+  CHECK(need(dout, "dout"));
+  CHECK(need(dq, "dq"));
+  CHECK(need(dk, "dk"));
+  CHECK(need(dv, "dv"));
+  CHECK(need(dw_p, "dw_p"));
+  const int has_gate = s_override == nullptr;
+  if (has_gate) {
+    CHECK(need(x, "x"));
+    CHECK(need(gate_w, "gate_w"));
+    if (dx) CHECK(need(dx, "dx"));
+    if (dgate_w) CHECK(need(dgate_w, "dgate_w"));
+    if (dgate_b && (reinterpret_cast<uintptr_t>(dgate_b) & 3u))
+      return fail(SALAD_ERR_ALIGN, "dgate_b is not 4-byte aligned");
+  } else {
+    CHECK(need(s_override, "s_override"));
+  }
+  if (ds_out) CHECK(need(ds_out, "ds_out"));
+  const Geom &g = inf.g;
+  const BwdPlan pl = bwd_plan(inf);
+  CHECK(need_ws(ws, ws_bytes, pl.total));
+  char *w = (char *)ws;
+  void *scratch = w;
+  bf16_t *wq = (bf16_t *)(w + pl.wq), *wk = (bf16_t *)(w + pl.wk), *wv = (bf16_t *)(w + pl.wv),
+         *wg = (bf16_t *)(w + pl.wg);
+  float *lse = (float *)(w + pl.lse), *dsum = (float *)(w + pl.dsum);
+  int32_t *idx = (int32_t *)(w + pl.idx);
+  float *gq = (float *)(w + pl.dq), *gk = (float *)(w + pl.dk), *gv = (float *)(w + pl.dv);
+  float *hm = (float *)(w + pl.h), *zv = (float *)(w + pl.z);
+  float *s = (float *)(w + pl.s);
+  double2 *tab = inf.rope ? (double2 *)(w + pl.rope_tab) : nullptr;
+  hipError_t e;
+
+  // gate values (and X's column sums for dL/dw)
+  if (has_gate) {
+    if ((e = launch_gate(g, 1, x, gate_w, gate_b, scratch, s, stream)) != hipSuccess ||
+        (e = launch_gate_colsum(g, (const bf16_t *)x, (float *)(w + pl.colsum), stream)) != hipSuccess)
+      return hip_status(e, "salad_attn_backward: gate");
+  } else if ((e = hipMemcpyAsync(s, s_override, sizeof(float) * g.B, hipMemcpyDeviceToDevice, stream)) !=
+             hipSuccess) {
+    return hip_status(e, "salad_attn_backward: copy s");
+  }
+  // working copies: rotated Q, K; V; dO
+  if ((inf.rope && (e = launch_rope_table(g, tab, stream)) != hipSuccess) ||
+      (e = launch_permute(g, 1, inf.rope, 0, q, wq, stream, tab)) != hipSuccess ||
+      (e = launch_permute(g, 1, inf.rope, 0, k, wk, stream, tab)) != hipSuccess ||
+      (e = launch_permute(g, 1, 0, 0, v, wv, stream)) != hipSuccess ||
+      (e = launch_permute(g, 1, 0, 0, dout, wg, stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_backward: permute");
+  const View qv = working_view(g, wq), kv = working_view(g, wk), vv = working_view(g, wv);
+  if ((e = launch_linear_state(g, 1, kv, vv, (float *)scratch, hm, zv, stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_backward: linear state");
+  int32_t *inv_off = nullptr, *inv_list = nullptr;
+  if (inf.any_topk) {
+    double *qm, *km, *sc;
+    select_regions(g, scratch, &qm, &km, &sc);
+    inv_off = (int32_t *)(w + pl.inv_off);
+    inv_list = (int32_t *)(w + pl.inv_list);
+    if ((e = launch_block_select(g, 1, qv, kv, qm, km, sc, idx, stream)) != hipSuccess ||
+        (e = launch_topk_inverse(g, idx, inv_off, inv_list, stream)) != hipSuccess)
+      return hip_status(e, "salad_attn_backward: block select");
+  }
+  // sparse branch: normalisers and D, then dQ, dK, dV
+  if ((e = launch_attn_bwd_prep(g, qv, kv, vv, idx, wg, lse, dsum, pl.Np, stream)) != hipSuccess ||
+      (e = prof_mark(0, stream)) != hipSuccess ||
+      (e = launch_attn_bwd(g, wq, wk, wv, wg, lse, dsum, pl.Np, idx, inv_off, inv_list, gq, gk, gv,
+                           stream)) != hipSuccess ||
+      (e = prof_mark(1, stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_backward: sparse attention");
+  // linear branch and projection (adds into dQ, dK, dV)
+  LinBwdScratch lw;
+  lw.mf = (float *)(w + pl.mf);
+  lw.mb = (bf16_t *)(w + pl.mb);
+  lw.partial = (float *)scratch;
+  lw.a_red = (float *)(w + pl.a_red);
+  lw.bz = (float *)(w + pl.bz);
+  lw.dhb = (bf16_t *)(w + pl.dhb);
+  lw.dhtb = (bf16_t *)(w + pl.dhtb);
+  lw.dwp_h = (float *)(w + pl.dwp_h);
+  lw.ds_part = (float *)(w + pl.ds_part);
+  if ((e = launch_linear_bwd(g, wq, wk, wv, wg, hm, zv, (const bf16_t *)w_p, s, gq, gk, gv, lw, dw_p,
+                             stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_backward: linear branch");
+  // gate
+  float *dt = (float *)(w + pl.dt);
+  if ((e = launch_gate_bwd(g, lw.ds_part, s, has_gate, (const float *)(w + pl.colsum), dt, ds_out,
+                           has_gate ? dgate_w : nullptr, has_gate ? dgate_b : nullptr, stream)) != hipSuccess ||
+      (has_gate && dx && (e = launch_gate_dx(g, dt, (const bf16_t *)gate_w, (bf16_t *)dx, stream)) != hipSuccess))
+    return hip_status(e, "salad_attn_backward: gate");
+  // back to the boundary layout (RoPE transposed for Q and K)
+  if ((e = launch_grad_scatter(g, gq, (bf16_t *)dq, tab, stream)) != hipSuccess ||
+      (e = launch_grad_scatter(g, gk, (bf16_t *)dk, tab, stream)) != hipSuccess ||
+      (e = launch_grad_scatter(g, gv, (bf16_t *)dv, nullptr, stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_backward: scatter");
   return SALAD_OK;
 }
 

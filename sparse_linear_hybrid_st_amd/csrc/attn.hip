@@ -26,15 +26,10 @@
 // f32 path (d = 64 or 128): one thread per query walks its key set.
 #include "common.h"
 #include "kernels.h"
+#include "mfma_util.h"
 
 namespace salad {
 
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-
-__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // ---------------------------------------------------------------------------
 // f32 reference-grade kernel: thread = (b, h, p).
@@ -90,36 +85,6 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(Geom g, View qv, View kv, 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel, d = 128.
 // ---------------------------------------------------------------------------
-constexpr int kD = 128;   // head dim
-constexpr int kBN = 64;   // keys per tile
-
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Workgroup barrier without the memory fence of __syncthreads(), whose
-// release half waits for every DMA in flight.  The barrier intrinsic by
-// itself does not order memory accesses in the compiler, so the empty asm
-// statements with a memory clobber pin every access (LDS reads, DMA issues)
-// to its side of the barrier, and the lgkmcnt wait makes this wave's LDS
-// reads complete before any wave passes.  DMA completion is waited for
-// explicitly (vmcnt) by the callers.
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt: no wait
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// K and V tiles are stored row-major ([key][d], 256-byte rows) in LDS.  The
-// 16-byte unit u of row j sits at u ^ kv_swz(j).  kv_swz is a bijection on
-// the low 4 bits of j that swaps its two 2-bit halves, so
-//   * the K operand reads (16 consecutive keys, one unit) hit 16 distinct
-//     units, and
-//   * the transposing V reads (4 consecutive keys x one 64-byte segment)
-//     hit 4 distinct segments.
-__device__ __forceinline__ int kv_swz(int j) { return ((j & 3) << 2) | ((j >> 2) & 3); }
-
 struct AttnArgs {
   Geom g;
   View q;
@@ -133,22 +98,23 @@ struct AttnArgs {
   const float *s_gate;   // fused: [B] gate values (branch dropping below g.drop_tau)
   View out;              // fused: output rows (boundary layout, scattered)
   View out_l;            // fused, full-width projection: s_b * O_l rows (base NULL otherwise)
+  const bf16_t *go;      // backward prep: dL/dO_s, working layout [B*H][N][128]
+  float *lse2;           // backward prep: [B*H][lse_stride] log2 of each row's softmax normaliser
+  float *dsum;           // backward prep: [B*H][lse_stride] D = dO . O_s per row
+  int lse_stride;        // backward prep: row stride of lse2 / dsum per head (>= N)
   int n_heads_sel;       // heads handled by this launch
   uint8_t heads[kMaxHeads];
   int tiles_per_head;    // query tiles per (b, head)
   int n_blocks;          // grid size (for the XCD-aware order)
 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
-// that each XCD walks a contiguous range of query tiles (neighbouring tiles
-// share most of their key window, which then stays in that XCD's L2).
-__device__ __forceinline__ int xcd_order(int bid, int T) {
-  const int q = T >> 3, r = T & 7, x = bid & 7, k = bid >> 3;
-  return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
-}
-
-template <int NW, bool FUSED>
+// MODE 0: O_s to a.o_s (fp32, working layout).  MODE 1: fused layer
+// epilogue (linear branch, projection, gate, scatter to token order).
+// MODE 2: backward preparation -- per row, the log2-domain normaliser
+// lse2 (P = exp2(scale*log2(e)*s - lse2)) and D = dO . O_s.
+template <int NW, int MODE>
 __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
+  constexpr bool FUSED = MODE == 1;
   constexpr int BM = NW * 32;
   constexpr int TILE = kBN * kD;                 // elements per K or V tile
   constexpr int DMA_PER_WAVE = (TILE * 2 / 1024) / NW;  // 1-KB DMA ops per tensor per wave
@@ -611,6 +577,28 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     return;
   }
 
+  if constexpr (MODE == 2) {
+    // both half-waves of a query column return together, so the exchange
+    // below sees its partner
+    if (pq >= g.N) return;
+    const bf16_t *grow = a.go + ((long long)bh * g.N + pq) * kD;
+    float dp = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const bf16x4 gv = *(const bf16x4 *)(grow + 32 * db + 8 * r4 + 4 * hl);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp = fmaf(o[db][4 * r4 + e] * inv, float(gv[e]), dp);
+      }
+    dp += __shfl_xor(dp, 32);
+    if (hl == 0) {
+      const long long row = (long long)bh * a.lse_stride + pq;
+      a.dsum[row] = dp;
+      a.lse2[row] = m_off + log2f(l_tot);
+    }
+    return;
+  }
   if (pq >= g.N) return;
   float *dst = a.o_s + ((long long)bh * g.N + pq) * kD;
 #pragma unroll
@@ -626,7 +614,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
 namespace {
 // One launch per head kind: window heads use 128-query tiles (4 waves),
 // Top-K heads one 64-query block per workgroup (2 waves).
-template <bool FUSED>
+template <int MODE>
 hipError_t launch_bf16(AttnArgs a, hipStream_t st) {
   const Geom &g = a.g;
   for (int mode = 0; mode < 2; ++mode) {
@@ -641,9 +629,9 @@ hipError_t launch_bf16(AttnArgs a, hipStream_t st) {
     const unsigned grid = unsigned(a.tiles_per_head) * a.n_heads_sel * g.B;
     a.n_blocks = int(grid);
     if (mode)
-      attn_bf16_kernel<2, FUSED><<<grid, 128, size_t(g.k) * sizeof(int32_t), st>>>(a);
+      attn_bf16_kernel<2, MODE><<<grid, 128, size_t(g.k) * sizeof(int32_t), st>>>(a);
     else
-      attn_bf16_kernel<4, FUSED><<<grid, 256, 0, st>>>(a);
+      attn_bf16_kernel<4, MODE><<<grid, 256, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -680,7 +668,24 @@ hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv
   for (int i = 0; i < 4; ++i) a.work[i] = ~0ull;
   a.idx = idx;
   a.o_s = o_s;
-  return launch_bf16<false>(a, st);
+  return launch_bf16<0>(a, st);
+}
+
+hipError_t launch_attn_bwd_prep(const Geom &g, View qv, View kv, View vv, const int32_t *idx,
+                                const bf16_t *go, float *lse2, float *dsum, int stride, hipStream_t st) {
+  if (!kv_streamable(g, kv, vv)) return hipErrorInvalidValue;
+  AttnArgs a = {};
+  a.g = g;
+  a.q = qv;
+  a.k = a.kd = kv;
+  a.v = a.vd = vv;
+  for (int i = 0; i < 4; ++i) a.work[i] = ~0ull;
+  a.idx = idx;
+  a.go = go;
+  a.lse2 = lse2;
+  a.dsum = dsum;
+  a.lse_stride = stride;
+  return launch_bf16<2>(a, st);
 }
 
 hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, View vd,
@@ -709,7 +714,7 @@ hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, 
   a.s_gate = s_gate;
   a.out = outv;
   a.out_l = outl;
-  return launch_bf16<true>(a, st);
+  return launch_bf16<1>(a, st);
 }
 
 }  // namespace salad

@@ -1,0 +1,560 @@
+// Backward of the sparse branch: dQ, dK and dV of softmax attention
+// restricted to the kept query-key pairs, for the bf16 working layout
+// (d = 128).
+//
+// The forward is the sparse branch of the SALAD structured summary
+// (paper.rainbus.top/paper/2601.16515), Prerequisites > Sparse Attention,
+// with the window and Top-K key sets of ijyty.com/news/870645 sections 1.1
+// and 1.2.  Its derivative, per query i over its kept keys j, with
+// P_ij = exp(scale q_i.k_j) / sum_j' exp(scale q_i.k_j'):
+//   dV_j += P_ij dO_i,   dP_ij = dO_i . v_j,   D_i = dO_i . O_i,
+//   dS_ij = P_ij (dP_ij - D_i),
+//   dQ_i = scale sum_j dS_ij k_j,   dK_j += scale dS_ij q_i.
+// P is recomputed from the per-row normaliser that the preparation pass
+// stored (lse2, in log2 units: P = exp2(scale log2(e) s - lse2)), so no N x N
+// matrix is kept.  The Top-K selection is held fixed.
+//
+// Two kernels, each accumulating in registers and writing every output row
+// once (no atomics, so results do not depend on scheduling):
+//   * attn_bwd_dq_kernel walks the kept key tiles of a query tile, like the
+//     forward: S^T = K Q^T and dP^T = V dO^T put one query per lane column,
+//     then dQ^T += K^T dS^T with K^T from transposing LDS reads;
+//   * attn_bwd_dkv_kernel walks the query tiles that keep a key tile:
+//     S = Q K^T and dP = dO V^T put one key per lane column, then
+//     dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T from transposing
+//     LDS reads.  Top-K heads find their query blocks in an inverse list
+//     (key block -> the query blocks that selected it) built per head.
+#include "common.h"
+#include "kernels.h"
+#include "mfma_util.h"
+
+namespace salad {
+
+struct BwdArgs {
+  Geom g;
+  const bf16_t *q, *k, *v, *go;  // working layout [B*H][N][128] (Q, K rotated)
+  const float *lse2, *dsum;      // [B*H][Np]: normaliser (log2 units) and D per row
+  int Np;                        // row stride of lse2 / dsum: N rounded up to 64
+  const int32_t *idx;            // Top-K selection [B*H][nb][k]
+  const int32_t *inv_off;        // Top-K: [B*H][nb + 1] offsets into inv_list of each key block
+  const int32_t *inv_list;       // Top-K: [B*H][nb * k] selecting query blocks, ascending per key block
+  float *dq, *dk, *dv;           // working layout fp32 [B*H][N][128]
+  int n_heads_sel;
+  uint8_t heads[kMaxHeads];
+  int tiles_per_head;
+  int n_blocks;
+};
+
+// ---------------------------------------------------------------------------
+// Top-K inverse lists.  For key block kb of head (b, h): the query blocks
+// whose selection contains kb, in ascending order.  One wave per (bh, kb)
+// scans every query block's (ascending) selection with a binary search;
+// ballots compact the hits in order.  Pass 0 counts, pass 1 writes at the
+// offsets of a per-head exclusive scan of the counts.
+// ---------------------------------------------------------------------------
+template <bool FILL>
+__global__ void __launch_bounds__(64) topk_inverse_kernel(Geom g, const int32_t *__restrict__ idx,
+                                                          int32_t *__restrict__ off,
+                                                          int32_t *__restrict__ list) {
+  const int kb = blockIdx.x, bh = blockIdx.y, h = bh % g.H, lane = threadIdx.x;
+  if (!bit(g.topk, h)) return;
+  const long long hb = (long long)bh * g.nb;
+  int n = FILL ? off[bh * (g.nb + 1) + kb] : 0;
+  for (int base = 0; base < g.nb; base += 64) {
+    const int qb = base + lane;
+    bool hit = false;
+    if (qb < g.nb) {
+      const int32_t *sel = idx + (hb + qb) * g.k;
+      int lo = 0, hi = g.k;  // first position with sel[pos] >= kb
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sel[mid] < kb) lo = mid + 1;
+        else hi = mid;
+      }
+      hit = lo < g.k && sel[lo] == kb;
+    }
+    const unsigned long long m = __ballot(hit);
+    if (FILL && hit) {
+      const int before = __popcll(m & ((1ull << lane) - 1ull));
+      list[hb * g.k + n + before] = qb;
+    }
+    n += __popcll(m);
+  }
+  if (!FILL && lane == 0) off[bh * (g.nb + 1) + kb] = n;
+}
+
+// Exclusive scan of the nb counts of one head (in place), total at [nb].
+__global__ void __launch_bounds__(256) topk_inverse_scan_kernel(Geom g, int32_t *__restrict__ off) {
+  const int bh = blockIdx.x, h = bh % g.H, t = threadIdx.x;
+  if (!bit(g.topk, h)) return;
+  int32_t *o = off + (long long)bh * (g.nb + 1);
+  __shared__ int part[256];
+  const int per = (g.nb + 255) / 256, s0 = t * per, s1 = min(g.nb, s0 + per);
+  int sum = 0;
+  for (int i = s0; i < s1; ++i) sum += o[i];
+  part[t] = sum;
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int c = part[i];
+      part[i] = run;
+      run += c;
+    }
+    o[g.nb] = run;
+  }
+  __syncthreads();
+  int run = part[t];
+  for (int i = s0; i < s1; ++i) {
+    const int c = o[i];
+    o[i] = run;
+    run += c;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared tile machinery.  A 64 x 128 bf16 tile of working rows (K, V, Q or
+// dO) is staged in LDS row-major with the kv_swz unit swizzle; DMA op i of
+// wave w fills rows 4*(i*NW + w) .. +3 (lane l: row + l/16, physical unit
+// l%16, which holds logical unit (l%16) ^ kv_swz(row)).  Rows past N re-read
+// row N-1: finite values whose pairs are masked.
+// ---------------------------------------------------------------------------
+template <int NW>
+struct TileDma {
+  static constexpr int PER_WAVE = 16 / NW;  // 1-KB DMA ops per tile per wave
+  int row[PER_WAVE], unit[PER_WAVE];
+  __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      row[i] = 4 * (i * NW + w) + (lane >> 4);
+      unit[i] = (lane & 15) ^ kv_swz(row[i]);
+    }
+  }
+  __device__ __forceinline__ void issue(const bf16_t *head, int r0, int N, bf16_t *dst, int w) const {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int r = min(r0 + row[i], N - 1);
+      __builtin_amdgcn_global_load_lds((const void *)(head + (long long)r * kD + unit[i] * 8),
+                                       (lds_void *)(dst + (4 * (i * NW + w)) * kD), 16, 0, 0);
+    }
+  }
+};
+
+// LDS element offsets used by both kernels.  Row operand (row l32 of a
+// 32-row block, logical unit 2ks + hl): k_lane + 16 * (ks ^ k_x).
+// Transposing operand (rows of a k-step as the MFMA k index, features of
+// d-block db as the lane index): t_off[r][db] plus 16*kk rows.
+struct OperandOffsets {
+  int k_lane, k_x;
+  int t_off[2][4];
+  __device__ __forceinline__ void init(int lane) {
+    const int hl = lane >> 5, l32 = lane & 31;
+    const int kswz = kv_swz(l32);
+    k_lane = l32 * kD + 8 * (hl ^ (kswz & 1));
+    k_x = kswz >> 1;
+    const int gq = lane >> 4, jl = lane & 15;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int row = 8 * r + 4 * hl + (jl >> 2);
+        const int d = 32 * db + 16 * (gq & 1) + 4 * (jl & 3);
+        t_off[r][db] = row * kD + (((d >> 3) ^ kv_swz(row)) << 3) + (d & 4);
+      }
+  }
+};
+
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+
+// A operand of k-step kk from a transposing read of tile Ts (rows 16kk..):
+// lane -> feature 32db + l32, k index -> rows 16kk + 8r + 4hl + e.
+__device__ __forceinline__ bf16x8 tr_operand(const bf16_t *Ts, const OperandOffsets &oo, int kk, int db) {
+  const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Ts + 16 * kk * kD + oo.t_off[0][db]));
+  const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Ts + 16 * kk * kD + oo.t_off[1][db]));
+  const s16x8 v = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+  return *(const bf16x8 *)&v;
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  A workgroup owns a query tile (128 queries, 4 waves, window heads;
+// one 64-query block, 2 waves, Top-K heads); wave w keeps queries
+// q0 + 32w + l32 and their dO rows as MFMA B operands.  Key tiles of 64 are
+// double-buffered in LDS.
+// ---------------------------------------------------------------------------
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 2) attn_bwd_dq_kernel(BwdArgs a) {
+  constexpr int BM = NW * 32;
+  constexpr bool TOPK = NW == 2;
+  constexpr int TILE = kBN * kD;
+  __shared__ __attribute__((aligned(1024))) bf16_t K0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t K1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t V0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t V1[TILE];
+  extern __shared__ int32_t sel_lds[];  // Top-K: first key row of each selected block
+  const Geom &g = a.g;
+  const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int tile = xcd_order(blockIdx.x, a.n_blocks);
+  const int qt = tile % a.tiles_per_head, bhs = tile / a.tiles_per_head;
+  const int h = a.heads[bhs % a.n_heads_sel], b = bhs / a.n_heads_sel;
+  const int q0 = qt * BM, bh = b * g.H + h;
+  const long long hrow = (long long)bh * g.N;
+  const bf16_t *hk = a.k + hrow * kD, *hv = a.v + hrow * kD;
+  const int pq = q0 + 32 * w + l32, pqc = min(pq, g.N - 1);
+
+  bf16x8 qf[8], gf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qf[ks] = *(const bf16x8 *)(a.q + (hrow + pqc) * kD + (2 * ks + hl) * 8);
+    gf[ks] = *(const bf16x8 *)(a.go + (hrow + pqc) * kD + (2 * ks + hl) * 8);
+  }
+  const float lse = a.lse2[(long long)bh * a.Np + pqc];
+  const float dsv = a.dsum[(long long)bh * a.Np + pqc];
+  const float c2 = g.scale * 1.4426950408889634f;
+
+  int n_tiles, kt_first = 0;
+  if (TOPK) {
+    n_tiles = g.k;
+    const int32_t *sel = a.idx + ((long long)bh * g.nb + q0 / g.block) * g.k;
+    for (int j = t; j < n_tiles; j += NW * 64) {
+      const int kb = sel[j];
+      sel_lds[j] = (kb >= 0 && kb < g.nb) ? kb * g.block : g.N;
+    }
+    __syncthreads();
+  } else {
+    const int lo = max(0, q0 - g.r), hi = min(g.N - 1, q0 + BM - 1 + g.r);
+    kt_first = lo / kBN;
+    n_tiles = hi / kBN - kt_first + 1;
+  }
+  auto tile_start = [&](int it) -> int { return TOPK ? sel_lds[it] : (kt_first + it) * kBN; };
+  const int wq_lo = q0 + 32 * w, wq_hi = min(q0 + 32 * w + 31, g.N - 1);
+
+  TileDma<NW> dma;
+  dma.init(w, lane);
+  OperandOffsets oo;
+  oo.init(lane);
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dq[i] = f32x16{};
+
+  auto compute = [&](int k0, const bf16_t *__restrict__ Ks, const bf16_t *__restrict__ Vs) {
+    bool any, full;
+    if (TOPK) {
+      any = k0 < g.N;
+      full = k0 + kBN <= g.N;
+    } else {
+      const int k1 = min(k0 + kBN, g.N) - 1;
+      any = (k0 <= wq_hi + g.r) && (k1 >= wq_lo - g.r) && (wq_lo <= wq_hi);
+      full = (k0 + kBN <= g.N) && (k0 >= wq_hi - g.r) && (k0 + kBN - 1 <= wq_lo + g.r);
+    }
+    if (!any) return;
+    // S^T = K Q^T and dP^T = V dO^T, two blocks of 32 keys each
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int o = kb * 32 * kD + oo.k_lane + 16 * (ks ^ oo.k_x);
+        s[kb] = mfma_32x32x16(*(const bf16x8 *)(Ks + o), qf[ks], s[kb]);
+        dp[kb] = mfma_32x32x16(*(const bf16x8 *)(Vs + o), gf[ks], dp[kb]);
+      }
+    // dS^T = P^T (dP^T - D); key of register r of block kb:
+    // k0 + 32kb + 8(r/4) + 4hl + r%4
+    bf16x8 dsb[4];
+    const int jl = k0 + 4 * hl;
+    const unsigned wb = unsigned(pq - jl + g.r);
+    const int lim = g.N - jl;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * half + e;
+          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const bool keep = full || ((c < lim) & (TOPK | (wb - unsigned(c) <= unsigned(2 * g.r))));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -lse));
+          v[e] = (__bf16)(keep ? p * (dp[kb][r] - dsv) : 0.f);
+        }
+        dsb[2 * kb + half] = v;
+      }
+    // dQ^T[d][q] += K^T[d][keys] dS^T[keys][q]
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 ka[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) ka[db] = tr_operand(Ks, oo, kk, db);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) dq[db] = mfma_32x32x16(ka[db], dsb[kk], dq[db]);
+    }
+  };
+
+  int k_cur = n_tiles > 0 ? tile_start(0) : 0;
+  if (n_tiles > 0) {
+    dma.issue(hk, k_cur, g.N, K0, w);
+    dma.issue(hv, k_cur, g.N, V0, w);
+  }
+  for (int it = 0; it < n_tiles; it += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    const int k_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
+    if (it + 1 < n_tiles) {
+      dma.issue(hk, k_nxt, g.N, K1, w);
+      dma.issue(hv, k_nxt, g.N, V1, w);
+    }
+    compute(k_cur, K0, V0);
+    if (it + 1 >= n_tiles) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    const int k_nn = it + 2 < n_tiles ? tile_start(it + 2) : 0;
+    if (it + 2 < n_tiles) {
+      dma.issue(hk, k_nn, g.N, K0, w);
+      dma.issue(hv, k_nn, g.N, V0, w);
+    }
+    compute(k_nxt, K1, V1);
+    k_cur = k_nn;
+  }
+
+  if (pq >= g.N) return;
+  float *dst = a.dq + (hrow + pq) * kD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 v = {dq[db][4 * r4] * g.scale, dq[db][4 * r4 + 1] * g.scale,
+                       dq[db][4 * r4 + 2] * g.scale, dq[db][4 * r4 + 3] * g.scale};
+      *(f32x4 *)(dst + 32 * db + 8 * r4 + 4 * hl) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  A workgroup owns a key tile (128 keys, 4 waves, window heads; one
+// 64-key block, 2 waves, Top-K heads); wave w keeps keys k0 + 32w + l32 and
+// their V rows as MFMA B operands.  Query tiles of 64 rows (Q, dO, lse2, D)
+// are double-buffered in LDS and consumed as two 32-query halves.
+// ---------------------------------------------------------------------------
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
+  constexpr int BK = NW * 32;
+  constexpr bool TOPK = NW == 2;
+  constexpr int TILE = kBN * kD;
+  __shared__ __attribute__((aligned(1024))) bf16_t Q0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t Q1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t G0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t G1[TILE];
+  __shared__ __attribute__((aligned(16))) float L0[kBN], L1[kBN], D0[kBN], D1[kBN];
+  extern __shared__ int32_t qsel_lds[];  // Top-K: first query row of each selecting block
+  const Geom &g = a.g;
+  const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int tile = xcd_order(blockIdx.x, a.n_blocks);
+  const int kt = tile % a.tiles_per_head, bhs = tile / a.tiles_per_head;
+  const int h = a.heads[bhs % a.n_heads_sel], b = bhs / a.n_heads_sel;
+  const int k0 = kt * BK, bh = b * g.H + h;
+  const long long hrow = (long long)bh * g.N;
+  const bf16_t *hq = a.q + hrow * kD, *hg = a.go + hrow * kD;
+  const float *hl2 = a.lse2 + (long long)bh * a.Np, *hds = a.dsum + (long long)bh * a.Np;
+  const int pk = k0 + 32 * w + l32, pkc = min(pk, g.N - 1);
+
+  bf16x8 kf[8], vf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    kf[ks] = *(const bf16x8 *)(a.k + (hrow + pkc) * kD + (2 * ks + hl) * 8);
+    vf[ks] = *(const bf16x8 *)(a.v + (hrow + pkc) * kD + (2 * ks + hl) * 8);
+  }
+  const float c2 = g.scale * 1.4426950408889634f;
+
+  int n_tiles, qt_first = 0;
+  if (TOPK) {
+    const int kb = k0 / g.block;
+    const int32_t *o = a.inv_off + (long long)bh * (g.nb + 1);
+    const int beg = o[kb];
+    n_tiles = o[kb + 1] - beg;
+    const int32_t *lst = a.inv_list + (long long)bh * g.nb * g.k + beg;
+    for (int j = t; j < n_tiles; j += NW * 64) qsel_lds[j] = lst[j] * g.block;
+    __syncthreads();
+  } else {
+    const int lo = max(0, k0 - g.r), hi = min(g.N - 1, k0 + BK - 1 + g.r);
+    qt_first = lo / kBN;
+    n_tiles = hi / kBN - qt_first + 1;
+  }
+  auto tile_start = [&](int it) -> int { return TOPK ? qsel_lds[it] : (qt_first + it) * kBN; };
+  const int wk_lo = k0 + 32 * w, wk_hi = k0 + 32 * w + 31;
+
+  TileDma<NW> dma;
+  dma.init(w, lane);
+  OperandOffsets oo;
+  oo.init(lane);
+  // lse2 and D of a query tile: 16 lanes of wave 0 move 64 floats each
+  // (the arrays are padded to a multiple of 64 rows per head)
+  auto issue_tile = [&](int q0, bf16_t *Qd, bf16_t *Gd, float *Ld, float *Dd) {
+    dma.issue(hq, q0, g.N, Qd, w);
+    dma.issue(hg, q0, g.N, Gd, w);
+    if (w == 0 && lane < 16) {
+      __builtin_amdgcn_global_load_lds((const void *)(hl2 + q0 + 4 * lane), (lds_void *)Ld, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(hds + q0 + 4 * lane), (lds_void *)Dd, 16, 0, 0);
+    }
+  };
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  auto compute = [&](int q0, const bf16_t *__restrict__ Qs, const bf16_t *__restrict__ Gs,
+                     const float *__restrict__ Ls, const float *__restrict__ Ds) {
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int i0 = q0 + 32 * qs;
+      bool any, full;
+      if (TOPK) {
+        any = i0 < g.N;
+        full = i0 + 31 < g.N;
+      } else {
+        any = (i0 < g.N) && (i0 <= wk_hi + g.r) && (i0 + 31 >= wk_lo - g.r);
+        full = (i0 + 31 < g.N) && (i0 + 31 - wk_lo <= g.r) && (wk_hi - i0 <= g.r);
+      }
+      if (!any) continue;
+      // S = Q K^T and dP = dO V^T for 32 queries (rows) x this wave's keys
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int o = qs * 32 * kD + oo.k_lane + 16 * (ks ^ oo.k_x);
+        s = mfma_32x32x16(*(const bf16x8 *)(Qs + o), kf[ks], s);
+        dp = mfma_32x32x16(*(const bf16x8 *)(Gs + o), vf[ks], dp);
+      }
+      // query of register r: i0 + 8(r/4) + 4hl + r%4
+      bf16x8 pb[2], dsb[2];
+      const unsigned wb = unsigned(i0 + 4 * hl - pk + g.r);  // i - pk + r = wb + c
+      const int lim = g.N - i0 - 4 * hl;                    // i < N  <=>  c < lim
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 lv = *(const f32x4 *)(Ls + 32 * qs + 8 * m + 4 * hl);
+        const f32x4 dv4 = *(const f32x4 *)(Ds + 32 * qs + 8 * m + 4 * hl);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * m + e, c = 8 * m + e;
+          const bool keep = full || ((c < lim) & (TOPK | (wb + unsigned(c) <= unsigned(2 * g.r))));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lv[e]));
+          const float pk_ = keep ? p : 0.f;
+          const float dsv = keep ? p * (dp[r] - dv4[e]) : 0.f;
+          pb[r >> 3][r & 7] = (__bf16)pk_;
+          dsb[r >> 3][r & 7] = (__bf16)dsv;
+        }
+      }
+      // dV^T[d][keys] += dO^T[d][q] P[q][keys];  dK^T += Q^T dS
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 ga[4], qa[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          ga[db] = tr_operand(Gs + qs * 32 * kD, oo, kk, db);
+          qa[db] = tr_operand(Qs + qs * 32 * kD, oo, kk, db);
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          dv[db] = mfma_32x32x16(ga[db], pb[kk], dv[db]);
+          dk[db] = mfma_32x32x16(qa[db], dsb[kk], dk[db]);
+        }
+      }
+    }
+  };
+
+  int q_cur = n_tiles > 0 ? tile_start(0) : 0;
+  if (n_tiles > 0) issue_tile(q_cur, Q0, G0, L0, D0);
+  for (int it = 0; it < n_tiles; it += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    const int q_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
+    if (it + 1 < n_tiles) issue_tile(q_nxt, Q1, G1, L1, D1);
+    compute(q_cur, Q0, G0, L0, D0);
+    if (it + 1 >= n_tiles) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    const int q_nn = it + 2 < n_tiles ? tile_start(it + 2) : 0;
+    if (it + 2 < n_tiles) issue_tile(q_nn, Q0, G0, L0, D0);
+    compute(q_nxt, Q1, G1, L1, D1);
+    q_cur = q_nn;
+  }
+
+  if (pk >= g.N) return;
+  float *dkr = a.dk + (hrow + pk) * kD, *dvr = a.dv + (hrow + pk) * kD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 kv4 = {dk[db][4 * r4] * g.scale, dk[db][4 * r4 + 1] * g.scale,
+                         dk[db][4 * r4 + 2] * g.scale, dk[db][4 * r4 + 3] * g.scale};
+      const f32x4 vv4 = {dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
+      *(f32x4 *)(dkr + 32 * db + 8 * r4 + 4 * hl) = kv4;
+      *(f32x4 *)(dvr + 32 * db + 8 * r4 + 4 * hl) = vv4;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers: one launch per head kind and kernel (window heads with 4
+// waves, Top-K heads with 2).
+// ---------------------------------------------------------------------------
+hipError_t launch_topk_inverse(const Geom &g, const int32_t *idx, int32_t *off, int32_t *list,
+                               hipStream_t st) {
+  const dim3 grid(g.nb, g.B * g.H);
+  topk_inverse_kernel<false><<<grid, 64, 0, st>>>(g, idx, off, list);
+  topk_inverse_scan_kernel<<<g.B * g.H, 256, 0, st>>>(g, off);
+  topk_inverse_kernel<true><<<grid, 64, 0, st>>>(g, idx, off, list);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, const bf16_t *v,
+                           const bf16_t *go, const float *lse2, const float *dsum, int Np,
+                           const int32_t *idx, const int32_t *inv_off, const int32_t *inv_list,
+                           float *dq, float *dk, float *dv, hipStream_t st) {
+  if (g.D != kD) return hipErrorInvalidValue;
+  BwdArgs a = {};
+  a.g = g;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.go = go;
+  a.lse2 = lse2;
+  a.dsum = dsum;
+  a.Np = Np;
+  a.idx = idx;
+  a.inv_off = inv_off;
+  a.inv_list = inv_list;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  for (int mode = 0; mode < 2; ++mode) {
+    a.n_heads_sel = 0;
+    for (int h = 0; h < g.H; ++h) {
+      const bool is_topk = (g.topk[h >> 6] >> (h & 63)) & 1ull;
+      if (is_topk == bool(mode)) a.heads[a.n_heads_sel++] = uint8_t(h);
+    }
+    if (a.n_heads_sel == 0) continue;
+    const int BM = mode ? 64 : 128;
+    a.tiles_per_head = (g.N + BM - 1) / BM;
+    const unsigned grid = unsigned(a.tiles_per_head) * a.n_heads_sel * g.B;
+    a.n_blocks = int(grid);
+    if (mode) {
+      attn_bwd_dq_kernel<2><<<grid, 128, size_t(g.k) * sizeof(int32_t), st>>>(a);
+      attn_bwd_dkv_kernel<2><<<grid, 128, size_t(g.nb) * sizeof(int32_t), st>>>(a);
+    } else {
+      attn_bwd_dq_kernel<4><<<grid, 256, 0, st>>>(a);
+      attn_bwd_dkv_kernel<4><<<grid, 256, 0, st>>>(a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace salad

@@ -72,6 +72,58 @@ hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, 
                              const uint64_t work[4], const int32_t *idx, const bf16_t *hp,
                              const float *z, const float *s_gate, View outv, View outl,
                              hipStream_t st);
+// Backward preparation (bf16, d = 128, working-layout views): the forward
+// sparse attention per row, reduced to lse2 (log2 of the softmax
+// normaliser in units of scale*log2(e) scores) and D = dO . O_s, with dO
+// (go) in working layout; lse2 / dsum rows are `stride` apart per head.
+hipError_t launch_attn_bwd_prep(const Geom &g, View qv, View kv, View vv, const int32_t *idx,
+                                const bf16_t *go, float *lse2, float *dsum, int stride, hipStream_t st);
+// ---- backward (bf16, d = 128, working layout) ------------------------------
+// Fixed-order sum of S split partials [B*H][S][D*D + D] into h and z.
+hipError_t launch_linear_reduce(const Geom &g, int S, const float *partial, float *h, float *z,
+                                hipStream_t st);
+// Top-K inverse lists: off [B*H][nb + 1] (per key block, the offset of its
+// selecting query blocks in list [B*H][nb * k]).
+hipError_t launch_topk_inverse(const Geom &g, const int32_t *idx, int32_t *off, int32_t *list,
+                               hipStream_t st);
+// Sparse-branch gradients into dq, dk, dv (fp32, working layout; written,
+// not accumulated).  lse2 / dsum rows are Np apart per head.
+hipError_t launch_attn_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, const bf16_t *v,
+                           const bf16_t *go, const float *lse2, const float *dsum, int Np,
+                           const int32_t *idx, const int32_t *inv_off, const int32_t *inv_list,
+                           float *dq, float *dk, float *dv, hipStream_t st);
+// Scratch of the linear-branch backward (sizes per B*H heads, d = 128):
+// mf [D*D] fp32, mb [D*D] bf16, partial [S][D*D + D] fp32 (S =
+// linear_splits), a_red [D*D] and bz [D] fp32, dhb, dhtb [D*D] bf16,
+// dwp_h [D*D] fp32, ds_part [16] fp32.
+struct LinBwdScratch {
+  float *mf;
+  bf16_t *mb;
+  float *partial, *a_red, *bz;
+  bf16_t *dhb, *dhtb;
+  float *dwp_h, *ds_part;
+};
+// Linear-branch and projection gradients: adds into dq, dk, dv (which must
+// hold the sparse-branch gradients), writes dw_p [d][d] and ws.ds_part
+// (16 partial sums of dL/ds per head; zero for dropped samples).
+hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, const bf16_t *v,
+                             const bf16_t *go, const float *hm, const float *zv, const bf16_t *w_p,
+                             const float *s_gate, float *dq, float *dk, float *dv, const LinBwdScratch &w,
+                             float *dw_p, hipStream_t st);
+// fp32 working-layout gradient rows -> io boundary layout [B,N,H,d], turned
+// back by the transposed RoPE rotation when table is non-NULL.
+hipError_t launch_grad_scatter(const Geom &g, const float *src, bf16_t *dst, const double2 *table,
+                               hipStream_t st);
+// Gate backward.  colsum: partial column sums of X [B][splits][C] fp32;
+// final: ds_b = sum of the heads' partials, dt_b = ds_b s_b (1 - s_b) (0 for
+// dropped samples or with s_override), dgate_w, dgate_b, optional ds_out;
+// dx: dX[b, n, :] = dt_b w / N.
+int gate_bwd_splits(const Geom &g);
+hipError_t launch_gate_colsum(const Geom &g, const bf16_t *x, float *partial, hipStream_t st);
+hipError_t launch_gate_bwd(const Geom &g, const float *ds_part, const float *s, int has_gate,
+                           const float *colsum, float *dt, float *ds_out, float *dgate_w,
+                           float *dgate_b, hipStream_t st);
+hipError_t launch_gate_dx(const Geom &g, const float *dt, const bf16_t *w, bf16_t *dx, hipStream_t st);
 // Whether the attention kernel can stream K, V rows through these views.
 bool kv_direct_ok(const Geom &g, View kd, View vd);
 hipError_t launch_linear_apply(const Geom &g, int bf16, View qv, const float *h, const float *z,

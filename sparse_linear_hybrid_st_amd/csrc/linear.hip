@@ -374,6 +374,13 @@ hipError_t launch_linear_partials(const Geom &g, View kv, View vv, float *partia
   return hipGetLastError();
 }
 
+hipError_t launch_linear_reduce(const Geom &g, int S, const float *partial, float *h, float *z,
+                                hipStream_t st) {
+  dim3 grid((g.D * g.D + g.D + 255) / 256, g.B * g.H);
+  linear_reduce_kernel<<<grid, 256, 0, st>>>(g.D, S, partial, h, z);
+  return hipGetLastError();
+}
+
 hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float *partial, float *h,
                                float *z, hipStream_t st) {
   const int S = linear_splits(g);

@@ -1,0 +1,121 @@
+"""Backward parity (salad_attn_backward) against the oracle's attn_backward,
+on small bf16 layers with ragged tails, every head kind, RoPE, a CFG pair,
+branch dropping and a fixed gate.
+
+Tolerances.  The device computes in bf16 MFMA operands with fp32
+accumulation: P and dS are rounded to bf16 (relative 2^-9) before the
+products, M = H W_p and dH are rounded to bf16 for the linear branch, and
+dQ, dK, dV, dX are stored in bf16 (relative 2^-9).  Each gradient is
+therefore compared relative to its own scale: max |err| <= 2e-2 * max|ref|
+and ||err|| <= 1e-2 * ||ref|| (Frobenius); the fp32 reductions dW_p,
+dgate_w, dgate_b and ds meet the same relative bar."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_linear_hybrid_st_amd as S
+from sparse_linear_hybrid_st_amd import configs as C
+from sparse_linear_hybrid_st_amd import inputs as I
+from tests.gpu_util import dev, host64, oracle_kwargs
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL, FRO_REL = 2e-2, 1e-2
+
+CASES = [
+    C.small("bwd-ragged-mixed", (5, 6, 7), 4, 128, "bf16", [0, 1, 2, 2], 37, 64, 2),
+    C.small("bwd-window-multi-tile", (6, 16, 24), 2, 128, "bf16", [1, 0], 300, 64, 1, seed=9),
+    C.small("bwd-topk-batch2", (4, 12, 20), 3, 128, "bf16", [2, 2, 2], 0, 64, 4, batch=2),
+    C.small("bwd-rope-cfg", (3, 4, 10), 4, 128, "bf16", [0, 1, 2, 2], 20, 64, 1, batch=2, rope=True,
+            rope_dims=(44, 42, 42), x_sample_shift=True),
+    C.small("bwd-short", (1, 1, 37), 1, 128, "bf16", [1], 5, 64, 1),
+]
+
+
+def _dout(w):
+    rng = np.random.default_rng(w.seed + 77)
+    g = rng.standard_normal((w.batch, w.N, w.n_heads, w.head_dim)).astype(np.float32)
+    return I.to_storage(g, w.io_dtype)
+
+
+def run_backward(w, inp, dout, s_override=None, branch_drop_tau=0.0):
+    p = S.problem_from_workload(w, branch_drop_tau=branch_drop_tau)
+    d = {n: dev(inp[n]) for n in ("q", "k", "v", "x", "w_p", "gate_w")}
+    go = dev(dout)
+    dq, dk, dv = (torch.empty_like(d["q"]) for _ in range(3))
+    dx = torch.empty_like(d["x"])
+    dwp = torch.empty((w.head_dim, w.head_dim), dtype=torch.float32, device="cuda")
+    dgw = torch.empty(w.n_heads * w.head_dim, dtype=torch.float32, device="cuda")
+    dgb = torch.empty(1, dtype=torch.float32, device="cuda")
+    ds = torch.empty(w.batch, dtype=torch.float32, device="cuda")
+    so = None if s_override is None else torch.tensor(s_override, dtype=torch.float32, device="cuda")
+    S.salad_attn_backward(p, d["q"], d["k"], d["v"], d["x"], d["w_p"], d["gate_w"], inp["gate_b"], go,
+                          dq, dk, dv, dwp, S.backward_workspace(p), dx=dx, dgate_w=dgw, dgate_b=dgb, ds=ds,
+                          s_override=so)
+    torch.cuda.synchronize()
+    return {"dq": host64(dq), "dk": host64(dk), "dv": host64(dv), "dx": host64(dx), "dw_p": host64(dwp),
+            "dgate_w": host64(dgw), "dgate_b": float(dgb.item()), "ds": host64(ds)}
+
+
+def oracle_backward(w, inp, dout, **extra):
+    return O.attn_backward(*(I.as_f64(inp[n]) for n in ("q", "k", "v", "x", "w_p", "gate_w")),
+                           inp["gate_b"], I.as_f64(dout), **oracle_kwargs(w), **extra)
+
+
+def assert_rel(got, ref, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    err = np.abs(got - ref)
+    fro = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    assert err.max() <= MAX_REL * scale, f"{what}: max err {err.max():.3g} vs scale {scale:.3g}"
+    assert fro <= FRO_REL, f"{what}: relative Frobenius error {fro:.3g}"
+    return float(err.max() / scale), fro
+
+
+def _compare(w, got, ref, names=("dq", "dk", "dv", "dw_p", "dx", "dgate_w", "ds")):
+    out = []
+    for n in names:
+        out.append((n,) + assert_rel(got[n], ref[n], f"{w.name}: {n}"))
+    print(w.name, " ".join(f"{n} {m:.2g}/{f:.2g}" for n, m, f in out))
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_backward_matches_oracle(w):
+    inp = I.make_inputs(w)
+    dout = _dout(w)
+    got = run_backward(w, inp, dout)
+    ref = oracle_backward(w, inp, dout)
+    _compare(w, got, ref)
+    assert abs(got["dgate_b"] - ref["dgate_b"]) <= MAX_REL * max(abs(ref["dgate_b"]), 1e-30) + 1e-7
+
+
+def test_backward_with_dropping_and_fixed_gate():
+    w = CASES[3]
+    inp = I.make_inputs(w)
+    dout = _dout(w)
+    s = np.array([O.gate(I.as_f64(inp["x"])[b], I.as_f64(inp["gate_w"]), inp["gate_b"])
+                  for b in range(w.batch)])
+    tau = float(s.mean())
+    got = run_backward(w, inp, dout, branch_drop_tau=tau)
+    ref = oracle_backward(w, inp, dout, drop_tau=tau)
+    _compare(w, got, ref, names=("dq", "dk", "dv", "dw_p", "dgate_w"))
+    lo = int(np.argmin(s))
+    assert got["ds"][lo] == 0.0 and np.all(got["dx"][lo] == 0.0)
+    s0 = [0.25, 0.6]
+    got = run_backward(w, inp, dout, s_override=s0)
+    ref = oracle_backward(w, inp, dout, s_override=np.array(s0))
+    _compare(w, got, ref, names=("dq", "dk", "dv", "dw_p", "ds"))
+
+
+def test_backward_is_deterministic():
+    w = CASES[0]
+    inp = I.make_inputs(w)
+    dout = _dout(w)
+    a = run_backward(w, inp, dout)
+    b = run_backward(w, inp, dout)
+    for n in ("dq", "dk", "dv", "dx", "dw_p", "dgate_w", "ds"):
+        assert np.array_equal(a[n], b[n]), n
