@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "ms/layer and effective TFLOP/s of hybrid attention at N=31,200, 90% sparsity"
+METRIC_BWD = "ms/layer and effective TFLOP/s of the hybrid attention backward at N=31,200, 90% sparsity"
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "attn_counters.json")
@@ -129,6 +130,9 @@ def main():
                     help="static projection W_p: one [d, d] matrix per head (default) or one "
                          "[C, C] matrix over each token's concatenated heads (a GEMM after the "
                          "attention kernel)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time salad_attn_backward (gradients of Q, K, V, X, W_p and the gate "
+                         "for a random output gradient) instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size reference for the HBM byte counters)")
@@ -157,17 +161,38 @@ def main():
     idx = torch.zeros((w.batch, w.n_heads, p.n_blocks, w.topk), dtype=torch.int32, device="cuda")
     ws = S.workspace(p)
 
-    def step():
+    def fwd():
         S.salad_attn_forward(p, dev["q"], dev["k"], dev["v"], dev["x"], dev["w_p"], dev["gate_w"],
                              inp["gate_b"], out, ws, s_out=s_out, idx_out=idx)
 
+    step = fwd
+    if args.backward:
+        if args.proj != "head":
+            sys.exit("--backward supports the per-head projection only")
+        g_out = I.to_storage(np.random.default_rng(w.seed + 77).standard_normal(
+            (w.batch, w.N, w.n_heads, w.head_dim), dtype=np.float32), w.io_dtype).cuda()
+        grads = {n: torch.empty_like(dev["q"]) for n in ("dq", "dk", "dv")}
+        dx = torch.empty_like(dev["x"])
+        dwp = torch.empty((w.head_dim, w.head_dim), dtype=torch.float32, device="cuda")
+        dgw = torch.empty(w.n_heads * w.head_dim, dtype=torch.float32, device="cuda")
+        dgb = torch.empty(1, dtype=torch.float32, device="cuda")
+        bws = S.backward_workspace(p)
+
+        def step():
+            S.salad_attn_backward(p, dev["q"], dev["k"], dev["v"], dev["x"], dev["w_p"], dev["gate_w"],
+                                  inp["gate_b"], g_out, grads["dq"], grads["dk"], grads["dv"], dwp, bws,
+                                  dx=dx, dgate_w=dgw, dgate_b=dgb)
+
+    fwd()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     pairs = pair_count(w)
     if 2 in w.head_kinds:
         pairs += topk_pairs_from_idx(w, idx.cpu().numpy())
-    flops = 4.0 * w.head_dim * pairs
+    # forward: QK^T and PV, 2 flops per multiply-add; backward: QK^T, dP,
+    # dV, dK and dQ (the algorithmic count, not counting recomputation)
+    flops = (10.0 if args.backward else 4.0) * w.head_dim * pairs
 
     S.salad_profile_enable(True)
     torch.cuda.synchronize()
@@ -198,7 +223,8 @@ def main():
             traffic = c.get("traffic_bytes_per_launch")
 
     rec = {
-        "metric": METRIC, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "metric": METRIC_BWD if args.backward else METRIC, "value": flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "ms_per_layer": ms,
@@ -206,21 +232,28 @@ def main():
                    "heads": w.n_heads, "head_dim": w.head_dim,
                    "head_kinds": "".join("STK"[k] for k in w.head_kinds),
                    "window_radius": w.window_radius, "block": w.block, "topk": w.topk,
-                   "rope": w.rope, "proj": args.proj,
+                   "rope": w.rope, "proj": args.proj, "pass": "backward" if args.backward else "forward",
                    "projection_gemm_flop": (2.0 * w.batch * w.N * (w.n_heads * w.head_dim) ** 2
                                             if args.proj == "full" else None),
                    "branch_drop_tau": args.branch_drop_tau,
                    "samples_dropped": int((s_out.cpu() < args.branch_drop_tau).sum()),
                    "computed_pairs": pairs,
                    "density": pairs / (w.batch * w.n_heads * w.N * w.N)},
-        "roofline": {"bound": "mfma", "kernel": "sparse attention (attn_bf16_kernel)",
+        "roofline": {"bound": "mfma",
+                     "kernel": ("sparse-branch gradients (attn_bwd_dq_kernel + attn_bwd_dkv_kernel)"
+                                if args.backward else "sparse attention (attn_bf16_kernel)"),
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
                      "avg_launch_ms": attn_avg, "launches": calls},
     }
     if w.io_dtype != "bf16":
         rec["dtype"] = "f32"
-    if not args.no_cpu_baseline:
+    if traffic is not None and args.backward:
+        traffic = None          # the stored counters are the forward kernel's
+    rec["roofline"]["traffic"] = traffic
+    if args.backward:
+        rec["cpu_baseline"] = None  # the oracle's backward is timed in the test suite, not here
+    elif not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w, inp, flops, args.cpu_seconds, args.proj)
     print(json.dumps(rec), flush=True)

@@ -554,10 +554,10 @@ namespace {
 // scratch (gate partials, then the linear-state and linear-backward split
 // partials, and the Top-K means and scores in between), working copies of
 // Q, K (rotated), V and dO, lse2 / D, the selection and its inverse lists,
-// fp32 dQ, dK, dV, the per-head linear state and backward matrices, the
-// gate's column sums and values, and the RoPE table.
+// the per-head linear state and backward matrices, the gate's column sums
+// and values, and the RoPE table.
 struct BwdPlan {
-  size_t wq, wk, wv, wg, lse, dsum, idx, inv_off, inv_list, dq, dk, dv, h, z;
+  size_t wq, wk, wv, wg, lse, dsum, idx, inv_off, inv_list, h, z;
   size_t mf, mb, a_red, bz, dhb, dhtb, dwp_h, ds_part, colsum, s, dt, rope_tab;
   int Np;
   size_t total;
@@ -587,9 +587,6 @@ BwdPlan bwd_plan(const Info &inf) {
   pl.idx = take(inf.any_topk ? BH * g.nb * g.k * sizeof(int32_t) : 0);
   pl.inv_off = take(inf.any_topk ? BH * (g.nb + 1) * sizeof(int32_t) : 0);
   pl.inv_list = take(inf.any_topk ? BH * g.nb * g.k * sizeof(int32_t) : 0);
-  pl.dq = take(rows * D * sizeof(float));
-  pl.dk = take(rows * D * sizeof(float));
-  pl.dv = take(rows * D * sizeof(float));
   pl.h = take(BH * D * D * sizeof(float));
   pl.z = take(BH * D * sizeof(float));
   pl.mf = take(BH * D * D * sizeof(float));
@@ -664,7 +661,6 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
          *wg = (bf16_t *)(w + pl.wg);
   float *lse = (float *)(w + pl.lse), *dsum = (float *)(w + pl.dsum);
   int32_t *idx = (int32_t *)(w + pl.idx);
-  float *gq = (float *)(w + pl.dq), *gk = (float *)(w + pl.dk), *gv = (float *)(w + pl.dv);
   float *hm = (float *)(w + pl.h), *zv = (float *)(w + pl.z);
   float *s = (float *)(w + pl.s);
   double2 *tab = inf.rope ? (double2 *)(w + pl.rope_tab) : nullptr;
@@ -699,14 +695,7 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
         (e = launch_topk_inverse(g, idx, inv_off, inv_list, stream)) != hipSuccess)
       return hip_status(e, "salad_attn_backward: block select");
   }
-  // sparse branch: normalisers and D, then dQ, dK, dV
-  if ((e = launch_attn_bwd_prep(g, qv, kv, vv, idx, wg, lse, dsum, pl.Np, stream)) != hipSuccess ||
-      (e = prof_mark(0, stream)) != hipSuccess ||
-      (e = launch_attn_bwd(g, wq, wk, wv, wg, lse, dsum, pl.Np, idx, inv_off, inv_list, gq, gk, gv,
-                           stream)) != hipSuccess ||
-      (e = prof_mark(1, stream)) != hipSuccess)
-    return hip_status(e, "salad_attn_backward: sparse attention");
-  // linear branch and projection (adds into dQ, dK, dV)
+  // linear branch and projection: whole-head sums (M, A, dZ, dH, dW_p, ds)
   LinBwdScratch lw;
   lw.mf = (float *)(w + pl.mf);
   lw.mb = (bf16_t *)(w + pl.mb);
@@ -717,20 +706,33 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
   lw.dhtb = (bf16_t *)(w + pl.dhtb);
   lw.dwp_h = (float *)(w + pl.dwp_h);
   lw.ds_part = (float *)(w + pl.ds_part);
-  if ((e = launch_linear_bwd(g, wq, wk, wv, wg, hm, zv, (const bf16_t *)w_p, s, gq, gk, gv, lw, dw_p,
-                             stream)) != hipSuccess)
+  if ((e = launch_linear_bwd(g, wq, wg, hm, zv, (const bf16_t *)w_p, s, lw, dw_p, stream)) != hipSuccess)
     return hip_status(e, "salad_attn_backward: linear branch");
+  // sparse branch (normalisers and D, then dQ and dK, dV, whose epilogues add
+  // the linear branch's per-row terms and write the final rows)
+  BwdOut bo;
+  bo.mb = lw.mb;
+  bo.dhb = lw.dhb;
+  bo.dhtb = lw.dhtb;
+  bo.zv = zv;
+  bo.dz = lw.bz;
+  bo.s_gate = s;
+  bo.rope_tab = tab;
+  bo.dq = (bf16_t *)dq;
+  bo.dk = (bf16_t *)dk;
+  bo.dv = (bf16_t *)dv;
+  if ((e = launch_attn_bwd_prep(g, qv, kv, vv, idx, wg, lse, dsum, pl.Np, stream)) != hipSuccess ||
+      (e = prof_mark(0, stream)) != hipSuccess ||
+      (e = launch_attn_bwd(g, wq, wk, wv, wg, lse, dsum, pl.Np, idx, inv_off, inv_list, bo, stream)) !=
+          hipSuccess ||
+      (e = prof_mark(1, stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_backward: sparse attention");
   // gate
   float *dt = (float *)(w + pl.dt);
   if ((e = launch_gate_bwd(g, lw.ds_part, s, has_gate, (const float *)(w + pl.colsum), dt, ds_out,
                            has_gate ? dgate_w : nullptr, has_gate ? dgate_b : nullptr, stream)) != hipSuccess ||
       (has_gate && dx && (e = launch_gate_dx(g, dt, (const bf16_t *)gate_w, (bf16_t *)dx, stream)) != hipSuccess))
     return hip_status(e, "salad_attn_backward: gate");
-  // back to the boundary layout (RoPE transposed for Q and K)
-  if ((e = launch_grad_scatter(g, gq, (bf16_t *)dq, tab, stream)) != hipSuccess ||
-      (e = launch_grad_scatter(g, gk, (bf16_t *)dk, tab, stream)) != hipSuccess ||
-      (e = launch_grad_scatter(g, gv, (bf16_t *)dv, nullptr, stream)) != hipSuccess)
-    return hip_status(e, "salad_attn_backward: scatter");
   return SALAD_OK;
 }
 

@@ -14,6 +14,12 @@
 // stored (lse2, in log2 units: P = exp2(scale log2(e) s - lse2)), so no N x N
 // matrix is kept.  The Top-K selection is held fixed.
 //
+// The epilogues finish the layer's gradient rows: they add the linear
+// branch's per-row terms (see linear_bwd.hip: dq from g M^T, den and dden;
+// dk, dv from dH and dZ, all computed on MFMA with M, dH, dH^T staged in
+// LDS), turn dQ and dK back through the transposed RoPE rotation, and store
+// bf16 rows in the token-order boundary layout.
+//
 // Two kernels, each accumulating in registers and writing every output row
 // once (no atomics, so results do not depend on scheduling):
 //   * attn_bwd_dq_kernel walks the kept key tiles of a query tile, like the
@@ -38,7 +44,7 @@ struct BwdArgs {
   const int32_t *idx;            // Top-K selection [B*H][nb][k]
   const int32_t *inv_off;        // Top-K: [B*H][nb + 1] offsets into inv_list of each key block
   const int32_t *inv_list;       // Top-K: [B*H][nb * k] selecting query blocks, ascending per key block
-  float *dq, *dk, *dv;           // working layout fp32 [B*H][N][128]
+  BwdOut out;                    // linear-branch inputs and the bf16 outputs
   int n_heads_sel;
   uint8_t heads[kMaxHeads];
   int tiles_per_head;
@@ -166,6 +172,53 @@ struct OperandOffsets {
 
 typedef __attribute__((ext_vector_type(8))) short s16x8;
 
+// (cos, sin) of the RoPE pair starting at even feature f for the token at
+// latent position (fr, y, x): the table holds one run per axis.
+__device__ __forceinline__ double2 rope_entry(const Geom &g, const double2 *tab, int fr, int y, int x, int f) {
+  const int h0 = g.rope_dims[0] >> 1, h1 = g.rope_dims[1] >> 1, h2 = g.rope_dims[2] >> 1;
+  const int d0 = g.rope_dims[0], d1 = g.rope_dims[1];
+  if (f < d0) return tab[fr * h0 + (f >> 1)];
+  if (f < d0 + d1) return tab[g.F * h0 + y * h1 + ((f - d0) >> 1)];
+  return tab[g.F * h0 + g.Hg * h1 + x * h2 + ((f - d0 - d1) >> 1)];
+}
+
+// Store gradient row values v[db][4 r4 + e] (feature 32db + 8r4 + 4hl + e)
+// of working row p of head h as bf16 at the row's token in the boundary
+// layout, rotated back by the transposed RoPE rotation when tab is set.
+__device__ __forceinline__ void store_grad_row(const Geom &g, const double2 *tab, bf16_t *dst, int b, int h,
+                                               int p, int hl, const f32x16 (&v)[4]) {
+  const int tok = bit(g.temporal, h) ? st_token(g, p) : p;
+  bf16_t *row = dst + (((long long)b * g.N + tok) * g.H + h) * kD;
+  int fr = 0, y = 0, x = 0;
+  if (tab) {
+    const int S = g.Hg * g.Wg;
+    fr = int(fdiv(g.fdS, uint32_t(tok)));
+    const int site = tok - fr * S;
+    y = int(fdiv(g.fdW, uint32_t(site)));
+    x = site - y * g.Wg;
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int f = 32 * db + 8 * r4 + 4 * hl;
+      bf16_t o[4];
+      if (tab) {
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const double2 cs = rope_entry(g, tab, fr, y, x, f + e);
+          const double g0 = double(v[db][4 * r4 + e]), g1 = double(v[db][4 * r4 + e + 1]);
+          o[e] = f64_to_bf16(g0 * cs.x + g1 * cs.y);
+          o[e + 1] = f64_to_bf16(-g0 * cs.y + g1 * cs.x);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(v[db][4 * r4 + e]);
+      }
+      *(uint2 *)(row + f) = *(const uint2 *)o;
+    }
+}
+
 // A operand of k-step kk from a transposing read of tile Ts (rows 16kk..):
 // lane -> feature 32db + l32, k index -> rows 16kk + 8r + 4hl + e.
 __device__ __forceinline__ bf16x8 tr_operand(const bf16_t *Ts, const OperandOffsets &oo, int kk, int db) {
@@ -265,11 +318,22 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bwd_dq_kernel(BwdArgs a) {
         dp[kb] = mfma_32x32x16(*(const bf16x8 *)(Vs + o), gf[ks], dp[kb]);
       }
     // dS^T = P^T (dP^T - D); key of register r of block kb:
-    // k0 + 32kb + 8(r/4) + 4hl + r%4
+    // k0 + 32kb + 8(r/4) + 4hl + r%4.  Edge tiles first set the scores of
+    // dropped pairs to -inf, so their P (and dS, as dP is finite) is 0.
+    if (!full) {
+      const int jl = k0 + 4 * hl;
+      const unsigned wb = unsigned(pq - jl + g.r);
+      const int lim = g.N - jl;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const bool keep = (c < lim) & (TOPK | (wb - unsigned(c) <= unsigned(2 * g.r)));
+          s[kb][r] = keep ? s[kb][r] : -INFINITY;
+        }
+    }
     bf16x8 dsb[4];
-    const int jl = k0 + 4 * hl;
-    const unsigned wb = unsigned(pq - jl + g.r);
-    const int lim = g.N - jl;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -278,10 +342,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
-          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
-          const bool keep = full || ((c < lim) & (TOPK | (wb - unsigned(c) <= unsigned(2 * g.r))));
           const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -lse));
-          v[e] = (__bf16)(keep ? p * (dp[kb][r] - dsv) : 0.f);
+          v[e] = (__bf16)(p * (dp[kb][r] - dsv));
         }
         dsb[2 * kb + half] = v;
       }
@@ -322,16 +384,70 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bwd_dq_kernel(BwdArgs a) {
     k_cur = k_nn;
   }
 
-  if (pq >= g.N) return;
-  float *dst = a.dq + (hrow + pq) * kD;
+  // ---- epilogue: dq = scale * (sparse) + linear-branch term, rotated back
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 v = {dq[db][4 * r4] * g.scale, dq[db][4 * r4 + 1] * g.scale,
-                       dq[db][4 * r4 + 2] * g.scale, dq[db][4 * r4 + 3] * g.scale};
-      *(f32x4 *)(dst + 32 * db + 8 * r4 + 4 * hl) = v;
+    for (int r = 0; r < 16; ++r) dq[db][r] *= g.scale;
+  const float sb = a.out.s_gate[b];
+  if (!(sb < g.drop_tau)) {
+    // gm^T = M g^T with M rows 0..63 in K0 and 64..127 in K1
+    __syncthreads();  // every wave is done with the key tiles
+    const bf16_t *mh = a.out.mb + (long long)bh * kD * kD;
+    dma.issue(mh, 0, kD, K0, w);
+    dma.issue(mh, 64, kD, K1, w);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    // one d-block of gm^T at a time (16 registers): a first pass forms
+    // den = relu(q) . Z + eps and t = relu(q) . gm over this lane's 64
+    // features and the other half-wave's (same query), a second pass
+    // recomputes the block and adds the term
+    const float *zr = a.out.zv + (long long)bh * kD;
+    const bf16_t *qrow = a.q + (hrow + pqc) * kD;
+    auto gm_block = [&](int db) __attribute__((always_inline)) {
+      const bf16_t *ms = (db < 2 ? K0 : K1) + (db & 1) * 32 * kD;
+      f32x16 r = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) r = mfma_32x32x16(*(const bf16x8 *)(ms + oo.k_lane + 16 * (ks ^ oo.k_x)), gf[ks], r);
+      return r;
+    };
+    float tp = 0.f, dp = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const f32x16 gm = gm_block(db);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int f = 32 * db + 8 * r4 + 4 * hl;
+        const bf16x4 q4 = *(const bf16x4 *)(qrow + f);
+        const f32x4 z4 = *(const f32x4 *)(zr + f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float av = fmaxf(float(q4[e]), 0.f);
+          tp = fmaf(av, gm[4 * r4 + e], tp);
+          dp = fmaf(av, z4[e], dp);
+        }
+      }
     }
+    tp += __shfl_xor(tp, 32);
+    dp += __shfl_xor(dp, 32);
+    const float den = dp + g.eps;
+    const float dden = -sb * tp / (den * den), cq = sb / den;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const f32x16 gm = gm_block(db);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int f = 32 * db + 8 * r4 + 4 * hl;
+        const bf16x4 q4 = *(const bf16x4 *)(qrow + f);
+        const f32x4 z4 = *(const f32x4 *)(zr + f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (float(q4[e]) > 0.f) dq[db][4 * r4 + e] += fmaf(cq, gm[4 * r4 + e], dden * z4[e]);
+      }
+    }
+  }
+  if (pq >= g.N) return;
+  store_grad_row(g, a.out.rope_tab, a.out.dq, b, h, pq, hl, dq);
 }
 
 // ---------------------------------------------------------------------------
@@ -432,23 +548,33 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
         s = mfma_32x32x16(*(const bf16x8 *)(Qs + o), kf[ks], s);
         dp = mfma_32x32x16(*(const bf16x8 *)(Gs + o), vf[ks], dp);
       }
-      // query of register r: i0 + 8(r/4) + 4hl + r%4
+      // query of register r: i0 + 8(r/4) + 4hl + r%4.  Edge blocks first
+      // set the scores of dropped pairs to -inf (P = 0); rows past N also
+      // get D = 0, as their lse2 / D slots hold no values
       bf16x8 pb[2], dsb[2];
       const unsigned wb = unsigned(i0 + 4 * hl - pk + g.r);  // i - pk + r = wb + c
       const int lim = g.N - i0 - 4 * hl;                    // i < N  <=>  c < lim
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const f32x4 lv = *(const f32x4 *)(Ls + 32 * qs + 8 * m + 4 * hl);
-        const f32x4 dv4 = *(const f32x4 *)(Ds + 32 * qs + 8 * m + 4 * hl);
+        f32x4 lv = *(const f32x4 *)(Ls + 32 * qs + 8 * m + 4 * hl);
+        f32x4 dv4 = *(const f32x4 *)(Ds + 32 * qs + 8 * m + 4 * hl);
+        if (!full) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * m + e, c = 8 * m + e;
+            const bool valid = c < lim;
+            const bool keep = valid & (TOPK | (wb + unsigned(c) <= unsigned(2 * g.r)));
+            s[r] = keep ? s[r] : -INFINITY;
+            lv[e] = valid ? lv[e] : 0.f;
+            dv4[e] = valid ? dv4[e] : 0.f;
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 4 * m + e, c = 8 * m + e;
-          const bool keep = full || ((c < lim) & (TOPK | (wb + unsigned(c) <= unsigned(2 * g.r))));
+          const int r = 4 * m + e;
           const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lv[e]));
-          const float pk_ = keep ? p : 0.f;
-          const float dsv = keep ? p * (dp[r] - dv4[e]) : 0.f;
-          pb[r >> 3][r & 7] = (__bf16)pk_;
-          dsb[r >> 3][r & 7] = (__bf16)dsv;
+          pb[r >> 3][r & 7] = (__bf16)p;
+          dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dv4[e]));
         }
       }
       // dV^T[d][keys] += dO^T[d][q] P[q][keys];  dK^T += Q^T dS
@@ -486,18 +612,56 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
     q_cur = q_nn;
   }
 
-  if (pk >= g.N) return;
-  float *dkr = a.dk + (hrow + pk) * kD, *dvr = a.dv + (hrow + pk) * kD;
+  // ---- epilogue: dk = scale * (sparse) + (dH v + dZ) [k > 0],
+  //      dv = (sparse) + dH^T relu(k); dk rotated back
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 kv4 = {dk[db][4 * r4] * g.scale, dk[db][4 * r4 + 1] * g.scale,
-                         dk[db][4 * r4 + 2] * g.scale, dk[db][4 * r4 + 3] * g.scale};
-      const f32x4 vv4 = {dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
-      *(f32x4 *)(dkr + 32 * db + 8 * r4 + 4 * hl) = kv4;
-      *(f32x4 *)(dvr + 32 * db + 8 * r4 + 4 * hl) = vv4;
+    for (int r = 0; r < 16; ++r) dk[db][r] *= g.scale;
+  if (!(a.out.s_gate[b] < g.drop_tau)) {
+    // dH rows 0..63 in Q0, 64..127 in Q1; dH^T rows likewise in G0, G1
+    __syncthreads();  // every wave is done with the query tiles
+    const long long hm_off = (long long)bh * kD * kD;
+    dma.issue(a.out.dhb + hm_off, 0, kD, Q0, w);
+    dma.issue(a.out.dhb + hm_off, 64, kD, Q1, w);
+    dma.issue(a.out.dhtb + hm_off, 0, kD, G0, w);
+    dma.issue(a.out.dhtb + hm_off, 64, kD, G1, w);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    // dv^T[j][key] += sum_i dH^T[j][i] relu(k)[i]
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      bf16x8 kr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kr[e] = float(kf[ks][e]) > 0.f ? kf[ks][e] : (__bf16)0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16_t *ht = (db < 2 ? G0 : G1) + (db & 1) * 32 * kD;
+        dv[db] = mfma_32x32x16(*(const bf16x8 *)(ht + oo.k_lane + 16 * (ks ^ oo.k_x)), kr, dv[db]);
+      }
     }
+    // dk^T[i][key] += ([k_i > 0] (sum_j dH[i][j] v[j] + dZ[i])), one d-block at a time
+    const float *dz = a.out.dz + (long long)bh * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      f32x16 lk = f32x16{};
+      const bf16_t *hs = (db < 2 ? Q0 : Q1) + (db & 1) * 32 * kD;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) lk = mfma_32x32x16(*(const bf16x8 *)(hs + oo.k_lane + 16 * (ks ^ oo.k_x)), vf[ks], lk);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int f = 32 * db + 8 * r4 + 4 * hl;
+        const bf16x4 k4 = *(const bf16x4 *)(a.k + (hrow + pkc) * kD + f);
+        const f32x4 z4 = *(const f32x4 *)(dz + f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (float(k4[e]) > 0.f) dk[db][4 * r4 + e] += lk[4 * r4 + e] + z4[e];
+      }
+    }
+  }
+  if (pk >= g.N) return;
+  store_grad_row(g, a.out.rope_tab, a.out.dk, b, h, pk, hl, dk);
+  store_grad_row(g, nullptr, a.out.dv, b, h, pk, hl, dv);
 }
 
 // ---------------------------------------------------------------------------
@@ -516,7 +680,7 @@ hipError_t launch_topk_inverse(const Geom &g, const int32_t *idx, int32_t *off, 
 hipError_t launch_attn_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, const bf16_t *v,
                            const bf16_t *go, const float *lse2, const float *dsum, int Np,
                            const int32_t *idx, const int32_t *inv_off, const int32_t *inv_list,
-                           float *dq, float *dk, float *dv, hipStream_t st) {
+                           const BwdOut &out, hipStream_t st) {
   if (g.D != kD) return hipErrorInvalidValue;
   BwdArgs a = {};
   a.g = g;
@@ -530,9 +694,7 @@ hipError_t launch_attn_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, cons
   a.idx = idx;
   a.inv_off = inv_off;
   a.inv_list = inv_list;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
+  a.out = out;
   for (int mode = 0; mode < 2; ++mode) {
     a.n_heads_sel = 0;
     for (int h = 0; h < g.H; ++h) {

@@ -86,12 +86,6 @@ hipError_t launch_linear_reduce(const Geom &g, int S, const float *partial, floa
 // selecting query blocks in list [B*H][nb * k]).
 hipError_t launch_topk_inverse(const Geom &g, const int32_t *idx, int32_t *off, int32_t *list,
                                hipStream_t st);
-// Sparse-branch gradients into dq, dk, dv (fp32, working layout; written,
-// not accumulated).  lse2 / dsum rows are Np apart per head.
-hipError_t launch_attn_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, const bf16_t *v,
-                           const bf16_t *go, const float *lse2, const float *dsum, int Np,
-                           const int32_t *idx, const int32_t *inv_off, const int32_t *inv_list,
-                           float *dq, float *dk, float *dv, hipStream_t st);
 // Scratch of the linear-branch backward (sizes per B*H heads, d = 128):
 // mf [D*D] fp32, mb [D*D] bf16, partial [S][D*D + D] fp32 (S =
 // linear_splits), a_red [D*D] and bz [D] fp32, dhb, dhtb [D*D] bf16,
@@ -103,17 +97,28 @@ struct LinBwdScratch {
   bf16_t *dhb, *dhtb;
   float *dwp_h, *ds_part;
 };
-// Linear-branch and projection gradients: adds into dq, dk, dv (which must
-// hold the sparse-branch gradients), writes dw_p [d][d] and ws.ds_part
-// (16 partial sums of dL/ds per head; zero for dropped samples).
-hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, const bf16_t *v,
-                             const bf16_t *go, const float *hm, const float *zv, const bf16_t *w_p,
-                             const float *s_gate, float *dq, float *dk, float *dv, const LinBwdScratch &w,
-                             float *dw_p, hipStream_t st);
-// fp32 working-layout gradient rows -> io boundary layout [B,N,H,d], turned
-// back by the transposed RoPE rotation when table is non-NULL.
-hipError_t launch_grad_scatter(const Geom &g, const float *src, bf16_t *dst, const double2 *table,
-                               hipStream_t st);
+// Linear-branch and projection gradients that need whole-head sums: M = H
+// W_p (mb), A and Bz = dZ (bz), dH and dH^T (dhb, dhtb), dw_p [d][d] and
+// ws.ds_part (16 partial sums of dL/ds per head; zero for dropped samples).
+hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *go, const float *hm,
+                             const float *zv, const bf16_t *w_p, const float *s_gate,
+                             const LinBwdScratch &w, float *dw_p, hipStream_t st);
+// dQ, dK, dV rows (bf16, boundary layout [B,N,H,d]) of the whole layer: the
+// sparse branch's gradients plus, in the epilogues, the linear branch's per
+// row terms (from M, Z, dH, dH^T, dZ and s; none for dropped samples) and
+// the transposed RoPE rotation of dQ and dK (table non-NULL).  lse2 / dsum
+// rows are Np apart per head.
+struct BwdOut {
+  const bf16_t *mb, *dhb, *dhtb;  // [B*H][128][128] bf16
+  const float *zv, *dz;           // [B*H][128]
+  const float *s_gate;            // [B]
+  const double2 *rope_tab;        // NULL: no RoPE
+  bf16_t *dq, *dk, *dv;           // boundary layout
+};
+hipError_t launch_attn_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, const bf16_t *v,
+                           const bf16_t *go, const float *lse2, const float *dsum, int Np,
+                           const int32_t *idx, const int32_t *inv_off, const int32_t *inv_list,
+                           const BwdOut &out, hipStream_t st);
 // Gate backward.  colsum: partial column sums of X [B][splits][C] fp32;
 // final: ds_b = sum of the heads' partials, dt_b = ds_b s_b (1 - s_b) (0 for
 // dropped samples or with s_override), dgate_w, dgate_b, optional ds_out;

@@ -14,11 +14,13 @@
 //   dk_n += (dH v_n + dZ) * [k_n > 0],   dv_n += dH^T relu(k_n).
 // A sample whose branch is dropped (s_b < drop_tau) is skipped throughout.
 //
-// Kernels: lin_bwd_prep (M per head), lin_bwd_rows (gm, dq, and split-N
-// partial sums of A and Bz on MFMA), the split reduction (the forward's
-// linear_reduce_kernel), lin_bwd_head (dH, dH^T as bf16, per-head dW_p and
-// <M, A>), lin_bwd_kv (dk, dv on MFMA) and lin_bwd_wp (dW_p summed over
-// heads in a fixed order).
+// Kernels here: lin_bwd_prep (M per head), lin_bwd_rows (gm and the
+// split-N partial sums of A and Bz on MFMA), the split reduction (the
+// forward's linear_reduce_kernel), lin_bwd_head (dH, dH^T as bf16, per-head
+// dW_p and <M, A>) and lin_bwd_wp (dW_p summed over heads in a fixed
+// order).  They run before the sparse-branch gradient kernels, whose
+// epilogues add the per-row terms (dq from gm, den and dden; dk, dv from
+// dH and dZ), so no gradient row is written twice.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_util.h"
@@ -84,11 +86,11 @@ __global__ void __launch_bounds__(256) lin_bwd_prep_kernel(Geom g, const float *
   }
 }
 
-// Per row gm, dq and the split-N partials of A (128 x 128) and Bz (128).
+// Per row gm and the split-N partials of A (128 x 128) and Bz (128).
 // Grid (S, B*H), 256 threads; split s covers rows [s*chunk, (s+1)*chunk).
 // A step handles 128 rows: wave w owns rows 32w + l32 (one per lane column)
-// for gm^T = M g^T on MFMA (M rows from LDS, g rows as B operands), the dot
-// products and dq; it then leaves a_n / den_n and g_n (bf16) in LDS, and
+// for gm^T = M g^T on MFMA (M rows from LDS, g rows as B operands) and the
+// dot products; it then leaves a_n / den_n and g_n (bf16) in LDS, and
 // each wave adds its 64 x 64 quadrant of A over the 128 rows with
 // transposing reads.  Fixed order throughout.
 __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16_t *__restrict__ q,
@@ -96,7 +98,6 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
                                                               const bf16_t *__restrict__ mb,
                                                               const float *__restrict__ zv,
                                                               const float *__restrict__ s_gate,
-                                                              float *__restrict__ dq,
                                                               float *__restrict__ partial, int S, int chunk) {
   constexpr int TT = 128;
   __shared__ __attribute__((aligned(1024))) bf16_t Ms[D * D];
@@ -178,25 +179,15 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
     dp += __shfl_xor(dp, 32);
     const float den = dp + g.eps;
     const float dden = -sb * tp / (den * den);
-    const float cq = sb / den, inv_den = 1.f / den;
+    const float inv_den = 1.f / den;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int f = 32 * db + 8 * r4 + 4 * hl;
-        const f32x4 z4 = *(const f32x4 *)(Zs + f);
         bf16x4 ap;
-        f32x4 add;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float qx = float(qv[db][r4][e]);
-          ap[e] = (__bf16)(valid ? fmaxf(qx, 0.f) * inv_den : 0.f);
-          add[e] = qx > 0.f ? fmaf(cq, gm[db][4 * r4 + e], dden * z4[e]) : 0.f;
-        }
-        if (valid) {
-          f32x4 *dst = (f32x4 *)(dq + (hrow + n) * D + f);
-          *dst = *dst + add;
-        }
+        for (int e = 0; e < 4; ++e) ap[e] = (__bf16)(valid ? fmaxf(float(qv[db][r4][e]), 0.f) * inv_den : 0.f);
         *(bf16x4 *)(At + rl * D + (((f >> 3) ^ kv_swz(rl)) << 3) + (f & 4)) = ap;
       }
 #pragma unroll
@@ -321,80 +312,6 @@ __global__ void __launch_bounds__(256) lin_bwd_head_kernel(Geom g, const float *
   if (t == 0) ds_part[bh * 16 + blk] = red[0];
 }
 
-// dk += (dH v + dZ) * [k > 0], dv += dH^T relu(k), per row on MFMA.  Grid
-// (S, B*H); wave w owns rows 32w + l32 of each 128-row step (one row per
-// lane column); dH and dH^T rows come from LDS, v and relu(k) rows are the
-// B operands.
-__global__ void __launch_bounds__(256, 1) lin_bwd_kv_kernel(Geom g, const bf16_t *__restrict__ k,
-                                                            const bf16_t *__restrict__ v,
-                                                            const bf16_t *__restrict__ dhb,
-                                                            const bf16_t *__restrict__ dhtb,
-                                                            const float *__restrict__ dz,
-                                                            const float *__restrict__ s_gate,
-                                                            float *__restrict__ dk, float *__restrict__ dv,
-                                                            int chunk) {
-  __shared__ __attribute__((aligned(1024))) bf16_t Hs[D * D];
-  __shared__ __attribute__((aligned(1024))) bf16_t Ht[D * D];
-  __shared__ __attribute__((aligned(16))) float Zs[D];
-  const int s = blockIdx.x, bh = blockIdx.y, b = bh / g.H;
-  const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, l32 = lane & 31;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  if (dropped(g, s_gate, b)) return;
-  const int n0 = s * chunk, n1 = min(g.N, n0 + chunk);
-  const long long hrow = (long long)bh * g.N;
-  stage_swizzled(Hs, dhb + (long long)bh * D * D, t);
-  stage_swizzled(Ht, dhtb + (long long)bh * D * D, t);
-  if (t < D) Zs[t] = dz[(long long)bh * D + t];
-  RowOp ro;
-  ro.init(lane);
-  __syncthreads();
-  for (int base = n0; base < n1; base += 128) {
-    const int n = base + 32 * w + l32;
-    const bool valid = n < n1;
-    const int nc = valid ? n : n0;
-    bf16x8 vf[8], kf[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      vf[ks] = *(const bf16x8 *)(v + (hrow + nc) * D + (2 * ks + hl) * 8);
-      const bf16x8 kr = *(const bf16x8 *)(k + (hrow + nc) * D + (2 * ks + hl) * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[ks][e] = float(kr[e]) > 0.f ? kr[e] : (__bf16)0.f;
-    }
-    f32x16 ak[4], av[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      ak[db] = f32x16{};
-      av[db] = f32x16{};
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        ak[db] = mfma_32x32x16(*(const bf16x8 *)(Hs + ro.at(db, ks)), vf[ks], ak[db]);
-        av[db] = mfma_32x32x16(*(const bf16x8 *)(Ht + ro.at(db, ks)), kf[ks], av[db]);
-      }
-    if (!valid) continue;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int f = 32 * db + 8 * r4 + 4 * hl;
-        const bf16x4 k4 = *(const bf16x4 *)(k + (hrow + n) * D + f);
-        const f32x4 z4 = *(const f32x4 *)(Zs + f);
-        f32x4 addk, addv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          addk[e] = float(k4[e]) > 0.f ? ak[db][4 * r4 + e] + z4[e] : 0.f;
-          addv[e] = av[db][4 * r4 + e];
-        }
-        f32x4 *pk = (f32x4 *)(dk + (hrow + n) * D + f);
-        f32x4 *pv = (f32x4 *)(dv + (hrow + n) * D + f);
-        *pk = *pk + addk;
-        *pv = *pv + addv;
-      }
-  }
-}
-
 // dW_p = sum over (b, h) of the heads' s H^T A, in head order.
 __global__ void __launch_bounds__(256) lin_bwd_wp_kernel(int BH, const float *__restrict__ dwp_h,
                                                          float *__restrict__ dw_p) {
@@ -405,22 +322,20 @@ __global__ void __launch_bounds__(256) lin_bwd_wp_kernel(int BH, const float *__
   dw_p[e] = acc;
 }
 
-hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, const bf16_t *v,
-                             const bf16_t *go, const float *hm, const float *zv, const bf16_t *w_p,
-                             const float *s_gate, float *dq, float *dk, float *dv, const LinBwdScratch &w,
-                             float *dw_p, hipStream_t st) {
+hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *go, const float *hm,
+                             const float *zv, const bf16_t *w_p, const float *s_gate,
+                             const LinBwdScratch &w, float *dw_p, hipStream_t st) {
   if (g.D != D) return hipErrorInvalidValue;
   const int BH = g.B * g.H;
   const int S = linear_splits(g);
   int chunk = (g.N + S - 1) / S;
   chunk = (chunk + 127) / 128 * 128;
   lin_bwd_prep_kernel<<<dim3(16, BH), 256, 0, st>>>(g, hm, w_p, s_gate, w.mf, w.mb);
-  lin_bwd_rows_kernel<<<dim3(S, BH), 256, 0, st>>>(g, q, go, w.mb, zv, s_gate, dq, w.partial, S, chunk);
+  lin_bwd_rows_kernel<<<dim3(S, BH), 256, 0, st>>>(g, q, go, w.mb, zv, s_gate, w.partial, S, chunk);
   hipError_t e = launch_linear_reduce(g, S, w.partial, w.a_red, w.bz, st);
   if (e != hipSuccess) return e;
   lin_bwd_head_kernel<<<dim3(16, BH), 256, 0, st>>>(g, w.a_red, hm, w.mf, w_p, s_gate, w.dhb, w.dhtb,
                                                     w.dwp_h, w.ds_part);
-  lin_bwd_kv_kernel<<<dim3(S, BH), 256, 0, st>>>(g, k, v, w.dhb, w.dhtb, w.bz, s_gate, dk, dv, chunk);
   lin_bwd_wp_kernel<<<(D * D + 255) / 256, 256, 0, st>>>(BH, w.dwp_h, dw_p);
   return hipGetLastError();
 }
