@@ -34,7 +34,7 @@ from . import salad_oracle as F
 
 __all__ = [
     "rope_3d_transpose", "sparse_attention_backward", "sparse_attention_head_backward",
-    "linear_backward", "gate_backward", "attn_backward",
+    "linear_backward", "gate_backward", "attn_backward", "attn_backward_rows",
 ]
 
 
@@ -242,3 +242,144 @@ def attn_backward(q, k, v, x, w_p, gate_w, gate_b, dout, *, grid, head_kinds, wi
             dgate_b += dbb
     return {"dq": dq, "dk": dk, "dv": dv, "dx": dx, "dw_p": dw_p, "dgate_w": dgate_w,
             "dgate_b": dgate_b, "ds": ds, "s": s}
+
+
+def attn_backward_rows(q, k, v, x, w_p, gate_w, gate_b, dout, *, rows_q=(), rows_kv=(), grid,
+                       head_kinds, window_radius, block, topk, io_dtype="bf16", rope=False,
+                       rope_dims=(44, 42, 42), rope_base=10000.0, softmax_scale=None,
+                       linear_eps=1e-6, s_override=None, drop_tau=0.0):
+    """Selected rows of ``attn_backward`` for layers too large to
+    differentiate whole: dQ at the (b, n, h) triples of ``rows_q``, dK and
+    dV at those of ``rows_kv``, and the whole-layer dW_p, dgate_w, dgate_b
+    and ds (their sums over tokens cost one pass over each head).
+
+    The same formulas as ``attn_backward``, evaluated where needed: a dQ row
+    needs only its query's kept keys; a dK / dV row of key j needs every
+    query i whose kept set holds j (the window is symmetric, so for window
+    heads those are the queries within r of j; for Top-K heads the rows of
+    the query blocks that selected j's block), each with its full softmax
+    row and D_i.  The linear branch's per-row terms use the head's sums
+    A = sum_n (a_n / den_n)^T g_n and Bz = sum_n dden_n a_n (see
+    ``linear_backward``, written here through M = H W_p).  Inputs may be
+    float32 arrays holding the storage values; each head is widened to
+    float64 when first used.  Returns a dict with "dq", "dk", "dv" (dicts
+    keyed by triple), "dw_p", "dgate_w", "dgate_b", "ds" and "s"."""
+    Fr, Hg, Wg = grid
+    B, N, H, d = np.shape(q)
+    scale = 1.0 / np.sqrt(d) if not softmax_scale or softmax_scale <= 0 else softmax_scale
+    w_p = np.asarray(w_p, np.float64)
+    gate_w = np.asarray(gate_w, np.float64)
+    s = np.empty(B)
+    for b in range(B):
+        s[b] = F.gate(np.asarray(x[b], np.float64), gate_w, gate_b) if s_override is None \
+            else float(s_override[b])
+    kept = [F.branch_kept(s[b], drop_tau) for b in range(B)]
+    cache = {}
+
+    def head(b, h):
+        """Token-order q, k (rotated and rounded as the forward), v, g, the
+        working order, the selection and the linear branch's head sums."""
+        key = (b, h)
+        if key in cache:
+            return cache[key]
+        qh = np.asarray(q[b:b + 1, :, h:h + 1], np.float64)
+        kh = np.asarray(k[b:b + 1, :, h:h + 1], np.float64)
+        if rope:
+            qh = F.round_to_io(F.rope_3d(qh, Fr, Hg, Wg, rope_dims, rope_base), io_dtype)
+            kh = F.round_to_io(F.rope_3d(kh, Fr, Hg, Wg, rope_dims, rope_base), io_dtype)
+        qh, kh = qh[0, :, 0], kh[0, :, 0]
+        vh = np.asarray(v[b, :, h], np.float64)
+        gh = np.asarray(dout[b, :, h], np.float64)
+        kind = int(head_kinds[h])
+        order = F.head_order(kind, Fr, Hg, Wg)
+        c = dict(q=qh, k=kh, v=vh, g=gh, kind=kind, order=order, pos=np.argsort(order),
+                 qw=qh[order], kw=kh[order], vw=vh[order], gw=gh[order], idx=None)
+        if kind == F.HEAD_TOPK:
+            c["idx"] = F.topk_blocks(F.block_means(c["qw"], block), F.block_means(c["kw"], block), topk)
+        Hm, Zv = F.linear_state(kh, vh)
+        M = Hm @ w_p
+        a = np.maximum(qh, 0.0)
+        den = a @ Zv + linear_eps
+        gm = gh @ M.T
+        dden = -s[b] * np.sum(a * gm, axis=1) / den ** 2
+        A = (a / den[:, None]).T @ gh
+        c.update(H=Hm, Z=Zv, M=M, den=den, gm=gm, dden=dden, A=A, Bz=a.T @ dden,
+                 dH=s[b] * (A @ w_p.T))
+        cache[key] = c
+        return c
+
+    def keys_of(c, p):
+        if c["kind"] == F.HEAD_TOPK:
+            return F.topk_keys(p, c["idx"], block, N)
+        return F.swa_keys(p, N, window_radius)
+
+    def queries_of(c, j):
+        if c["kind"] == F.HEAD_TOPK:
+            kb = j // block
+            qbs = [qb for qb in range(c["idx"].shape[0]) if kb in set(int(t) for t in c["idx"][qb])]
+            if not qbs:
+                return np.zeros(0, dtype=np.int64)
+            return np.concatenate([np.arange(qb * block, min(N, (qb + 1) * block)) for qb in qbs])
+        return F.swa_keys(j, N, window_radius)   # |i - j| <= r is symmetric
+
+    def softmax_row(c, p):
+        J = keys_of(c, p)
+        lg = scale * (c["kw"][J] @ c["qw"][p])
+        e = np.exp(lg - lg.max())
+        P = e / e.sum()
+        dP = c["vw"][J] @ c["gw"][p]
+        return J, P, dP, P @ dP
+
+    def rotate_back(row, n):
+        if not rope:
+            return row
+        g = np.zeros((1, N, 1, d))
+        g[0, n, 0] = row
+        return rope_3d_transpose(g, Fr, Hg, Wg, rope_dims, rope_base)[0, n, 0]
+
+    out = {"dq": {}, "dk": {}, "dv": {}}
+    for (b, n, h) in rows_q:
+        c = head(b, h)
+        p = int(c["pos"][n])
+        J, P, dP, D = softmax_row(c, p)
+        row = scale * ((P * (dP - D)) @ c["kw"][J])
+        if kept[b]:
+            row = row + ((s[b] / c["den"][n]) * c["gm"][n] + c["dden"][n] * c["Z"]) * (c["q"][n] > 0)
+        out["dq"][(b, n, h)] = rotate_back(row, n)
+    for (b, n, h) in rows_kv:
+        c = head(b, h)
+        j = int(c["pos"][n])
+        dk = np.zeros(d)
+        dv = np.zeros(v.shape[3])
+        for i in queries_of(c, j):
+            J, P, dP, D = softmax_row(c, int(i))
+            t = np.searchsorted(J, j)
+            if t >= len(J) or J[t] != j:
+                continue
+            dv += P[t] * c["gw"][i]
+            dk += scale * P[t] * (dP[t] - D) * c["qw"][i]
+        if kept[b]:
+            dk = dk + (c["dH"] @ c["v"][n] + c["Bz"]) * (c["k"][n] > 0)
+            dv = dv + c["dH"].T @ np.maximum(c["k"][n], 0.0)
+        out["dk"][(b, n, h)] = rotate_back(dk, n)
+        out["dv"][(b, n, h)] = dv
+
+    dw_p = np.zeros_like(w_p)
+    ds = np.zeros(B)
+    for b in range(B):
+        if not kept[b]:
+            continue
+        for h in range(H):
+            c = head(b, h)
+            dw_p += s[b] * (c["H"].T @ c["A"])
+            ds[b] += float(np.sum(c["M"] * c["A"]))
+            del cache[(b, h)]
+    dgate_w = np.zeros_like(gate_w)
+    dgate_b = 0.0
+    if s_override is None:
+        for b in range(B):
+            dt = ds[b] * s[b] * (1.0 - s[b])
+            dgate_w += dt * np.asarray(x[b], np.float64).mean(axis=0)
+            dgate_b += dt
+    out.update(dw_p=dw_p, dgate_w=dgate_w, dgate_b=dgate_b, ds=ds, s=s)
+    return out

@@ -119,3 +119,55 @@ def test_backward_is_deterministic():
     b = run_backward(w, inp, dout)
     for n in ("dq", "dk", "dv", "dx", "dw_p", "dgate_w", "ds"):
         assert np.array_equal(a[n], b[n]), n
+
+
+# ---- full workload sizes: sampled rows --------------------------------------
+
+def _sample(w, n_q, n_kv, seed):
+    """(b, n, h) rows at sequence edges and window-tile boundaries of each
+    head kind, plus random rows."""
+    rng = np.random.default_rng(seed)
+    kinds = {}
+    for h, kd in enumerate(w.head_kinds):
+        kinds.setdefault(kd, []).append(h)
+    edge = []
+    for kd, hs in sorted(kinds.items()):
+        order = O.head_order(kd, *w.grid)
+        for p in (0, 127, w.N - 1):
+            edge.append((int(rng.integers(w.batch)), int(order[p]), int(rng.choice(hs))))
+    rand = [(int(rng.integers(w.batch)), int(rng.integers(w.N)), int(rng.integers(w.n_heads)))
+            for _ in range(max(n_q, n_kv))]
+    return sorted(set(edge + rand[:n_q])), sorted(set(edge[:len(kinds)] + rand[:n_kv]))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["480p-stswa-h12", "480p-topk-h40", "480p-cfg-rope-mixed-h40"])
+def test_backward_full_size_sampled_rows(name):
+    """The bench workloads at full size, through salad_attn_backward as
+    bench.py --backward runs it: sampled dQ rows and dK / dV rows, and the
+    whole-layer dW_p, dw, db and ds, against the oracle's rows form."""
+    w = C.all_workloads()[name]
+    inp = I.make_inputs(w)
+    dout = _dout(w)
+    got = run_backward(w, inp, dout)
+    rows_q, rows_kv = _sample(w, 10, 4, seed=11)
+    args = [inp[n].float().numpy() for n in ("q", "k", "v", "x")] + \
+        [I.as_f64(inp[n]) for n in ("w_p", "gate_w")]
+    ref = O.attn_backward_rows(*args, inp["gate_b"], dout.float().numpy(), rows_q=rows_q, rows_kv=rows_kv,
+                               **oracle_kwargs(w))
+    res = []
+    for n, rows in (("dq", rows_q), ("dk", rows_kv), ("dv", rows_kv)):
+        g_ = np.stack([got[n][b, t, h] for (b, t, h) in rows])
+        r_ = np.stack([ref[n][key] for key in rows])
+        res.append((n,) + assert_rel(g_, r_, f"{name}: {n} rows"))
+    for n in ("dw_p", "dgate_w", "ds"):
+        res.append((n,) + assert_rel(got[n], ref[n], f"{name}: {n}"))
+    assert abs(got["dgate_b"] - ref["dgate_b"]) <= MAX_REL * abs(ref["dgate_b"]) + 1e-7
+    # dX is dt_b w / N on every token: check two rows
+    for b in range(w.batch):
+        dt = ref["ds"][b] * ref["s"][b] * (1.0 - ref["s"][b])
+        exp_row = dt * I.as_f64(inp["gate_w"]) / w.N
+        for t in (0, w.N - 1):
+            assert_rel(got["dx"][b, t], exp_row, f"{name}: dx row")
+    print(name, " ".join(f"{n} {m:.2g}/{f:.2g}" for n, m, f in res))

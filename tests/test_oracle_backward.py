@@ -136,3 +136,29 @@ def test_sparse_gradients_match_torch_autograd_with_zero_projection():
             np.testing.assert_allclose(g["dv"][b, order, h], vt.grad.numpy(), atol=1e-12)
     # W_p = 0: the gate's output does not reach the layer, so no gradient reaches it
     assert np.all(g["ds"] == 0.0) and np.all(g["dx"] == 0.0)
+
+
+@pytest.mark.parametrize("rope,drop", [(False, False), (True, False), (True, True)])
+def test_rows_mode_equals_full_backward(rope, drop):
+    """The rows form (used at full workload sizes) gives the full form's
+    rows and whole-layer gradients."""
+    inp, G, kw = _problem(rope, seed=8)
+    extra = {}
+    if drop:
+        s = np.array([O.gate(inp["x"][b], inp["gate_w"], inp["gate_b"]) for b in range(2)])
+        extra["drop_tau"] = float(s.mean())
+    args = [inp[n] for n in ("q", "k", "v", "x", "w_p", "gate_w")] + [inp["gate_b"], G]
+    full = O.attn_backward(*args, **kw, **extra)
+    rng = np.random.default_rng(9)
+    B, N, H, _ = inp["q"].shape
+    rows = sorted({(int(rng.integers(B)), int(rng.integers(N)), int(rng.integers(H))) for _ in range(12)}
+                  | {(0, 0, 2), (1, N - 1, 1), (0, 7, 0)})
+    part = O.attn_backward_rows(*args, rows_q=rows, rows_kv=rows, **kw, **extra)
+    for key in rows:
+        b, n, h = key
+        np.testing.assert_allclose(part["dq"][key], full["dq"][b, n, h], atol=1e-12)
+        np.testing.assert_allclose(part["dk"][key], full["dk"][b, n, h], atol=1e-12)
+        np.testing.assert_allclose(part["dv"][key], full["dv"][b, n, h], atol=1e-12)
+    for name in ("dw_p", "dgate_w", "ds"):
+        np.testing.assert_allclose(part[name], full[name], atol=1e-12)
+    assert abs(part["dgate_b"] - full["dgate_b"]) <= 1e-12
