@@ -42,6 +42,7 @@ __all__ = [
     "swa_keys", "topk_keys", "sparse_attention", "sparse_attention_head",
     "linear_state", "linear_apply", "gate", "combine", "combine_full", "output_projection",
     "swa_pair_count", "topk_pair_count", "branch_kept", "attn_forward",
+    "dense_attention", "window_errors", "calibrate_windows",
 ]
 
 HEAD_SPATIAL = 0
@@ -489,3 +490,63 @@ def attn_forward(q, k, v, x, w_p, gate_w, gate_b, *, grid, head_kinds,
             out[b] = output_projection(out[b].reshape(N, H * dv), w_o).reshape(N, H, dv)
     return {"out": out, "o_s": o_s_all, "o_l": o_l_all, "H": Hs, "Z": Zs, "s": s,
             "idx": idx_all, "orders": orders, "q_used": q_used, "k_used": k_used}
+
+
+# --------------------------------------------------------------------------
+# Per-head window calibration  ([I] 1.1)
+# --------------------------------------------------------------------------
+
+def dense_attention(qw, kw, vw, scale: float) -> np.ndarray:
+    """Full softmax attention of every query over every key (the reference
+    the window is calibrated against): one row at a time, as
+    ``sparse_attention`` with every key kept."""
+    N = np.shape(qw)[0]
+    return sparse_attention(qw, kw, vw, lambda p: np.arange(N, dtype=np.int64), scale)
+
+
+def window_errors(qw, kw, vw, radii, scale: float) -> np.ndarray:
+    """Relative squared error of window attention against dense attention
+    for one working-order head, per radius:
+    e(r) = ||O_window(r) - O_dense||_F^2 / ||O_dense||_F^2 over all the head's
+    rows ([I] 1.1 scores a window by a relative squared error against full
+    attention; reading: Frobenius norms over the head's tokens)."""
+    od = dense_attention(qw, kw, vw, scale)
+    N = od.shape[0]
+    den = float(np.sum(od * od))
+    out = np.empty(len(radii))
+    for i, r in enumerate(radii):
+        ow = sparse_attention(qw, kw, vw, lambda p, r=int(r): swa_keys(p, N, r), scale)
+        out[i] = float(np.sum((ow - od) ** 2)) / den
+    return out
+
+
+def calibrate_windows(q, k, v, *, grid, head_kinds, radii, tau=2.0, softmax_scale=None):
+    """Per-head window radius by the greedy rule of [I] 1.1: the smallest
+    radius, among ``radii`` (ascending), whose relative squared error
+    against dense attention is at most ``tau`` on every calibration sample
+    (the batch entries stand in for the pages' eight analysis prompts);
+    N - 1 (the dense window, error 0) when none is.  Each head is evaluated
+    in its working order (Top-K heads as window heads in token order).
+    Readings: the bound is on the maximum over samples of the per-sample
+    error; tau is an input (the pages print 2.0).  Returns (errors
+    [len(radii), B, H], radius per head [H])."""
+    F, Hg, Wg = grid
+    q = np.asarray(q)
+    B, N, H, d = q.shape
+    scale = 1.0 / np.sqrt(d) if not softmax_scale or softmax_scale <= 0 else softmax_scale
+    radii = [int(r) for r in radii]
+    if any(b <= a for a, b in zip(radii, radii[1:])):
+        raise ValueError("radii must be ascending")
+    err = np.empty((len(radii), B, H))
+    for h in range(H):
+        order = head_order(int(head_kinds[h]), F, Hg, Wg)
+        for b in range(B):
+            w = [np.asarray(t[b, :, h], np.float64)[order] for t in (q, k, v)]
+            err[:, b, h] = window_errors(*w, radii, scale)
+    choice = np.full(H, N - 1, dtype=np.int64)
+    for h in range(H):
+        for i, r in enumerate(radii):
+            if err[i, :, h].max() <= tau:
+                choice[h] = r
+                break
+    return err, choice

@@ -13,6 +13,7 @@ import oracle.salad_backward as sb
 import oracle.salad_oracle as so
 from tests import test_oracle_attention as TA
 from tests import test_oracle_backward as TB
+from tests import test_oracle_calibrate as TC
 from tests import test_oracle_linear as TL
 from tests import test_oracle_order as TO
 from tests import test_oracle_rope as TR
@@ -149,6 +150,31 @@ def _gate_bwd_no_one_minus_s(x, w, b, ds):         # sigmoid derivative taken as
     return np.broadcast_to(dt * w / x.shape[0], x.shape).copy(), dt * x.mean(axis=0), dt
 
 
+def _window_errors_by_window_norm(qw, kw, vw, radii, scale):   # divides by ||O_window|| instead
+    od = so.dense_attention(qw, kw, vw, scale)
+    N = od.shape[0]
+    out = np.empty(len(radii))
+    for i, r in enumerate(radii):
+        ow = so.sparse_attention(qw, kw, vw, lambda p, r=int(r): so.swa_keys(p, N, r), scale)
+        out[i] = float(np.sum((ow - od) ** 2)) / float(np.sum(ow * ow))
+    return out
+
+
+def _calibrate_mean_over_samples(q, k, v, *, grid, head_kinds, radii, tau=2.0, softmax_scale=None):
+    err, _ = _orig_calibrate(q, k, v, grid=grid, head_kinds=head_kinds, radii=radii, tau=tau,
+                             softmax_scale=softmax_scale)
+    N = np.shape(q)[1]
+    choice = np.full(err.shape[2], N - 1, dtype=np.int64)
+    for h in range(err.shape[2]):
+        for i, r in enumerate(radii):
+            if err[i, :, h].mean() <= tau:         # the bound on the average sample
+                choice[h] = r
+                break
+    return err, choice
+
+
+_orig_calibrate = so.calibrate_windows
+
 CASES = [
     ("st_permutation", _perm_inverse, lambda: TO.test_st_permutation_matches_sort_construction((4, 8, 8))),
     ("swa_keys", _swa_keys_short, lambda: TA.test_window_matches_masked_dense(64, 5)),
@@ -172,6 +198,8 @@ CASES = [
     ("rope_3d_transpose", _rope_t_as_forward, lambda: TB.test_backward_matches_finite_differences(True)),
     ("linear_backward", _linear_bwd_no_den, lambda: TB.test_backward_matches_finite_differences(False)),
     ("gate_backward", _gate_bwd_no_one_minus_s, lambda: TB.test_backward_matches_finite_differences(False)),
+    ("window_errors", _window_errors_by_window_norm, TC.test_errors_match_masked_sdpa_and_dense_is_exact),
+    ("calibrate_windows", _calibrate_mean_over_samples, TC.test_greedy_choice_is_smallest_radius_meeting_the_bound),
 ]
 
 
