@@ -111,8 +111,9 @@ typedef struct {
 } salad_problem;
 
 /* Bytes of workspace that any entry point below except salad_attn_backward
- * may need for problem *p (the largest over them); the backward has its own
- * size, salad_backward_workspace_size.  Errors: NULL, SHAPE, UNSUPPORTED. */
+ * and salad_window_calibrate may need for problem *p (the largest over
+ * them); those two have their own sizes (salad_backward_workspace_size,
+ * salad_calibrate_workspace_size).  Errors: NULL, SHAPE, UNSUPPORTED. */
 salad_status salad_workspace_size(const salad_problem *p, size_t *bytes);
 
 /* Head-wise token permutation ([I] 1.1), optionally with 3D RoPE ([S] step 3,
@@ -223,6 +224,26 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
                                  const void *dout, void *dq, void *dk, void *dv, float *dw_p,
                                  void *dx, float *dgate_w, float *dgate_b, float *ds_out,
                                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Per-head window calibration ([I] 1.1): for every head of the problem,
+ * evaluated as a window head in its working order (Top-K heads in token
+ * order), the relative squared error of window attention against dense
+ * attention for each candidate radius:
+ *   err[i][b][h] = ||O_window(radii[i]) - O_dense||_F^2 / ||O_dense||_F^2
+ * over the head's N rows of sample b (float64, device, [n_radii][B][H]),
+ * and choice[h] (int32, device, [H]) = the smallest radii[i] with
+ * max_b err[i][b][h] <= tau, or N - 1 (the dense window) when none is.
+ * The batch entries are the calibration samples.  qw, kw, vw in working
+ * layout, io_dtype.  radii: host array, 1 <= n_radii <= 64, strictly
+ * ascending, >= 0 (radii past N - 1 act as N - 1).  tau >= 0 (the pages
+ * use 2.0).  window_radius, block and topk of *p are ignored.  Workspace:
+ * salad_calibrate_workspace_size.  Errors: NULL, ALIGN, SHAPE, WORKSPACE,
+ * UNSUPPORTED, HIP. */
+salad_status salad_calibrate_workspace_size(const salad_problem *p, size_t *bytes);
+salad_status salad_window_calibrate(const salad_problem *p, const void *qw, const void *kw,
+                                    const void *vw, const int32_t *radii, int n_radii, float tau,
+                                    double *err, int32_t *choice, void *ws, size_t ws_bytes,
+                                    hipStream_t stream);
 
 /* Output projection ([S] step 7): out[b,n,:] = in[b,n,:] W_o, a row vector
  * times W_o [C, C] row-major, no bias; in, out [B, N, C] (equivalently

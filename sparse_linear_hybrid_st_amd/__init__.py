@@ -31,7 +31,8 @@ STATUS = {0: "SALAD_OK", 1: "SALAD_ERR_NULL", 2: "SALAD_ERR_SHAPE", 3: "SALAD_ER
 EXPORTS = ("salad_workspace_size", "salad_permute", "salad_block_select", "salad_sparse_attn",
            "salad_linear_state", "salad_linear_apply", "salad_gate", "salad_combine",
            "salad_attn_forward", "salad_output_projection", "salad_backward_workspace_size",
-           "salad_attn_backward", "salad_profile_enable", "salad_profile_read", "salad_last_error")
+           "salad_attn_backward", "salad_calibrate_workspace_size", "salad_window_calibrate",
+           "salad_profile_enable", "salad_profile_read", "salad_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
             "salad_attn_forward": [P, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp],
             "salad_output_projection": [P, vp, vp, vp, vp],
             "salad_backward_workspace_size": [P, ctypes.POINTER(sz)],
+            "salad_calibrate_workspace_size": [P, ctypes.POINTER(sz)],
+            "salad_window_calibrate": [P, vp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp],
             "salad_attn_backward": [P, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     vp, sz, vp],
         }
@@ -313,6 +316,32 @@ def salad_attn_backward(p: Problem, q, k, v, x, w_p, gate_w, gate_b: float, dout
         _ptr(dgate_w, "dgate_w", C, torch.float32), _ptr(dgate_b, "dgate_b", 1, torch.float32),
         _ptr(ds, "ds", p.batch, torch.float32), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def salad_calibrate_workspace_size(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().salad_calibrate_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def salad_window_calibrate(p: Problem, qw, kw, vw, radii, tau: float, err, choice, ws, stream=None):
+    """Per-head window calibration: err (float64 [len(radii), B, H]) and
+    choice (int32 [H]) on the device; radii is a host sequence of ints."""
+    import torch
+    n, _ = _sizes(p)
+    dt = _io_dtype(p)
+    r = (ctypes.c_int32 * len(radii))(*[int(x) for x in radii])
+    _check(lib().salad_window_calibrate(
+        ctypes.byref(p), _ptr(qw, "qw", n, dt), _ptr(kw, "kw", n, dt), _ptr(vw, "vw", n, dt),
+        ctypes.cast(r, ctypes.c_void_p), len(radii), float(tau),
+        _ptr(err, "err", len(radii) * p.batch * p.n_heads, torch.float64),
+        _ptr(choice, "choice", p.n_heads, torch.int32), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def calibrate_workspace(p: Problem, device="cuda"):
+    import torch
+    return torch.empty(max(salad_calibrate_workspace_size(p), 16), dtype=torch.uint8, device=device)
 
 
 def backward_workspace(p: Problem, device="cuda"):

@@ -546,6 +546,79 @@ salad_status salad_output_projection(const salad_problem *p, const void *in, con
   return SALAD_OK;
 }
 
+// ---- window calibration ---------------------------------------------------------
+
+namespace {
+struct CalibPlan {
+  size_t od, ow, part, total;
+};
+CalibPlan calib_plan(const Info &inf) {
+  const Geom &g = inf.g;
+  const size_t rows = size_t(g.B) * g.H * g.N;
+  CalibPlan pl;
+  pl.od = 0;
+  pl.ow = up(rows * g.D * sizeof(float));
+  pl.part = pl.ow + up(rows * g.D * sizeof(float));
+  pl.total = pl.part + up(size_t(g.B) * g.H * calib_splits(g) * 2 * sizeof(double));
+  return pl;
+}
+}  // namespace
+
+salad_status salad_calibrate_workspace_size(const salad_problem *p, size_t *bytes) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  if (!bytes) return fail(SALAD_ERR_NULL, "bytes is NULL");
+  *bytes = calib_plan(inf).total;
+  return SALAD_OK;
+}
+
+salad_status salad_window_calibrate(const salad_problem *p, const void *qw, const void *kw, const void *vw,
+                                    const int32_t *radii, int n_radii, float tau, double *err,
+                                    int32_t *choice, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  CHECK(need(qw, "qw"));
+  CHECK(need(kw, "kw"));
+  CHECK(need(vw, "vw"));
+  CHECK(need(err, "err"));
+  CHECK(need(choice, "choice"));
+  if (!radii) return fail(SALAD_ERR_NULL, "radii is NULL");
+  if (n_radii < 1 || n_radii > kMaxCalibRadii)
+    return fail(SALAD_ERR_SHAPE, "n_radii must be in [1, %d] (got %d)", kMaxCalibRadii, n_radii);
+  if (!(tau >= 0.f) || !std::isfinite(tau)) return fail(SALAD_ERR_SHAPE, "tau must be finite and >= 0");
+  CalibRadii cr;
+  cr.n = n_radii;
+  for (int i = 0; i < n_radii; ++i) {
+    if (radii[i] < 0 || (i > 0 && radii[i] <= radii[i - 1]))
+      return fail(SALAD_ERR_SHAPE, "radii must be >= 0 and strictly ascending");
+    cr.r[i] = radii[i];
+  }
+  const CalibPlan pl = calib_plan(inf);
+  CHECK(need_ws(ws, ws_bytes, pl.total));
+  // every head as a window head in its working order
+  Geom g = inf.g;
+  for (int i = 0; i < 4; ++i) g.topk[i] = 0;
+  char *w = (char *)ws;
+  float *od = (float *)(w + pl.od), *ow = (float *)(w + pl.ow);
+  double *part = (double *)(w + pl.part);
+  const View qv = working_view(g, qw), kv = working_view(g, kw), vv = working_view(g, vw);
+  hipError_t e;
+  g.r = g.N - 1;  // dense: every key in every query's window
+  if ((e = launch_sparse_attn(g, inf.bf16, qv, kv, vv, nullptr, od, stream)) != hipSuccess)
+    return hip_status(e, "salad_window_calibrate: dense attention");
+  const size_t slice = size_t(g.B) * g.H;
+  for (int i = 0; i < n_radii; ++i) {
+    g.r = std::min(radii[i], g.N - 1);
+    if ((e = launch_sparse_attn(g, inf.bf16, qv, kv, vv, nullptr, ow, stream)) != hipSuccess ||
+        (e = launch_calib_err(g, od, ow, part, err + i * slice, stream)) != hipSuccess)
+      return hip_status(e, "salad_window_calibrate: window attention");
+  }
+  g.r = inf.g.r;
+  if ((e = launch_calib_choose(g, cr, tau, err, choice, stream)) != hipSuccess)
+    return hip_status(e, "salad_window_calibrate: choice");
+  return SALAD_OK;
+}
+
 // ---- backward -----------------------------------------------------------------
 
 namespace {

@@ -129,6 +129,20 @@ hipError_t launch_gate_bwd(const Geom &g, const float *ds_part, const float *s, 
                            const float *colsum, float *dt, float *ds_out, float *dgate_w,
                            float *dgate_b, hipStream_t st);
 hipError_t launch_gate_dx(const Geom &g, const float *dt, const bf16_t *w, bf16_t *dx, hipStream_t st);
+// ---- window calibration --------------------------------------------------
+constexpr int kMaxCalibRadii = 64;
+struct CalibRadii {
+  int n;
+  int32_t r[kMaxCalibRadii];
+};
+// Row chunks per (b, h) of the error reduction; part holds 2 doubles per chunk.
+int calib_splits(const Geom &g);
+// err[bh] = ||ow - od||^2 / ||od||^2 over each (b, h)'s rows (fp32 working layout).
+hipError_t launch_calib_err(const Geom &g, const float *od, const float *ow, double *part, double *err,
+                            hipStream_t st);
+// choice[h]: the first radius with max_b err[i][b][h] <= tau, else N - 1.
+hipError_t launch_calib_choose(const Geom &g, const CalibRadii &radii, float tau, const double *err,
+                               int32_t *choice, hipStream_t st);
 // Whether the attention kernel can stream K, V rows through these views.
 bool kv_direct_ok(const Geom &g, View kd, View vd);
 hipError_t launch_linear_apply(const Geom &g, int bf16, View qv, const float *h, const float *z,
