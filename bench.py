@@ -115,6 +115,49 @@ def cpu_baseline(w, inp, flops_total: float, target_s: float = 15.0, proj: str =
     }
 
 
+def calibrate_bench(args, w, inp, p):
+    """One JSON line for salad_window_calibrate on this workload's inputs:
+    time per call, and the dense pass's rate (4 d N^2 per head) as its
+    roofline figure."""
+    import numpy as np
+    import torch
+
+    import sparse_linear_hybrid_st_amd as S
+    radii = [int(r) for r in args.calibrate.split(",")]
+    qkv = [torch.empty_like(inp[n].cuda()) for n in ("q", "k", "v")]
+    for n, dst in zip(("q", "k", "v"), qkv):
+        S.salad_permute(p, 0, 0, inp[n].cuda(), dst)
+    err = torch.empty((len(radii), w.batch, w.n_heads), dtype=torch.float64, device="cuda")
+    choice = torch.empty(w.n_heads, dtype=torch.int32, device="cuda")
+    ws = S.calibrate_workspace(p)
+
+    def call():
+        S.salad_window_calibrate(p, *qkv, radii, 2.0, err, choice, ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    pairs_dense = w.batch * w.n_heads * w.N * w.N
+    pairs_win = sum(w.batch * w.n_heads * (w.N * (2 * min(r, w.N - 1) + 1) - min(r, w.N - 1) * (min(r, w.N - 1) + 1))
+                    for r in radii)
+    flops = 4.0 * w.head_dim * (pairs_dense + pairs_win)
+    print(json.dumps({
+        "metric": "window calibration: ms per call (dense attention + one window pass per radius)",
+        "value": ms, "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.io_dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "radii": radii, "tau": 2.0,
+                   "chosen": choice.cpu().tolist(),
+                   "worst_error": err.max(dim=1).values.cpu().numpy().round(4).tolist()},
+        "effective_tflops": flops / (ms * 1e-3) / 1e12}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +176,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time salad_attn_backward (gradients of Q, K, V, X, W_p and the gate "
                          "for a random output gradient) instead of the forward")
+    ap.add_argument("--calibrate", default=None, metavar="R1,R2,...",
+                    help="time salad_window_calibrate (dense attention plus one window pass per "
+                         "radius in this comma-separated list) instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size reference for the HBM byte counters)")
@@ -160,6 +206,9 @@ def main():
     s_out = torch.empty(w.batch, dtype=torch.float32, device="cuda")
     idx = torch.zeros((w.batch, w.n_heads, p.n_blocks, w.topk), dtype=torch.int32, device="cuda")
     ws = S.workspace(p)
+
+    if args.calibrate:
+        sys.exit(calibrate_bench(args, w, inp, p))
 
     def fwd():
         S.salad_attn_forward(p, dev["q"], dev["k"], dev["v"], dev["x"], dev["w_p"], dev["gate_w"],
