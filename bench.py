@@ -176,6 +176,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time salad_attn_backward (gradients of Q, K, V, X, W_p and the gate "
                          "for a random output gradient) instead of the forward")
+    ap.add_argument("--recompute", action="store_true",
+                    help="with --backward: do not hand the forward's output and row normalisers to "
+                         "the backward (it then recomputes the forward's sparse branch)")
     ap.add_argument("--calibrate", default=None, metavar="R1,R2,...",
                     help="time salad_window_calibrate (dense attention plus one window pass per "
                          "radius in this comma-separated list) instead of the forward")
@@ -226,13 +229,19 @@ def main():
         dgw = torch.empty(w.n_heads * w.head_dim, dtype=torch.float32, device="cuda")
         dgb = torch.empty(1, dtype=torch.float32, device="cuda")
         bws = S.backward_workspace(p)
+        lse = None if args.recompute else torch.empty((w.batch, w.n_heads, w.N), dtype=torch.float32,
+                                                      device="cuda")
 
         def step():
             S.salad_attn_backward(p, dev["q"], dev["k"], dev["v"], dev["x"], dev["w_p"], dev["gate_w"],
                                   inp["gate_b"], g_out, grads["dq"], grads["dk"], grads["dv"], dwp, bws,
-                                  dx=dx, dgate_w=dgw, dgate_b=dgb)
+                                  dx=dx, dgate_w=dgw, dgate_b=dgb,
+                                  out_saved=None if args.recompute else out, lse_saved=lse)
 
-    fwd()
+    # the forward once (its output and, for the backward, row normalisers)
+    S.salad_attn_forward(p, dev["q"], dev["k"], dev["v"], dev["x"], dev["w_p"], dev["gate_w"],
+                         inp["gate_b"], out, ws, s_out=s_out, idx_out=idx,
+                         lse_out=lse if args.backward else None)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -281,7 +290,10 @@ def main():
                    "heads": w.n_heads, "head_dim": w.head_dim,
                    "head_kinds": "".join("STK"[k] for k in w.head_kinds),
                    "window_radius": w.window_radius, "block": w.block, "topk": w.topk,
-                   "rope": w.rope, "proj": args.proj, "pass": "backward" if args.backward else "forward",
+                   "rope": w.rope, "proj": args.proj,
+                   "pass": ("backward (recomputing the forward's sparse branch)" if args.recompute else
+                            "backward (given the forward's output and row normalisers)")
+                   if args.backward else "forward",
                    "projection_gemm_flop": (2.0 * w.batch * w.N * (w.n_heads * w.head_dim) ** 2
                                             if args.proj == "full" else None),
                    "branch_drop_tau": args.branch_drop_tau,

@@ -192,12 +192,15 @@ salad_status salad_combine(const salad_problem *p, const float *o_s, const float
  * receive the gate values (before any dropping) and the block selection
  * when non-NULL.  A sample with s_b < branch_drop_tau gets
  * out = O_s; the decision is taken on the device, so nothing synchronises.
- * Workspace: salad_workspace_size. */
+ * lse_out (device float [B,H,N], optional, bf16 storage only): for each
+ * working row of each head, log2 of its sparse-branch softmax normaliser
+ * in units of scale*log2(e) scores, to be handed to salad_attn_backward
+ * with out.  Workspace: salad_workspace_size. */
 salad_status salad_attn_forward(const salad_problem *p, const void *q, const void *k,
                                 const void *v, const void *x, const void *w_p,
                                 const void *gate_w, float gate_b, const float *s_override,
-                                void *out, float *s_out, int32_t *idx_out, void *ws,
-                                size_t ws_bytes, hipStream_t stream);
+                                void *out, float *s_out, int32_t *idx_out, float *lse_out,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Backward of salad_attn_forward (head-wise projection, bf16 storage,
  * d = 128): the gradients of L = sum(dout * out) that fine-tuning the
@@ -209,7 +212,11 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
  * sample with s_b < branch_drop_tau gets no gradient through its linear
  * branch, W_p or the gate; with s_override the gate is not differentiated.
  *
- * Inputs as for salad_attn_forward, plus dout [B,N,H,d] (bf16).  Outputs:
+ * Inputs as for salad_attn_forward, plus dout [B,N,H,d] (bf16) and,
+ * optionally, the forward's out and lse_out for the same inputs (out_saved,
+ * lse_saved; both or neither): with them the sparse branch's normalisers
+ * are reused and D = dO . O_s comes from out (O_s = out - s_b O_l W_p);
+ * without them the forward's sparse branch is recomputed.  Outputs:
  * dq, dk, dv [B,N,H,d] bf16 (w.r.t. the unrotated Q, K); dw_p [d,d] float32;
  * when the gate is computed (s_override NULL): dx [B,N,C] bf16, dgate_w [C]
  * and dgate_b [1] float32, each optional (NULL: not written); ds_out [B]
@@ -221,9 +228,10 @@ salad_status salad_backward_workspace_size(const salad_problem *p, size_t *bytes
 salad_status salad_attn_backward(const salad_problem *p, const void *q, const void *k,
                                  const void *v, const void *x, const void *w_p,
                                  const void *gate_w, float gate_b, const float *s_override,
-                                 const void *dout, void *dq, void *dk, void *dv, float *dw_p,
-                                 void *dx, float *dgate_w, float *dgate_b, float *ds_out,
-                                 void *ws, size_t ws_bytes, hipStream_t stream);
+                                 const void *dout, const void *out_saved, const float *lse_saved,
+                                 void *dq, void *dk, void *dv, float *dw_p, void *dx,
+                                 float *dgate_w, float *dgate_b, float *ds_out, void *ws,
+                                 size_t ws_bytes, hipStream_t stream);
 
 /* Per-head window calibration ([I] 1.1): for every head of the problem,
  * evaluated as a window head in its working order (Top-K heads in token

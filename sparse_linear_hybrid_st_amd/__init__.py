@@ -97,13 +97,13 @@ def lib() -> ctypes.CDLL:
             "salad_linear_apply": [P, vp, vp, vp, vp, vp],
             "salad_gate": [P, vp, vp, f32, vp, vp, sz, vp],
             "salad_combine": [P, vp, vp, vp, vp, vp, vp],
-            "salad_attn_forward": [P, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp],
+            "salad_attn_forward": [P, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, sz, vp],
             "salad_output_projection": [P, vp, vp, vp, vp],
             "salad_backward_workspace_size": [P, ctypes.POINTER(sz)],
             "salad_calibrate_workspace_size": [P, ctypes.POINTER(sz)],
             "salad_window_calibrate": [P, vp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp],
             "salad_attn_backward": [P, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                    vp, sz, vp],
+                                    vp, vp, vp, sz, vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -267,7 +267,7 @@ def salad_combine(p: Problem, o_s, o_l, w_p, s, out, stream=None):
 
 
 def salad_attn_forward(p: Problem, q, k, v, x, w_p, gate_w, gate_b: float, out, ws,
-                       s_override=None, s_out=None, idx_out=None, stream=None):
+                       s_override=None, s_out=None, idx_out=None, lse_out=None, stream=None):
     import torch
     n, _ = _sizes(p)
     dt = _io_dtype(p)
@@ -279,6 +279,7 @@ def salad_attn_forward(p: Problem, q, k, v, x, w_p, gate_w, gate_b: float, out, 
         _ptr(gate_w, "gate_w", C, dt), float(gate_b),
         _ptr(s_override, "s_override", p.batch, torch.float32), _ptr(out, "out", n, dt),
         _ptr(s_out, "s_out", p.batch, torch.float32), _ptr(idx_out, "idx_out", nidx, torch.int32),
+        _ptr(lse_out, "lse_out", p.batch * p.n_heads * p.N, torch.float32),
         _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -298,10 +299,12 @@ def salad_backward_workspace_size(p: Problem) -> int:
 
 
 def salad_attn_backward(p: Problem, q, k, v, x, w_p, gate_w, gate_b: float, dout, dq, dk, dv, dw_p, ws,
-                        dx=None, dgate_w=None, dgate_b=None, ds=None, s_override=None, stream=None):
+                        dx=None, dgate_w=None, dgate_b=None, ds=None, s_override=None, out_saved=None,
+                        lse_saved=None, stream=None):
     """Gradients of sum(dout * salad_attn_forward(...)): dq, dk, dv [B,N,H,d]
     and dx [B,N,C] in bf16; dw_p [d,d], dgate_w [C], dgate_b [1], ds [B] in
-    float32 (dx, dgate_w, dgate_b, ds optional)."""
+    float32 (dx, dgate_w, dgate_b, ds optional).  out_saved / lse_saved: the
+    forward's out and lse_out for the same inputs (skips the recompute)."""
     import torch
     n, _ = _sizes(p)
     dt = _io_dtype(p)
@@ -311,6 +314,8 @@ def salad_attn_backward(p: Problem, q, k, v, x, w_p, gate_w, gate_b: float, dout
         _ptr(x, "x", p.batch * p.N * C, dt), _ptr(w_p, "w_p", p.w_p_numel, dt),
         _ptr(gate_w, "gate_w", C, dt), float(gate_b),
         _ptr(s_override, "s_override", p.batch, torch.float32), _ptr(dout, "dout", n, dt),
+        _ptr(out_saved, "out_saved", n, dt),
+        _ptr(lse_saved, "lse_saved", p.batch * p.n_heads * p.N, torch.float32),
         _ptr(dq, "dq", n, dt), _ptr(dk, "dk", n, dt), _ptr(dv, "dv", n, dt),
         _ptr(dw_p, "dw_p", p.head_dim ** 2, torch.float32), _ptr(dx, "dx", p.batch * p.N * C, dt),
         _ptr(dgate_w, "dgate_w", C, torch.float32), _ptr(dgate_b, "dgate_b", 1, torch.float32),

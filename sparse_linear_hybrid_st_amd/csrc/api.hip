@@ -403,7 +403,7 @@ salad_status salad_combine(const salad_problem *p, const float *o_s, const float
 salad_status salad_attn_forward(const salad_problem *p, const void *q, const void *k, const void *v,
                                 const void *x, const void *w_p, const void *gate_w, float gate_b,
                                 const float *s_override, void *out, float *s_out, int32_t *idx_out,
-                                void *ws, size_t ws_bytes, hipStream_t stream) {
+                                float *lse_out, void *ws, size_t ws_bytes, hipStream_t stream) {
   Info inf;
   CHECK(validate(p, &inf));
   CHECK(need(q, "q"));
@@ -419,6 +419,10 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
   }
   if (s_out) CHECK(need(s_out, "s_out"));
   if (idx_out) CHECK(need(idx_out, "idx_out"));
+  if (lse_out) {
+    CHECK(need(lse_out, "lse_out"));
+    if (!inf.bf16) return fail(SALAD_ERR_UNSUPPORTED, "lse_out needs bf16 storage (the backward is bf16 only)");
+  }
   const Geom &g = inf.g;
   const Plan pl = plan(inf);
   CHECK(need_ws(ws, ws_bytes, pl.total_forward));
@@ -489,7 +493,7 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
     if (!inf.full) outl.base = nullptr;
     if ((e = prof_mark(0, stream)) != hipSuccess ||
         (e = launch_attn_fused(g, qv, kw, vw, kd, vd, work, idx, hp, zv, s, boundary_view(g, out), outl,
-                               stream)) != hipSuccess ||
+                               lse_out, stream)) != hipSuccess ||
         (e = prof_mark(1, stream)) != hipSuccess)
       return hip_status(e, "salad_attn_forward: attention");
     if (inf.full) return project_full(inf, w + pl.olt, w_p, out, stream);
@@ -699,9 +703,10 @@ salad_status salad_backward_workspace_size(const salad_problem *p, size_t *bytes
 
 salad_status salad_attn_backward(const salad_problem *p, const void *q, const void *k, const void *v,
                                  const void *x, const void *w_p, const void *gate_w, float gate_b,
-                                 const float *s_override, const void *dout, void *dq, void *dk, void *dv,
-                                 float *dw_p, void *dx, float *dgate_w, float *dgate_b, float *ds_out,
-                                 void *ws, size_t ws_bytes, hipStream_t stream) {
+                                 const float *s_override, const void *dout, const void *out_saved,
+                                 const float *lse_saved, void *dq, void *dk, void *dv, float *dw_p, void *dx,
+                                 float *dgate_w, float *dgate_b, float *ds_out, void *ws, size_t ws_bytes,
+                                 hipStream_t stream) {
   Info inf;
   CHECK(validate_backward(p, &inf));
   CHECK(need(q, "q"));
@@ -725,6 +730,11 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
     CHECK(need(s_override, "s_override"));
   }
   if (ds_out) CHECK(need(ds_out, "ds_out"));
+  const bool saved = out_saved || lse_saved;
+  if (saved) {
+    CHECK(need(out_saved, "out_saved"));
+    CHECK(need(lse_saved, "lse_saved"));
+  }
   const Geom &g = inf.g;
   const BwdPlan pl = bwd_plan(inf);
   CHECK(need_ws(ws, ws_bytes, pl.total));
@@ -779,7 +789,17 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
   lw.dhtb = (bf16_t *)(w + pl.dhtb);
   lw.dwp_h = (float *)(w + pl.dwp_h);
   lw.ds_part = (float *)(w + pl.ds_part);
-  if ((e = launch_linear_bwd(g, wq, wg, hm, zv, (const bf16_t *)w_p, s, lw, dw_p, stream)) != hipSuccess)
+  // with the forward's output and normalisers, D comes from the linear
+  // pass and the normalisers are copied into the padded rows; otherwise the
+  // forward's sparse branch is recomputed below
+  View outv = boundary_view(g, out_saved);
+  if (!saved) outv.base = nullptr;
+  if (saved && (e = hipMemcpy2DAsync(lse, size_t(pl.Np) * sizeof(float), lse_saved, size_t(g.N) * sizeof(float),
+                                     size_t(g.N) * sizeof(float), size_t(g.B) * g.H, hipMemcpyDeviceToDevice,
+                                     stream)) != hipSuccess)
+    return hip_status(e, "salad_attn_backward: copy lse");
+  if ((e = launch_linear_bwd(g, wq, wg, hm, zv, (const bf16_t *)w_p, s, lw, dw_p, outv, dsum, pl.Np, stream)) !=
+      hipSuccess)
     return hip_status(e, "salad_attn_backward: linear branch");
   // sparse branch (normalisers and D, then dQ and dK, dV, whose epilogues add
   // the linear branch's per-row terms and write the final rows)
@@ -794,7 +814,7 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
   bo.dq = (bf16_t *)dq;
   bo.dk = (bf16_t *)dk;
   bo.dv = (bf16_t *)dv;
-  if ((e = launch_attn_bwd_prep(g, qv, kv, vv, idx, wg, lse, dsum, pl.Np, stream)) != hipSuccess ||
+  if ((!saved && (e = launch_attn_bwd_prep(g, qv, kv, vv, idx, wg, lse, dsum, pl.Np, stream)) != hipSuccess) ||
       (e = prof_mark(0, stream)) != hipSuccess ||
       (e = launch_attn_bwd(g, wq, wk, wv, wg, lse, dsum, pl.Np, idx, inv_off, inv_list, bo, stream)) !=
           hipSuccess ||

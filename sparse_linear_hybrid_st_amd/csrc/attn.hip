@@ -99,7 +99,8 @@ struct AttnArgs {
   View out;              // fused: output rows (boundary layout, scattered)
   View out_l;            // fused, full-width projection: s_b * O_l rows (base NULL otherwise)
   const bf16_t *go;      // backward prep: dL/dO_s, working layout [B*H][N][128]
-  float *lse2;           // backward prep: [B*H][lse_stride] log2 of each row's softmax normaliser
+  float *lse2;           // backward prep: [B*H][lse_stride] log2 of each row's softmax normaliser;
+                         // fused: optional [B*H][N] copy of the same for a later backward
   float *dsum;           // backward prep: [B*H][lse_stride] D = dO . O_s per row
   int lse_stride;        // backward prep: row stride of lse2 / dsum per head (>= N)
   int n_heads_sel;       // heads handled by this launch
@@ -474,6 +475,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   const float inv = 1.f / l_tot;
 
   if constexpr (FUSED) {
+    // For a later backward: each row's normaliser in log2 units ([B*H][N])
+    if (a.lse2 && hl == 0 && pq < g.N) a.lse2[(long long)bh * g.N + pq] = m_off + log2f(l_tot);
     // Branch dropping ([G] 2 C): a sample whose gate value is below the
     // threshold keeps only the sparse branch (its state was not computed).
     if (a.s_gate[b] < g.drop_tau) {
@@ -690,7 +693,7 @@ hipError_t launch_attn_bwd_prep(const Geom &g, View qv, View kv, View vv, const 
 
 hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, View vd,
                              const uint64_t work[4], const int32_t *idx, const bf16_t *hp,
-                             const float *z, const float *s_gate, View outv, View outl,
+                             const float *z, const float *s_gate, View outv, View outl, float *lse_out,
                              hipStream_t st) {
   bool any_work = false, any_direct = false;
   for (int h = 0; h < g.H; ++h) {
@@ -714,6 +717,7 @@ hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, 
   a.s_gate = s_gate;
   a.out = outv;
   a.out_l = outl;
+  a.lse2 = lse_out;
   return launch_bf16<1>(a, st);
 }
 

@@ -67,10 +67,12 @@ hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial,
 // others through kd, vd (rows in working order where they already are).
 // s_gate: samples with s_b < g.drop_tau skip the linear term (out = O_s).
 // outl.base non-NULL (full-width projection, hp = H^T): out receives O_s
-// and outl receives s_b * O_l (zero rows for dropped samples).
+// and outl receives s_b * O_l (zero rows for dropped samples).  lse_out
+// (nullable, [B*H][N] by working row): each row's softmax normaliser in
+// log2 units, for a later backward.
 hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, View vd,
                              const uint64_t work[4], const int32_t *idx, const bf16_t *hp,
-                             const float *z, const float *s_gate, View outv, View outl,
+                             const float *z, const float *s_gate, View outv, View outl, float *lse_out,
                              hipStream_t st);
 // Backward preparation (bf16, d = 128, working-layout views): the forward
 // sparse attention per row, reduced to lse2 (log2 of the softmax
@@ -100,9 +102,12 @@ struct LinBwdScratch {
 // Linear-branch and projection gradients that need whole-head sums: M = H
 // W_p (mb), A and Bz = dZ (bz), dH and dH^T (dhb, dhtb), dw_p [d][d] and
 // ws.ds_part (16 partial sums of dL/ds per head; zero for dropped samples).
+// outv.base non-NULL (the forward's output, boundary layout): also each
+// working row's D = dO . O_s into dsum (rows Np apart per head).
 hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *go, const float *hm,
                              const float *zv, const bf16_t *w_p, const float *s_gate,
-                             const LinBwdScratch &w, float *dw_p, hipStream_t st);
+                             const LinBwdScratch &w, float *dw_p, View outv, float *dsum, int Np,
+                             hipStream_t st);
 // dQ, dK, dV rows (bf16, boundary layout [B,N,H,d]) of the whole layer: the
 // sparse branch's gradients plus, in the epilogues, the linear branch's per
 // row terms (from M, Z, dH, dH^T, dZ and s; none for dropped samples) and

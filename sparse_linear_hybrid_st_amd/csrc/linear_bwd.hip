@@ -86,7 +86,12 @@ __global__ void __launch_bounds__(256) lin_bwd_prep_kernel(Geom g, const float *
   }
 }
 
-// Per row gm and the split-N partials of A (128 x 128) and Bz (128).
+// Per row gm and the split-N partials of A (128 x 128) and Bz (128).  With
+// the forward's output given (outv.base non-NULL), also each row's
+// D = dO . O_s for the sparse branch's backward, from
+// O_s = out - s_b O_l W_p = out - s_b (a M) / den, whose dot with dO is
+// dO . out - s_b t / den (t = a . gm, already at hand); dropped samples
+// (out = O_s) only get D = dO . out.
 // Grid (S, B*H), 256 threads; split s covers rows [s*chunk, (s+1)*chunk).
 // A step handles 128 rows: wave w owns rows 32w + l32 (one per lane column)
 // for gm^T = M g^T on MFMA (M rows from LDS, g rows as B operands) and the
@@ -98,7 +103,8 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
                                                               const bf16_t *__restrict__ mb,
                                                               const float *__restrict__ zv,
                                                               const float *__restrict__ s_gate,
-                                                              float *__restrict__ partial, int S, int chunk) {
+                                                              float *__restrict__ partial, int S, int chunk,
+                                                              View outv, float *__restrict__ dsum, int Np) {
   constexpr int TT = 128;
   __shared__ __attribute__((aligned(1024))) bf16_t Ms[D * D];
   __shared__ __attribute__((aligned(1024))) bf16_t At[TT * D];
@@ -109,8 +115,36 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
   const int s = blockIdx.x, bh = blockIdx.y, b = bh / g.H;
   const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  if (dropped(g, s_gate, b)) return;
   const int n0 = s * chunk, n1 = min(g.N, n0 + chunk);
+  const int h = bh % g.H;
+  const bf16_t *outb = (const bf16_t *)outv.base;
+  // dO . out over this lane's features f = 32db + 8r4 + 4hl + e of row n,
+  // completed across the two half-waves (same row)
+  auto go_out = [&](int n) __attribute__((always_inline)) {
+    const bf16_t *gr = go + ((long long)bh * g.N + n) * D;
+    const bf16_t *orow = outb + row_offset(g, outv, b, h, n);
+    float acc = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int f = 32 * db + 8 * r4 + 4 * hl;
+        const bf16x4 g4 = *(const bf16x4 *)(gr + f), o4 = *(const bf16x4 *)(orow + f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf(float(g4[e]), float(o4[e]), acc);
+      }
+    return acc + __shfl_xor(acc, 32);
+  };
+  if (dropped(g, s_gate, b)) {
+    if (!outb) return;
+    for (int base = n0; base < n1; base += 128) {
+      const int n = base + 32 * w + l32;
+      if (n >= n1) continue;  // both half-waves of a row skip together
+      const float dv = go_out(n);
+      if (hl == 0) dsum[(long long)bh * Np + n] = dv;
+    }
+    return;
+  }
   const float sb = s_gate[b];
   const long long hrow = (long long)bh * g.N;
   stage_swizzled(Ms, mb + (long long)bh * D * D, t);
@@ -180,6 +214,10 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
     const float den = dp + g.eps;
     const float dden = -sb * tp / (den * den);
     const float inv_den = 1.f / den;
+    if (outb) {
+      const float dv = go_out(nc) - sb * tp * inv_den;
+      if (valid && hl == 0) dsum[(long long)bh * Np + n] = dv;
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -324,14 +362,16 @@ __global__ void __launch_bounds__(256) lin_bwd_wp_kernel(int BH, const float *__
 
 hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *go, const float *hm,
                              const float *zv, const bf16_t *w_p, const float *s_gate,
-                             const LinBwdScratch &w, float *dw_p, hipStream_t st) {
+                             const LinBwdScratch &w, float *dw_p, View outv, float *dsum, int Np,
+                             hipStream_t st) {
   if (g.D != D) return hipErrorInvalidValue;
   const int BH = g.B * g.H;
   const int S = linear_splits(g);
   int chunk = (g.N + S - 1) / S;
   chunk = (chunk + 127) / 128 * 128;
   lin_bwd_prep_kernel<<<dim3(16, BH), 256, 0, st>>>(g, hm, w_p, s_gate, w.mf, w.mb);
-  lin_bwd_rows_kernel<<<dim3(S, BH), 256, 0, st>>>(g, q, go, w.mb, zv, s_gate, w.partial, S, chunk);
+  lin_bwd_rows_kernel<<<dim3(S, BH), 256, 0, st>>>(g, q, go, w.mb, zv, s_gate, w.partial, S, chunk, outv,
+                                                    dsum, Np);
   hipError_t e = launch_linear_reduce(g, S, w.partial, w.a_red, w.bz, st);
   if (e != hipSuccess) return e;
   lin_bwd_head_kernel<<<dim3(16, BH), 256, 0, st>>>(g, w.a_red, hm, w.mf, w_p, s_gate, w.dhb, w.dhtb,

@@ -99,7 +99,7 @@ def test_null_and_misaligned_pointers_fail_before_launch():
     # workspace too small / missing
     assert L.salad_gate(ctypes.byref(p), a, a, 0.0, a, None, 0, None) == 5
     assert L.salad_gate(ctypes.byref(p), a, a, 0.0, a, a, 16, None) == 5
-    assert L.salad_attn_forward(ctypes.byref(p), a, a, a, a, a, a, 0.0, None, a, None, None,
+    assert L.salad_attn_forward(ctypes.byref(p), a, a, a, a, a, a, 0.0, None, a, None, None, None,
                                 a, 16, None) == 5
     assert b"workspace" in L.salad_last_error()
     assert L.salad_workspace_size(None, None) == 1

@@ -40,20 +40,28 @@ def _dout(w):
     return I.to_storage(g, w.io_dtype)
 
 
-def run_backward(w, inp, dout, s_override=None, branch_drop_tau=0.0):
+def run_backward(w, inp, dout, s_override=None, branch_drop_tau=0.0, saved=False):
+    """salad_attn_backward on the device; with saved=True the forward runs
+    first and its out and row normalisers are handed to the backward."""
     p = S.problem_from_workload(w, branch_drop_tau=branch_drop_tau)
     d = {n: dev(inp[n]) for n in ("q", "k", "v", "x", "w_p", "gate_w")}
     go = dev(dout)
+    so = None if s_override is None else torch.tensor(s_override, dtype=torch.float32, device="cuda")
+    out = lse = None
+    if saved:
+        out = torch.empty_like(d["q"])
+        lse = torch.empty((w.batch, w.n_heads, w.N), dtype=torch.float32, device="cuda")
+        S.salad_attn_forward(p, d["q"], d["k"], d["v"], d["x"], d["w_p"], d["gate_w"], inp["gate_b"], out,
+                             S.workspace(p), s_override=so, lse_out=lse)
     dq, dk, dv = (torch.empty_like(d["q"]) for _ in range(3))
     dx = torch.empty_like(d["x"])
     dwp = torch.empty((w.head_dim, w.head_dim), dtype=torch.float32, device="cuda")
     dgw = torch.empty(w.n_heads * w.head_dim, dtype=torch.float32, device="cuda")
     dgb = torch.empty(1, dtype=torch.float32, device="cuda")
     ds = torch.empty(w.batch, dtype=torch.float32, device="cuda")
-    so = None if s_override is None else torch.tensor(s_override, dtype=torch.float32, device="cuda")
     S.salad_attn_backward(p, d["q"], d["k"], d["v"], d["x"], d["w_p"], d["gate_w"], inp["gate_b"], go,
                           dq, dk, dv, dwp, S.backward_workspace(p), dx=dx, dgate_w=dgw, dgate_b=dgb, ds=ds,
-                          s_override=so)
+                          s_override=so, out_saved=out, lse_saved=lse)
     torch.cuda.synchronize()
     return {"dq": host64(dq), "dk": host64(dk), "dv": host64(dv), "dx": host64(dx), "dw_p": host64(dwp),
             "dgate_w": host64(dgw), "dgate_b": float(dgb.item()), "ds": host64(ds)}
@@ -83,30 +91,32 @@ def _compare(w, got, ref, names=("dq", "dk", "dv", "dw_p", "dx", "dgate_w", "ds"
     print(w.name, " ".join(f"{n} {m:.2g}/{f:.2g}" for n, m, f in out))
 
 
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
 @pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
-def test_backward_matches_oracle(w):
+def test_backward_matches_oracle(w, saved):
     inp = I.make_inputs(w)
     dout = _dout(w)
-    got = run_backward(w, inp, dout)
+    got = run_backward(w, inp, dout, saved=saved)
     ref = oracle_backward(w, inp, dout)
     _compare(w, got, ref)
     assert abs(got["dgate_b"] - ref["dgate_b"]) <= MAX_REL * max(abs(ref["dgate_b"]), 1e-30) + 1e-7
 
 
-def test_backward_with_dropping_and_fixed_gate():
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+def test_backward_with_dropping_and_fixed_gate(saved):
     w = CASES[3]
     inp = I.make_inputs(w)
     dout = _dout(w)
     s = np.array([O.gate(I.as_f64(inp["x"])[b], I.as_f64(inp["gate_w"]), inp["gate_b"])
                   for b in range(w.batch)])
     tau = float(s.mean())
-    got = run_backward(w, inp, dout, branch_drop_tau=tau)
+    got = run_backward(w, inp, dout, branch_drop_tau=tau, saved=saved)
     ref = oracle_backward(w, inp, dout, drop_tau=tau)
     _compare(w, got, ref, names=("dq", "dk", "dv", "dw_p", "dgate_w"))
     lo = int(np.argmin(s))
     assert got["ds"][lo] == 0.0 and np.all(got["dx"][lo] == 0.0)
     s0 = [0.25, 0.6]
-    got = run_backward(w, inp, dout, s_override=s0)
+    got = run_backward(w, inp, dout, s_override=s0, saved=saved)
     ref = oracle_backward(w, inp, dout, s_override=np.array(s0))
     _compare(w, got, ref, names=("dq", "dk", "dv", "dw_p", "ds"))
 
@@ -150,7 +160,7 @@ def test_backward_full_size_sampled_rows(name):
     w = C.all_workloads()[name]
     inp = I.make_inputs(w)
     dout = _dout(w)
-    got = run_backward(w, inp, dout)
+    got = run_backward(w, inp, dout, saved=True)
     rows_q, rows_kv = _sample(w, 10, 4, seed=11)
     args = [inp[n].float().numpy() for n in ("q", "k", "v", "x")] + \
         [I.as_f64(inp[n]) for n in ("w_p", "gate_w")]
