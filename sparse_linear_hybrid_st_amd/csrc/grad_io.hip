@@ -65,20 +65,29 @@ __global__ void __launch_bounds__(64) gate_bwd_kernel(Geom g, const float *__res
   if (has_gate && dgate_b) *dgate_b = float(db);
 }
 
-// dgate_w[c] = sum_b dt_b mean_n X_b[n][c], one thread per column, the
-// column's split sums added in order.
+// dgate_w[c] = sum_b dt_b mean_n X_b[n][c].  A workgroup owns 32 columns;
+// thread t adds splits t/32, t/32 + 8, ... of column t%32 (coalesced across
+// the columns), then the 8 partial sums of a column are added in order.
 __global__ void __launch_bounds__(256) gate_dw_kernel(Geom g, const float *__restrict__ dt,
                                                       const float *__restrict__ colsum, int splits,
                                                       float *__restrict__ dgate_w) {
-  const int C = g.H * g.D, c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= C) return;
+  const int C = g.H * g.D, t = threadIdx.x;
+  const int c = blockIdx.x * 32 + (t & 31), sg = t >> 5;
+  __shared__ double part[8][32];
   double acc = 0.0;
-  for (int b = 0; b < g.B; ++b) {
-    double xs = 0.0;
-    for (int sp = 0; sp < splits; ++sp) xs += double(colsum[((long long)b * splits + sp) * C + c]);
-    acc += double(dt[b]) * xs / double(g.N);
+  if (c < C)
+    for (int b = 0; b < g.B; ++b) {
+      double xs = 0.0;
+      for (int sp = sg; sp < splits; sp += 8) xs += double(colsum[((long long)b * splits + sp) * C + c]);
+      acc += double(dt[b]) * xs;
+    }
+  part[sg][t & 31] = acc;
+  __syncthreads();
+  if (sg == 0 && c < C) {
+    double sum = 0.0;
+    for (int i = 0; i < 8; ++i) sum += part[i][t];
+    dgate_w[c] = float(sum / double(g.N));
   }
-  dgate_w[c] = float(acc);
 }
 
 hipError_t launch_gate_bwd(const Geom &g, const float *ds_part, const float *s, int has_gate,
@@ -87,7 +96,7 @@ hipError_t launch_gate_bwd(const Geom &g, const float *ds_part, const float *s, 
   gate_bwd_kernel<<<1, 64, 0, st>>>(g, ds_part, s, has_gate, dt, ds_out, dgate_b);
   if (has_gate && dgate_w) {
     const int C = g.H * g.D;
-    gate_dw_kernel<<<(C + 255) / 256, 256, 0, st>>>(g, dt, colsum, gate_bwd_splits(g), dgate_w);
+    gate_dw_kernel<<<(C + 31) / 32, 256, 0, st>>>(g, dt, colsum, gate_bwd_splits(g), dgate_w);
   }
   return hipGetLastError();
 }
@@ -100,9 +109,10 @@ __global__ void __launch_bounds__(256) gate_dx_kernel(Geom g, const float *__res
   if (e >= (long long)g.N * C) return;
   const int c = int(e % C);
   const float k = dt[b] / float(g.N);
-  bf16_t o[8];
+  bf16_t wv[8], o[8];
+  *(u32x4_g *)wv = *(const u32x4_g *)(w + c);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = f32_to_bf16(k * bf16_to_f32(w[c + i]));
+  for (int i = 0; i < 8; ++i) o[i] = f32_to_bf16(k * bf16_to_f32(wv[i]));
   *(u32x4_g *)(dx + (long long)b * g.N * C + e) = *(const u32x4_g *)o;
 }
 
