@@ -455,11 +455,17 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bwd_dq_kernel(BwdArgs a) {
 // 64-key block, 2 waves, Top-K heads); wave w keeps keys k0 + 32w + l32 and
 // their V rows as MFMA B operands.  Query tiles of 64 rows (Q, dO, lse2, D)
 // are double-buffered in LDS and consumed as two 32-query halves.
+// WHICH = 0 computes dK and dV together (one wave per SIMD: two 32 x 128
+// accumulators and the K, V rows exceed the 256 registers that two waves
+// per SIMD allow); WHICH = 1 computes dV only (S, P, dV) and WHICH = 2 dK
+// only (S, dP, dS, dK), each within two waves per SIMD, at the price of S
+// computed in both passes.
 // ---------------------------------------------------------------------------
-template <int NW>
-__global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
+template <int NW, int WHICH>
+__global__ void __launch_bounds__(NW * 64, WHICH == 0 ? 1 : 2) attn_bwd_dkv_kernel(BwdArgs a) {
   constexpr int BK = NW * 32;
   constexpr bool TOPK = NW == 2;
+  constexpr bool DO_V = WHICH != 2, DO_K = WHICH != 1;
   constexpr int TILE = kBN * kD;
   __shared__ __attribute__((aligned(1024))) bf16_t Q0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t Q1[TILE];
@@ -483,7 +489,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     kf[ks] = *(const bf16x8 *)(a.k + (hrow + pkc) * kD + (2 * ks + hl) * 8);
-    vf[ks] = *(const bf16x8 *)(a.v + (hrow + pkc) * kD + (2 * ks + hl) * 8);
+    if (DO_K) vf[ks] = *(const bf16x8 *)(a.v + (hrow + pkc) * kD + (2 * ks + hl) * 8);
   }
   const float c2 = g.scale * 1.4426950408889634f;
 
@@ -546,7 +552,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
       for (int ks = 0; ks < 8; ++ks) {
         const int o = qs * 32 * kD + oo.k_lane + 16 * (ks ^ oo.k_x);
         s = mfma_32x32x16(*(const bf16x8 *)(Qs + o), kf[ks], s);
-        dp = mfma_32x32x16(*(const bf16x8 *)(Gs + o), vf[ks], dp);
+        if (DO_K) dp = mfma_32x32x16(*(const bf16x8 *)(Gs + o), vf[ks], dp);
       }
       // query of register r: i0 + 8(r/4) + 4hl + r%4.  Edge blocks first
       // set the scores of dropped pairs to -inf (P = 0); rows past N also
@@ -557,7 +563,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         f32x4 lv = *(const f32x4 *)(Ls + 32 * qs + 8 * m + 4 * hl);
-        f32x4 dv4 = *(const f32x4 *)(Ds + 32 * qs + 8 * m + 4 * hl);
+        f32x4 dv4 = DO_K ? *(const f32x4 *)(Ds + 32 * qs + 8 * m + 4 * hl) : f32x4{};
         if (!full) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -573,8 +579,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * m + e;
           const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lv[e]));
-          pb[r >> 3][r & 7] = (__bf16)p;
-          dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dv4[e]));
+          if (DO_V) pb[r >> 3][r & 7] = (__bf16)p;
+          if (DO_K) dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dv4[e]));
         }
       }
       // dV^T[d][keys] += dO^T[d][q] P[q][keys];  dK^T += Q^T dS
@@ -583,13 +589,13 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
         bf16x8 ga[4], qa[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          ga[db] = tr_operand(Gs + qs * 32 * kD, oo, kk, db);
-          qa[db] = tr_operand(Qs + qs * 32 * kD, oo, kk, db);
+          if (DO_V) ga[db] = tr_operand(Gs + qs * 32 * kD, oo, kk, db);
+          if (DO_K) qa[db] = tr_operand(Qs + qs * 32 * kD, oo, kk, db);
         }
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          dv[db] = mfma_32x32x16(ga[db], pb[kk], dv[db]);
-          dk[db] = mfma_32x32x16(qa[db], dsb[kk], dk[db]);
+          if (DO_V) dv[db] = mfma_32x32x16(ga[db], pb[kk], dv[db]);
+          if (DO_K) dk[db] = mfma_32x32x16(qa[db], dsb[kk], dk[db]);
         }
       }
     }
@@ -622,15 +628,19 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
     // dH rows 0..63 in Q0, 64..127 in Q1; dH^T rows likewise in G0, G1
     __syncthreads();  // every wave is done with the query tiles
     const long long hm_off = (long long)bh * kD * kD;
-    dma.issue(a.out.dhb + hm_off, 0, kD, Q0, w);
-    dma.issue(a.out.dhb + hm_off, 64, kD, Q1, w);
-    dma.issue(a.out.dhtb + hm_off, 0, kD, G0, w);
-    dma.issue(a.out.dhtb + hm_off, 64, kD, G1, w);
+    if (DO_K) {
+      dma.issue(a.out.dhb + hm_off, 0, kD, Q0, w);
+      dma.issue(a.out.dhb + hm_off, 64, kD, Q1, w);
+    }
+    if (DO_V) {
+      dma.issue(a.out.dhtb + hm_off, 0, kD, G0, w);
+      dma.issue(a.out.dhtb + hm_off, 64, kD, G1, w);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     // dv^T[j][key] += sum_i dH^T[j][i] relu(k)[i]
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 8 && DO_V; ++ks) {
       bf16x8 kr;
 #pragma unroll
       for (int e = 0; e < 8; ++e) kr[e] = float(kf[ks][e]) > 0.f ? kf[ks][e] : (__bf16)0.f;
@@ -643,7 +653,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
     // dk^T[i][key] += ([k_i > 0] (sum_j dH[i][j] v[j] + dZ[i])), one d-block at a time
     const float *dz = a.out.dz + (long long)bh * kD;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < 4 && DO_K; ++db) {
       f32x16 lk = f32x16{};
       const bf16_t *hs = (db < 2 ? Q0 : Q1) + (db & 1) * 32 * kD;
 #pragma unroll
@@ -660,8 +670,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bwd_dkv_kernel(BwdArgs a) {
     }
   }
   if (pk >= g.N) return;
-  store_grad_row(g, a.out.rope_tab, a.out.dk, b, h, pk, hl, dk);
-  store_grad_row(g, nullptr, a.out.dv, b, h, pk, hl, dv);
+  if (DO_K) store_grad_row(g, a.out.rope_tab, a.out.dk, b, h, pk, hl, dk);
+  if (DO_V) store_grad_row(g, nullptr, a.out.dv, b, h, pk, hl, dv);
 }
 
 // ---------------------------------------------------------------------------
@@ -708,10 +718,11 @@ hipError_t launch_attn_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, cons
     a.n_blocks = int(grid);
     if (mode) {
       attn_bwd_dq_kernel<2><<<grid, 128, size_t(g.k) * sizeof(int32_t), st>>>(a);
-      attn_bwd_dkv_kernel<2><<<grid, 128, size_t(g.nb) * sizeof(int32_t), st>>>(a);
+      attn_bwd_dkv_kernel<2, 0><<<grid, 128, size_t(g.nb) * sizeof(int32_t), st>>>(a);
     } else {
       attn_bwd_dq_kernel<4><<<grid, 256, 0, st>>>(a);
-      attn_bwd_dkv_kernel<4><<<grid, 256, 0, st>>>(a);
+      attn_bwd_dkv_kernel<4, 1><<<grid, 256, 0, st>>>(a);
+      attn_bwd_dkv_kernel<4, 2><<<grid, 256, 0, st>>>(a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
