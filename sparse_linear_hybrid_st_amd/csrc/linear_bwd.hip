@@ -111,7 +111,6 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
   __shared__ __attribute__((aligned(1024))) bf16_t Gt[TT * D];
   __shared__ __attribute__((aligned(16))) float Zs[D];
   __shared__ float wrow[TT];
-  __shared__ float bzx[D];
   const int s = blockIdx.x, bh = blockIdx.y, b = bh / g.H;
   const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -171,7 +170,7 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  float bz = 0.f;  // Bz[t & 127], rows of half t >> 7
+  float bz[4] = {0.f, 0.f, 0.f, 0.f};  // Bz[4(t%32) .. +3] over rows of group t/32
   __syncthreads();
 
   for (int base = n0; base < n1; base += TT) {
@@ -254,14 +253,18 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
 #pragma unroll
         for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma_32x32x16(av[bi], bv[bj], acc[bi][bj]);
     }
-    // Bz[f] += sum_rows (a/den)[row][f] * (dden den)[row]  (= dden a)
+    // Bz[f] += sum_rows (a/den)[row][f] * (dden den)[row]  (= dden a):
+    // thread t takes features 4(t%32) .. +3 (one 8-byte read a row) over
+    // the 16 rows of group t/32
     {
-      const int f = t & (D - 1), r0 = (t >> 7) * 64;
-#pragma unroll 8
-      for (int rr = 0; rr < 64; ++rr) {
+      const int f = 4 * (t & 31), r0 = (t >> 5) * 16;
+#pragma unroll 4
+      for (int rr = 0; rr < 16; ++rr) {
         const int row = r0 + rr;
-        const float av = bf16_to_f32(At[row * D + (((f >> 3) ^ kv_swz(row)) << 3) + (f & 7)]);
-        bz = fmaf(av, wrow[row], bz);
+        const bf16x4 a4 = *(const bf16x4 *)(At + row * D + (((f >> 3) ^ kv_swz(row)) << 3) + (f & 4));
+        const float wv = wrow[row];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bz[e] = fmaf(float(a4[e]), wv, bz[e]);
       }
     }
     __syncthreads();  // At, Gt, wrow are refilled next step
@@ -278,9 +281,18 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
         const int j = j0 + 32 * bj + l32;
         out[i * D + j] = acc[bi][bj][r];
       }
-  if (t >= D) bzx[t - D] = bz;
+  // the 8 row groups' partial sums, added in group order
+  float *bzs = (float *)At;  // [8][128], At is free after the last step
   __syncthreads();
-  if (t < D) out[D * D + t] = bz + bzx[t];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bzs[(t >> 5) * D + 4 * (t & 31) + e] = bz[e];
+  __syncthreads();
+  if (t < D) {
+    float acc_z = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc_z += bzs[i * D + t];
+    out[D * D + t] = acc_z;
+  }
 }
 
 // Per head, from the reduced A (fp32 [128][128]) and Bz: dH = s A W_p^T as
