@@ -235,14 +235,18 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16_t *Ts, const OperandOffs
 // double-buffered in LDS.
 // ---------------------------------------------------------------------------
 template <int NW>
-__global__ void __launch_bounds__(NW * 64, 2) attn_bwd_dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int BM = NW * 32;
   constexpr bool TOPK = NW == 2;
+  // Top-K workgroups (2 waves) keep one K and one V buffer: 32 KB lets four
+  // of them share a CU, whose other workgroups cover each one's DMA wait;
+  // window workgroups (4 waves) double-buffer.
+  constexpr bool SINGLE = TOPK;
   constexpr int TILE = kBN * kD;
   __shared__ __attribute__((aligned(1024))) bf16_t K0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16_t K1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t K1[SINGLE ? 8 : TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t V0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16_t V1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t V1[SINGLE ? 8 : TILE];
   extern __shared__ int32_t sel_lds[];  // Top-K: first key row of each selected block
   const Geom &g = a.g;
   const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, l32 = lane & 31;
@@ -363,25 +367,40 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bwd_dq_kernel(BwdArgs a) {
     dma.issue(hk, k_cur, g.N, K0, w);
     dma.issue(hv, k_cur, g.N, V0, w);
   }
-  for (int it = 0; it < n_tiles; it += 2) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    const int k_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
-    if (it + 1 < n_tiles) {
-      dma.issue(hk, k_nxt, g.N, K1, w);
-      dma.issue(hv, k_nxt, g.N, V1, w);
+  if constexpr (SINGLE) {
+    // one buffer: wait for tile it, compute, then (every wave done) refill
+    for (int it = 0; it < n_tiles; ++it) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      compute(k_cur, K0, V0);
+      if (it + 1 < n_tiles) {
+        k_cur = tile_start(it + 1);
+        __syncthreads();
+        dma.issue(hk, k_cur, g.N, K0, w);
+        dma.issue(hv, k_cur, g.N, V0, w);
+      }
     }
-    compute(k_cur, K0, V0);
-    if (it + 1 >= n_tiles) break;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    const int k_nn = it + 2 < n_tiles ? tile_start(it + 2) : 0;
-    if (it + 2 < n_tiles) {
-      dma.issue(hk, k_nn, g.N, K0, w);
-      dma.issue(hv, k_nn, g.N, V0, w);
+  } else {
+    for (int it = 0; it < n_tiles; it += 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const int k_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
+      if (it + 1 < n_tiles) {
+        dma.issue(hk, k_nxt, g.N, K1, w);
+        dma.issue(hv, k_nxt, g.N, V1, w);
+      }
+      compute(k_cur, K0, V0);
+      if (it + 1 >= n_tiles) break;
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const int k_nn = it + 2 < n_tiles ? tile_start(it + 2) : 0;
+      if (it + 2 < n_tiles) {
+        dma.issue(hk, k_nn, g.N, K0, w);
+        dma.issue(hv, k_nn, g.N, V0, w);
+      }
+      compute(k_nxt, K1, V1);
+      k_cur = k_nn;
     }
-    compute(k_nxt, K1, V1);
-    k_cur = k_nn;
   }
 
   // ---- epilogue: dq = scale * (sparse) + linear-branch term, rotated back
@@ -391,11 +410,13 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bwd_dq_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) dq[db][r] *= g.scale;
   const float sb = a.out.s_gate[b];
   if (!(sb < g.drop_tau)) {
-    // gm^T = M g^T with M rows 0..63 in K0 and 64..127 in K1
+    // gm^T = M g^T with M rows 0..63 in K0 and 64..127 in K1 (V0 when
+    // single-buffered)
     __syncthreads();  // every wave is done with the key tiles
+    bf16_t *const M1 = SINGLE ? V0 : K1;
     const bf16_t *mh = a.out.mb + (long long)bh * kD * kD;
     dma.issue(mh, 0, kD, K0, w);
-    dma.issue(mh, 64, kD, K1, w);
+    dma.issue(mh, 64, kD, M1, w);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     // one d-block of gm^T at a time (16 registers): a first pass forms
@@ -405,7 +426,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bwd_dq_kernel(BwdArgs a) {
     const float *zr = a.out.zv + (long long)bh * kD;
     const bf16_t *qrow = a.q + (hrow + pqc) * kD;
     auto gm_block = [&](int db) __attribute__((always_inline)) {
-      const bf16_t *ms = (db < 2 ? K0 : K1) + (db & 1) * 32 * kD;
+      const bf16_t *ms = (db < 2 ? K0 : M1) + (db & 1) * 32 * kD;
       f32x16 r = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) r = mfma_32x32x16(*(const bf16x8 *)(ms + oo.k_lane + 16 * (ks ^ oo.k_x)), gf[ks], r);
@@ -462,16 +483,22 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bwd_dq_kernel(BwdArgs a) {
 // computed in both passes.
 // ---------------------------------------------------------------------------
 template <int NW, int WHICH>
-__global__ void __launch_bounds__(NW * 64, WHICH == 0 ? 1 : 2) attn_bwd_dkv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WHICH == 0 ? 1 : 2, WHICH == 0 ? 1 : 2)))
+attn_bwd_dkv_kernel(BwdArgs a) {
   constexpr int BK = NW * 32;
   constexpr bool TOPK = NW == 2;
   constexpr bool DO_V = WHICH != 2, DO_K = WHICH != 1;
+  // Top-K workgroups of a single pass could keep one Q and one dO buffer
+  // (four workgroups per CU, as in the dQ kernel); the others double-buffer.
+  // Top-K heads run the joint pass: measured at 480p Top-K, the two
+  // single-buffered passes took 7.3 ms against 6.2 ms joint.
+  constexpr bool SINGLE = TOPK && WHICH != 0;
   constexpr int TILE = kBN * kD;
   __shared__ __attribute__((aligned(1024))) bf16_t Q0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16_t Q1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t Q1[SINGLE ? 8 : TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t G0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16_t G1[TILE];
-  __shared__ __attribute__((aligned(16))) float L0[kBN], L1[kBN], D0[kBN], D1[kBN];
+  __shared__ __attribute__((aligned(1024))) bf16_t G1[SINGLE ? 8 : TILE];
+  __shared__ __attribute__((aligned(16))) float L0[kBN], L1[SINGLE ? 4 : kBN], D0[kBN], D1[SINGLE ? 4 : kBN];
   extern __shared__ int32_t qsel_lds[];  // Top-K: first query row of each selecting block
   const Geom &g = a.g;
   const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, l32 = lane & 31;
@@ -603,19 +630,32 @@ __global__ void __launch_bounds__(NW * 64, WHICH == 0 ? 1 : 2) attn_bwd_dkv_kern
 
   int q_cur = n_tiles > 0 ? tile_start(0) : 0;
   if (n_tiles > 0) issue_tile(q_cur, Q0, G0, L0, D0);
-  for (int it = 0; it < n_tiles; it += 2) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    const int q_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
-    if (it + 1 < n_tiles) issue_tile(q_nxt, Q1, G1, L1, D1);
-    compute(q_cur, Q0, G0, L0, D0);
-    if (it + 1 >= n_tiles) break;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    const int q_nn = it + 2 < n_tiles ? tile_start(it + 2) : 0;
-    if (it + 2 < n_tiles) issue_tile(q_nn, Q0, G0, L0, D0);
-    compute(q_nxt, Q1, G1, L1, D1);
-    q_cur = q_nn;
+  if constexpr (SINGLE) {
+    for (int it = 0; it < n_tiles; ++it) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      compute(q_cur, Q0, G0, L0, D0);
+      if (it + 1 < n_tiles) {
+        q_cur = tile_start(it + 1);
+        __syncthreads();
+        issue_tile(q_cur, Q0, G0, L0, D0);
+      }
+    }
+  } else {
+    for (int it = 0; it < n_tiles; it += 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const int q_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
+      if (it + 1 < n_tiles) issue_tile(q_nxt, Q1, G1, L1, D1);
+      compute(q_cur, Q0, G0, L0, D0);
+      if (it + 1 >= n_tiles) break;
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const int q_nn = it + 2 < n_tiles ? tile_start(it + 2) : 0;
+      if (it + 2 < n_tiles) issue_tile(q_nn, Q0, G0, L0, D0);
+      compute(q_nxt, Q1, G1, L1, D1);
+      q_cur = q_nn;
+    }
   }
 
   // ---- epilogue: dk = scale * (sparse) + (dH v + dZ) [k > 0],
@@ -625,16 +665,19 @@ __global__ void __launch_bounds__(NW * 64, WHICH == 0 ? 1 : 2) attn_bwd_dkv_kern
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[db][r] *= g.scale;
   if (!(a.out.s_gate[b] < g.drop_tau)) {
-    // dH rows 0..63 in Q0, 64..127 in Q1; dH^T rows likewise in G0, G1
+    // dH rows 0..63 in Q0, 64..127 in Q1; dH^T rows likewise in G0, G1.
+    // Single-buffered (one of the two per pass): rows 64..127 in G0 / Q0.
     __syncthreads();  // every wave is done with the query tiles
+    bf16_t *const H0 = Q0, *const H1 = SINGLE ? G0 : Q1;
+    bf16_t *const T0 = SINGLE ? Q0 : G0, *const T1 = SINGLE ? G0 : G1;
     const long long hm_off = (long long)bh * kD * kD;
     if (DO_K) {
-      dma.issue(a.out.dhb + hm_off, 0, kD, Q0, w);
-      dma.issue(a.out.dhb + hm_off, 64, kD, Q1, w);
+      dma.issue(a.out.dhb + hm_off, 0, kD, H0, w);
+      dma.issue(a.out.dhb + hm_off, 64, kD, H1, w);
     }
     if (DO_V) {
-      dma.issue(a.out.dhtb + hm_off, 0, kD, G0, w);
-      dma.issue(a.out.dhtb + hm_off, 64, kD, G1, w);
+      dma.issue(a.out.dhtb + hm_off, 0, kD, T0, w);
+      dma.issue(a.out.dhtb + hm_off, 64, kD, T1, w);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
@@ -646,7 +689,7 @@ __global__ void __launch_bounds__(NW * 64, WHICH == 0 ? 1 : 2) attn_bwd_dkv_kern
       for (int e = 0; e < 8; ++e) kr[e] = float(kf[ks][e]) > 0.f ? kf[ks][e] : (__bf16)0.f;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16_t *ht = (db < 2 ? G0 : G1) + (db & 1) * 32 * kD;
+        const bf16_t *ht = (db < 2 ? T0 : T1) + (db & 1) * 32 * kD;
         dv[db] = mfma_32x32x16(*(const bf16x8 *)(ht + oo.k_lane + 16 * (ks ^ oo.k_x)), kr, dv[db]);
       }
     }
@@ -655,7 +698,7 @@ __global__ void __launch_bounds__(NW * 64, WHICH == 0 ? 1 : 2) attn_bwd_dkv_kern
 #pragma unroll
     for (int db = 0; db < 4 && DO_K; ++db) {
       f32x16 lk = f32x16{};
-      const bf16_t *hs = (db < 2 ? Q0 : Q1) + (db & 1) * 32 * kD;
+      const bf16_t *hs = (db < 2 ? H0 : H1) + (db & 1) * 32 * kD;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) lk = mfma_32x32x16(*(const bf16x8 *)(hs + oo.k_lane + 16 * (ks ^ oo.k_x)), vf[ks], lk);
 #pragma unroll
