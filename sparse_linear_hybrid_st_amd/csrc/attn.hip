@@ -323,7 +323,11 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   // same values the PV product weighs V with.
   auto softmax = [&](int k0, bool full, f32x16 (&s)[2], bf16x8 (&pb)[4]) {
     if (!full) {
-      const int jl = k0 + 4 * hl;                        // j = jl + c below
+      int jl = k0 + 4 * hl;                              // j = jl + c below
+      // opaque to the optimiser: otherwise it carries the 32 per-score
+      // differences below across tiles as induction variables, updating
+      // them on every tile although only edge tiles use them
+      asm volatile("" : "+v"(jl));
       const unsigned wb = unsigned(pq - jl + g.r);        // pq - j + r = wb - c
       const int lim = g.N - jl;                          // j < N  <=>  c < lim
 #pragma unroll
