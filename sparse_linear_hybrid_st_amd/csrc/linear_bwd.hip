@@ -97,7 +97,10 @@ __global__ void __launch_bounds__(256) lin_bwd_prep_kernel(Geom g, const float *
 // for gm^T = M g^T on MFMA (M rows from LDS, g rows as B operands) and the
 // dot products; it then leaves a_n / den_n and g_n (bf16) in LDS, and
 // each wave adds its 64 x 64 quadrant of A over the 128 rows with
-// transposing reads.  Fixed order throughout.
+// transposing reads.  Each step's rows (dO, q and out) are loaded into
+// registers during the step before, so the global loads overlap the MFMA
+// work (one wave per SIMD here: nothing else hides them).  Fixed order
+// throughout.
 __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16_t *__restrict__ q,
                                                               const bf16_t *__restrict__ go,
                                                               const bf16_t *__restrict__ mb,
@@ -118,7 +121,7 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
   const int h = bh % g.H;
   const bf16_t *outb = (const bf16_t *)outv.base;
   // dO . out over this lane's features f = 32db + 8r4 + 4hl + e of row n,
-  // completed across the two half-waves (same row)
+  // completed across the two half-waves (same row); dropped samples only
   auto go_out = [&](int n) __attribute__((always_inline)) {
     const bf16_t *gr = go + ((long long)bh * g.N + n) * D;
     const bf16_t *orow = outb + row_offset(g, outv, b, h, n);
@@ -173,15 +176,36 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
   float bz[4] = {0.f, 0.f, 0.f, 0.f};  // Bz[4(t%32) .. +3] over rows of group t/32
   __syncthreads();
 
-  for (int base = n0; base < n1; base += TT) {
+  // one step's rows in registers: dO as B operands (features 16ks + 8hl + e)
+  // and q in the accumulator layout (features 32db + 8r4 + 4hl + e)
+  struct Rows {
+    bf16x8 gf[8];
+    bf16x4 qv[4][4];
+  };
+  auto load_rows = [&](int base, Rows &R) __attribute__((always_inline)) {
+    const int n = base + 32 * w + l32;
+    const long long nc = hrow + (n < n1 ? n : n0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) R.gf[ks] = *(const bf16x8 *)(go + nc * D + (2 * ks + hl) * 8);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) R.qv[db][r4] = *(const bf16x4 *)(q + nc * D + 32 * db + 8 * r4 + 4 * hl);
+  };
+  auto step = [&](int base, Rows &R) __attribute__((always_inline)) {
     const int rl = 32 * w + l32, n = base + rl;
     const bool valid = n < n1;
-    const int nc = valid ? n : n0;
-    bf16x8 gf[8];
+    // this step's out row (dO layout: its dot with dO needs only matching
+    // features), issued before the MFMAs that hide its latency
+    bf16x8 of[8];
+    if (outb) {
+      const bf16_t *orow = outb + row_offset(g, outv, b, h, valid ? n : n0);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      gf[ks] = *(const bf16x8 *)(go + (hrow + nc) * D + (2 * ks + hl) * 8);
-      if (!valid) gf[ks] = bf16x8{};
+      for (int ks = 0; ks < 8; ++ks) of[ks] = *(const bf16x8 *)(orow + (2 * ks + hl) * 8);
+    }
+    if (!valid) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) R.gf[ks] = bf16x8{};
     }
     // gm^T[f][n] = sum_j M[f][j] g_n[j]
     f32x16 gm[4];
@@ -190,20 +214,18 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) gm[db] = mfma_32x32x16(*(const bf16x8 *)(Ms + ro.at(db, ks)), gf[ks], gm[db]);
+      for (int db = 0; db < 4; ++db) gm[db] = mfma_32x32x16(*(const bf16x8 *)(Ms + ro.at(db, ks)), R.gf[ks], gm[db]);
     // this lane's features f = 32db + 8r4 + 4hl + e
-    bf16x4 qv[4][4];
     float tp = 0.f, dp = 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int f = 32 * db + 8 * r4 + 4 * hl;
-        qv[db][r4] = *(const bf16x4 *)(q + (hrow + nc) * D + f);
         const f32x4 z4 = *(const f32x4 *)(Zs + f);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float av = fmaxf(float(qv[db][r4][e]), 0.f);
+          const float av = fmaxf(float(R.qv[db][r4][e]), 0.f);
           tp = fmaf(av, gm[db][4 * r4 + e], tp);
           dp = fmaf(av, z4[e], dp);
         }
@@ -214,9 +236,18 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
     const float dden = -sb * tp / (den * den);
     const float inv_den = 1.f / den;
     if (outb) {
-      const float dv = go_out(nc) - sb * tp * inv_den;
-      if (valid && hl == 0) dsum[(long long)bh * Np + n] = dv;
+      typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+      float go_dot = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          go_dot = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{R.gf[ks][e], R.gf[ks][e + 1]},
+                                                   bf16x2{of[ks][e], of[ks][e + 1]}, go_dot, false);
+      go_dot += __shfl_xor(go_dot, 32);
+      if (valid && hl == 0) dsum[(long long)bh * Np + n] = go_dot - sb * tp * inv_den;
     }
+    const float a_scale = valid ? inv_den : 0.f;  // rows past the range add nothing
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -224,12 +255,12 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
         const int f = 32 * db + 8 * r4 + 4 * hl;
         bf16x4 ap;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ap[e] = (__bf16)(valid ? fmaxf(float(qv[db][r4][e]), 0.f) * inv_den : 0.f);
+        for (int e = 0; e < 4; ++e) ap[e] = (__bf16)(fmaxf(float(R.qv[db][r4][e]), 0.f) * a_scale);
         *(bf16x4 *)(At + rl * D + (((f >> 3) ^ kv_swz(rl)) << 3) + (f & 4)) = ap;
       }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      *(bf16x8 *)(Gt + rl * D + (((2 * ks + hl) ^ kv_swz(rl)) << 3)) = gf[ks];
+      *(bf16x8 *)(Gt + rl * D + (((2 * ks + hl) ^ kv_swz(rl)) << 3)) = R.gf[ks];
     if (hl == 0) wrow[rl] = valid ? dden * den : 0.f;
     __syncthreads();
     // A[i][j] += sum_rows (a/den)[row][i] g[row][j]
@@ -268,6 +299,16 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
       }
     }
     __syncthreads();  // At, Gt, wrow are refilled next step
+  };
+  // two named register sets, alternating: step on one while the other loads
+  Rows R0, R1;
+  if (n0 < n1) load_rows(n0, R0);
+  for (int base = n0; base < n1; base += 2 * TT) {
+    if (base + TT < n1) load_rows(base + TT, R1);
+    step(base, R0);
+    if (base + TT >= n1) break;
+    if (base + 2 * TT < n1) load_rows(base + 2 * TT, R0);
+    step(base + TT, R1);
   }
 
   float *out = partial + ((long long)bh * S + s) * (D * D + D);
@@ -378,9 +419,16 @@ hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *go, c
                              hipStream_t st) {
   if (g.D != D) return hipErrorInvalidValue;
   const int BH = g.B * g.H;
-  const int S = linear_splits(g);
+  // one workgroup per CU (LDS-bound) and one round of them: at most 256
+  // workgroups, each over a longer row range (S never exceeds the split
+  // count the partial-sum workspace is sized for)
+  const int chunks = (g.N + 127) / 128;
+  int S = 256 / BH;
+  S = S < 1 ? 1 : (S > chunks ? chunks : S);
+  if (S > linear_splits(g)) S = linear_splits(g);
   int chunk = (g.N + S - 1) / S;
   chunk = (chunk + 127) / 128 * 128;
+  S = (g.N + chunk - 1) / chunk;
   lin_bwd_prep_kernel<<<dim3(16, BH), 256, 0, st>>>(g, hm, w_p, s_gate, w.mf, w.mb);
   lin_bwd_rows_kernel<<<dim3(S, BH), 256, 0, st>>>(g, q, go, w.mb, zv, s_gate, w.partial, S, chunk, outv,
                                                     dsum, Np);
