@@ -634,7 +634,7 @@ namespace {
 // the per-head linear state and backward matrices, the gate's column sums
 // and values, and the RoPE table.
 struct BwdPlan {
-  size_t wq, wk, wv, wg, lse, dsum, idx, inv_off, inv_list, h, z;
+  size_t wq, wk, wv, wg, wqr, wkr, lse, dsum, idx, inv_off, inv_list, h, z;
   size_t mf, mb, a_red, bz, dhb, dhtb, dwp_h, ds_part, colsum, s, dt, rope_tab;
   int Np;
   size_t total;
@@ -659,6 +659,8 @@ BwdPlan bwd_plan(const Info &inf) {
   pl.wk = take(rows * D * 2);
   pl.wv = take(rows * D * 2);
   pl.wg = take(rows * D * 2);
+  pl.wqr = take(inf.rope ? rows * D * 2 : 0);  // rotated Q, K in the boundary layout
+  pl.wkr = take(inf.rope ? rows * D * 2 : 0);
   pl.lse = take(BH * pl.Np * sizeof(float));
   pl.dsum = take(BH * pl.Np * sizeof(float));
   pl.idx = take(inf.any_topk ? BH * g.nb * g.k * sizeof(int32_t) : 0);
@@ -758,23 +760,42 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
              hipSuccess) {
     return hip_status(e, "salad_attn_backward: copy s");
   }
-  // working copies: rotated Q, K; V; dO
-  if ((inf.rope && (e = launch_rope_table(g, tab, stream)) != hipSuccess) ||
-      (e = launch_permute(g, 1, inf.rope, 0, q, wq, stream, tab)) != hipSuccess ||
-      (e = launch_permute(g, 1, inf.rope, 0, k, wk, stream, tab)) != hipSuccess ||
-      (e = launch_permute(g, 1, 0, 0, v, wv, stream)) != hipSuccess ||
-      (e = launch_permute(g, 1, 0, 0, dout, wg, stream)) != hipSuccess)
+  // Q and K rotated first (boundary layout) when RoPE is on.  Heads whose
+  // working order is the token order are then read in place; the temporal
+  // heads get working copies: Q and dO from the permute, K and V from the
+  // linear-state pass, which reads every head's K and V anyway.
+  const void *qsrc = q, *ksrc = k;
+  if (inf.rope) {
+    if ((e = launch_rope_table(g, tab, stream)) != hipSuccess ||
+        (e = launch_rope_rows(g, 1, q, w + pl.wqr, tab, stream)) != hipSuccess ||
+        (e = launch_rope_rows(g, 1, k, w + pl.wkr, tab, stream)) != hipSuccess)
+      return hip_status(e, "salad_attn_backward: rope");
+    qsrc = w + pl.wqr;
+    ksrc = w + pl.wkr;
+  }
+  const View qb = boundary_view(g, qsrc), kb = boundary_view(g, ksrc), vb = boundary_view(g, v);
+  View kd = kb, vd = vb;
+  kd.perm = vd.perm = 0;
+  uint64_t work[4];
+  const bool direct = kv_direct_ok(g, kd, vd);
+  for (int i = 0; i < 4; ++i) work[i] = direct ? g.temporal[i] : ~0ull;
+  bool any_work = false;
+  for (int i = 0; i < 4; ++i) any_work |= work[i] != 0;
+  if (any_work && ((e = launch_permute(g, 1, 0, 0, qsrc, wq, stream, nullptr, work)) != hipSuccess ||
+                   (e = launch_permute(g, 1, 0, 0, dout, wg, stream, nullptr, work)) != hipSuccess))
     return hip_status(e, "salad_attn_backward: permute");
-  const View qv = working_view(g, wq), kv = working_view(g, wk), vv = working_view(g, wv);
-  if ((e = launch_linear_state(g, 1, kv, vv, (float *)scratch, hm, zv, stream)) != hipSuccess)
+  const View kv = working_view(g, wk), vv = working_view(g, wv);
+  if ((e = launch_linear_partials(g, kb, vb, (float *)scratch, wk, wv, work, nullptr, stream)) != hipSuccess ||
+      (e = launch_linear_reduce(g, linear_splits(g), (const float *)scratch, hm, zv, stream)) != hipSuccess)
     return hip_status(e, "salad_attn_backward: linear state");
   int32_t *inv_off = nullptr, *inv_list = nullptr;
   if (inf.any_topk) {
+    // Top-K heads are never temporal: their working rows are the token rows
     double *qm, *km, *sc;
     select_regions(g, scratch, &qm, &km, &sc);
     inv_off = (int32_t *)(w + pl.inv_off);
     inv_list = (int32_t *)(w + pl.inv_list);
-    if ((e = launch_block_select(g, 1, qv, kv, qm, km, sc, idx, stream)) != hipSuccess ||
+    if ((e = launch_block_select(g, 1, qb, kb, qm, km, sc, idx, stream)) != hipSuccess ||
         (e = launch_topk_inverse(g, idx, inv_off, inv_list, stream)) != hipSuccess)
       return hip_status(e, "salad_attn_backward: block select");
   }
@@ -798,8 +819,8 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
                                      size_t(g.N) * sizeof(float), size_t(g.B) * g.H, hipMemcpyDeviceToDevice,
                                      stream)) != hipSuccess)
     return hip_status(e, "salad_attn_backward: copy lse");
-  if ((e = launch_linear_bwd(g, wq, wg, hm, zv, (const bf16_t *)w_p, s, lw, dw_p, outv, dsum, pl.Np, stream)) !=
-      hipSuccess)
+  if ((e = launch_linear_bwd(g, wq, wg, (const bf16_t *)qsrc, (const bf16_t *)dout, work, hm, zv,
+                             (const bf16_t *)w_p, s, lw, dw_p, outv, dsum, pl.Np, stream)) != hipSuccess)
     return hip_status(e, "salad_attn_backward: linear branch");
   // sparse branch (normalisers and D, then dQ and dK, dV, whose epilogues add
   // the linear branch's per-row terms and write the final rows)
@@ -814,9 +835,11 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
   bo.dq = (bf16_t *)dq;
   bo.dk = (bf16_t *)dk;
   bo.dv = (bf16_t *)dv;
-  if ((!saved && (e = launch_attn_bwd_prep(g, qv, kv, vv, idx, wg, lse, dsum, pl.Np, stream)) != hipSuccess) ||
+  if ((!saved && (e = launch_attn_bwd_prep(g, qb, kv, vv, kd, vd, work, idx, wg, (const bf16_t *)dout, lse,
+                                          dsum, pl.Np, stream)) != hipSuccess) ||
       (e = prof_mark(0, stream)) != hipSuccess ||
-      (e = launch_attn_bwd(g, wq, wk, wv, wg, lse, dsum, pl.Np, idx, inv_off, inv_list, bo, stream)) !=
+      (e = launch_attn_bwd(g, wq, wk, wv, wg, (const bf16_t *)qsrc, (const bf16_t *)ksrc, (const bf16_t *)v,
+                           (const bf16_t *)dout, work, lse, dsum, pl.Np, idx, inv_off, inv_list, bo, stream)) !=
           hipSuccess ||
       (e = prof_mark(1, stream)) != hipSuccess)
     return hip_status(e, "salad_attn_backward: sparse attention");

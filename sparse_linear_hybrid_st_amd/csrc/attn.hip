@@ -98,7 +98,8 @@ struct AttnArgs {
   const float *s_gate;   // fused: [B] gate values (branch dropping below g.drop_tau)
   View out;              // fused: output rows (boundary layout, scattered)
   View out_l;            // fused, full-width projection: s_b * O_l rows (base NULL otherwise)
-  const bf16_t *go;      // backward prep: dL/dO_s, working layout [B*H][N][128]
+  const bf16_t *go;      // backward prep: dL/dO_s, working layout [B*H][N][128] (heads in work)
+  const bf16_t *god;     // backward prep: dL/dO_s, boundary layout [B,N,H,128] (other heads)
   float *lse2;           // backward prep: [B*H][lse_stride] log2 of each row's softmax normaliser;
                          // fused: optional [B*H][N] copy of the same for a later backward
   float *dsum;           // backward prep: [B*H][lse_stride] D = dO . O_s per row
@@ -588,7 +589,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     // both half-waves of a query column return together, so the exchange
     // below sees its partner
     if (pq >= g.N) return;
-    const bf16_t *grow = a.go + ((long long)bh * g.N + pq) * kD;
+    const bf16_t *grow = from_work ? a.go + ((long long)bh * g.N + pq) * kD
+                                   : a.god + (((long long)b * g.N + pq) * g.H + h) * kD;
     float dp = 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -678,17 +680,28 @@ hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv
   return launch_bf16<0>(a, st);
 }
 
-hipError_t launch_attn_bwd_prep(const Geom &g, View qv, View kv, View vv, const int32_t *idx,
-                                const bf16_t *go, float *lse2, float *dsum, int stride, hipStream_t st) {
-  if (!kv_streamable(g, kv, vv)) return hipErrorInvalidValue;
+hipError_t launch_attn_bwd_prep(const Geom &g, View qv, View kw, View vw, View kd, View vd,
+                                const uint64_t work[4], const int32_t *idx, const bf16_t *go,
+                                const bf16_t *god, float *lse2, float *dsum, int stride, hipStream_t st) {
+  bool any_work = false, any_direct = false;
+  for (int h = 0; h < g.H; ++h) {
+    const bool w = (work[h >> 6] >> (h & 63)) & 1ull;
+    any_work |= w;
+    any_direct |= !w;
+  }
+  if ((any_work && !kv_streamable(g, kw, vw)) || (any_direct && !kv_streamable(g, kd, vd)))
+    return hipErrorInvalidValue;
   AttnArgs a = {};
   a.g = g;
   a.q = qv;
-  a.k = a.kd = kv;
-  a.v = a.vd = vv;
-  for (int i = 0; i < 4; ++i) a.work[i] = ~0ull;
+  a.k = kw;
+  a.v = vw;
+  a.kd = kd;
+  a.vd = vd;
+  for (int i = 0; i < 4; ++i) a.work[i] = work[i];
   a.idx = idx;
   a.go = go;
+  a.god = god;
   a.lse2 = lse2;
   a.dsum = dsum;
   a.lse_stride = stride;

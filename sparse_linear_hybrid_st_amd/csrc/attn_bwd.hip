@@ -38,7 +38,9 @@ namespace salad {
 
 struct BwdArgs {
   Geom g;
-  const bf16_t *q, *k, *v, *go;  // working layout [B*H][N][128] (Q, K rotated)
+  const bf16_t *q, *k, *v, *go;      // working layout [B*H][N][128] (Q, K rotated): heads in `work`
+  const bf16_t *qd, *kd, *vd, *god;  // boundary layout [B][N][H][128] (Q, K rotated): other heads
+  uint64_t work[4];                  // heads read from the working copies
   const float *lse2, *dsum;      // [B*H][Np]: normaliser (log2 units) and D per row
   int Np;                        // row stride of lse2 / dsum: N rounded up to 64
   const int32_t *idx;            // Top-K selection [B*H][nb][k]
@@ -118,12 +120,41 @@ __global__ void __launch_bounds__(256) topk_inverse_scan_kernel(Geom g, int32_t 
   }
 }
 
+// Rows of one (b, h): the working copy (rows 128 apart) for heads in
+// `work`, else the boundary layout in place (rows H*128 apart), which holds
+// those heads' rows in their working order, the token order.
+struct HeadRows {
+  const bf16_t *q, *k, *v, *go;
+  int stride;
+};
+__device__ __forceinline__ HeadRows head_rows(const BwdArgs &a, int b, int h) {
+  const Geom &g = a.g;
+  HeadRows r;
+  if (bit(a.work, h)) {
+    const long long o = ((long long)b * g.H + h) * g.N * kD;
+    r.q = a.q + o;
+    r.k = a.k + o;
+    r.v = a.v + o;
+    r.go = a.go + o;
+    r.stride = kD;
+  } else {
+    const long long o = ((long long)b * g.N * g.H + h) * kD;
+    r.q = a.qd + o;
+    r.k = a.kd + o;
+    r.v = a.vd + o;
+    r.go = a.god + o;
+    r.stride = g.H * kD;
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Shared tile machinery.  A 64 x 128 bf16 tile of working rows (K, V, Q or
 // dO) is staged in LDS row-major with the kv_swz unit swizzle; DMA op i of
 // wave w fills rows 4*(i*NW + w) .. +3 (lane l: row + l/16, physical unit
-// l%16, which holds logical unit (l%16) ^ kv_swz(row)).  Rows past N re-read
-// row N-1: finite values whose pairs are masked.
+// l%16, which holds logical unit (l%16) ^ kv_swz(row)); source rows are
+// `stride` elements apart.  Rows past N re-read row N-1: finite values whose
+// pairs are masked.
 // ---------------------------------------------------------------------------
 template <int NW>
 struct TileDma {
@@ -136,11 +167,12 @@ struct TileDma {
       unit[i] = (lane & 15) ^ kv_swz(row[i]);
     }
   }
-  __device__ __forceinline__ void issue(const bf16_t *head, int r0, int N, bf16_t *dst, int w) const {
+  __device__ __forceinline__ void issue(const bf16_t *head, int r0, int N, bf16_t *dst, int w,
+                                        int stride = kD) const {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int r = min(r0 + row[i], N - 1);
-      __builtin_amdgcn_global_load_lds((const void *)(head + (long long)r * kD + unit[i] * 8),
+      __builtin_amdgcn_global_load_lds((const void *)(head + (long long)r * stride + unit[i] * 8),
                                        (lds_void *)(dst + (4 * (i * NW + w)) * kD), 16, 0, 0);
     }
   }
@@ -255,15 +287,16 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
   const int qt = tile % a.tiles_per_head, bhs = tile / a.tiles_per_head;
   const int h = a.heads[bhs % a.n_heads_sel], b = bhs / a.n_heads_sel;
   const int q0 = qt * BM, bh = b * g.H + h;
-  const long long hrow = (long long)bh * g.N;
-  const bf16_t *hk = a.k + hrow * kD, *hv = a.v + hrow * kD;
+  const HeadRows hr = head_rows(a, b, h);
+  const bf16_t *hk = hr.k, *hv = hr.v;
+  const int rs = hr.stride;
   const int pq = q0 + 32 * w + l32, pqc = min(pq, g.N - 1);
 
   bf16x8 qf[8], gf[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    qf[ks] = *(const bf16x8 *)(a.q + (hrow + pqc) * kD + (2 * ks + hl) * 8);
-    gf[ks] = *(const bf16x8 *)(a.go + (hrow + pqc) * kD + (2 * ks + hl) * 8);
+    qf[ks] = *(const bf16x8 *)(hr.q + (long long)pqc * rs + (2 * ks + hl) * 8);
+    gf[ks] = *(const bf16x8 *)(hr.go + (long long)pqc * rs + (2 * ks + hl) * 8);
   }
   const float lse = a.lse2[(long long)bh * a.Np + pqc];
   const float dsv = a.dsum[(long long)bh * a.Np + pqc];
@@ -364,8 +397,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
 
   int k_cur = n_tiles > 0 ? tile_start(0) : 0;
   if (n_tiles > 0) {
-    dma.issue(hk, k_cur, g.N, K0, w);
-    dma.issue(hv, k_cur, g.N, V0, w);
+    dma.issue(hk, k_cur, g.N, K0, w, rs);
+    dma.issue(hv, k_cur, g.N, V0, w, rs);
   }
   if constexpr (SINGLE) {
     // one buffer: wait for tile it, compute, then (every wave done) refill
@@ -376,8 +409,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
       if (it + 1 < n_tiles) {
         k_cur = tile_start(it + 1);
         __syncthreads();
-        dma.issue(hk, k_cur, g.N, K0, w);
-        dma.issue(hv, k_cur, g.N, V0, w);
+        dma.issue(hk, k_cur, g.N, K0, w, rs);
+        dma.issue(hv, k_cur, g.N, V0, w, rs);
       }
     }
   } else {
@@ -386,8 +419,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
       __syncthreads();
       const int k_nxt = it + 1 < n_tiles ? tile_start(it + 1) : 0;
       if (it + 1 < n_tiles) {
-        dma.issue(hk, k_nxt, g.N, K1, w);
-        dma.issue(hv, k_nxt, g.N, V1, w);
+        dma.issue(hk, k_nxt, g.N, K1, w, rs);
+        dma.issue(hv, k_nxt, g.N, V1, w, rs);
       }
       compute(k_cur, K0, V0);
       if (it + 1 >= n_tiles) break;
@@ -395,8 +428,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
       __syncthreads();
       const int k_nn = it + 2 < n_tiles ? tile_start(it + 2) : 0;
       if (it + 2 < n_tiles) {
-        dma.issue(hk, k_nn, g.N, K0, w);
-        dma.issue(hv, k_nn, g.N, V0, w);
+        dma.issue(hk, k_nn, g.N, K0, w, rs);
+        dma.issue(hv, k_nn, g.N, V0, w, rs);
       }
       compute(k_nxt, K1, V1);
       k_cur = k_nn;
@@ -424,7 +457,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
     // features and the other half-wave's (same query), a second pass
     // recomputes the block and adds the term
     const float *zr = a.out.zv + (long long)bh * kD;
-    const bf16_t *qrow = a.q + (hrow + pqc) * kD;
+    const bf16_t *qrow = hr.q + (long long)pqc * rs;
     auto gm_block = [&](int db) __attribute__((always_inline)) {
       const bf16_t *ms = (db < 2 ? K0 : M1) + (db & 1) * 32 * kD;
       f32x16 r = f32x16{};
@@ -507,16 +540,17 @@ attn_bwd_dkv_kernel(BwdArgs a) {
   const int kt = tile % a.tiles_per_head, bhs = tile / a.tiles_per_head;
   const int h = a.heads[bhs % a.n_heads_sel], b = bhs / a.n_heads_sel;
   const int k0 = kt * BK, bh = b * g.H + h;
-  const long long hrow = (long long)bh * g.N;
-  const bf16_t *hq = a.q + hrow * kD, *hg = a.go + hrow * kD;
+  const HeadRows hr = head_rows(a, b, h);
+  const bf16_t *hq = hr.q, *hg = hr.go;
+  const int rs = hr.stride;
   const float *hl2 = a.lse2 + (long long)bh * a.Np, *hds = a.dsum + (long long)bh * a.Np;
   const int pk = k0 + 32 * w + l32, pkc = min(pk, g.N - 1);
 
   bf16x8 kf[8], vf[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    kf[ks] = *(const bf16x8 *)(a.k + (hrow + pkc) * kD + (2 * ks + hl) * 8);
-    if (DO_K) vf[ks] = *(const bf16x8 *)(a.v + (hrow + pkc) * kD + (2 * ks + hl) * 8);
+    kf[ks] = *(const bf16x8 *)(hr.k + (long long)pkc * rs + (2 * ks + hl) * 8);
+    if (DO_K) vf[ks] = *(const bf16x8 *)(hr.v + (long long)pkc * rs + (2 * ks + hl) * 8);
   }
   const float c2 = g.scale * 1.4426950408889634f;
 
@@ -544,8 +578,8 @@ attn_bwd_dkv_kernel(BwdArgs a) {
   // lse2 and D of a query tile: 16 lanes of wave 0 move 64 floats each
   // (the arrays are padded to a multiple of 64 rows per head)
   auto issue_tile = [&](int q0, bf16_t *Qd, bf16_t *Gd, float *Ld, float *Dd) {
-    dma.issue(hq, q0, g.N, Qd, w);
-    dma.issue(hg, q0, g.N, Gd, w);
+    dma.issue(hq, q0, g.N, Qd, w, rs);
+    dma.issue(hg, q0, g.N, Gd, w, rs);
     if (w == 0 && lane < 16) {
       __builtin_amdgcn_global_load_lds((const void *)(hl2 + q0 + 4 * lane), (lds_void *)Ld, 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void *)(hds + q0 + 4 * lane), (lds_void *)Dd, 16, 0, 0);
@@ -704,7 +738,7 @@ attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int f = 32 * db + 8 * r4 + 4 * hl;
-        const bf16x4 k4 = *(const bf16x4 *)(a.k + (hrow + pkc) * kD + f);
+        const bf16x4 k4 = *(const bf16x4 *)(hr.k + (long long)pkc * rs + f);
         const f32x4 z4 = *(const f32x4 *)(dz + f);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -731,8 +765,9 @@ hipError_t launch_topk_inverse(const Geom &g, const int32_t *idx, int32_t *off, 
 }
 
 hipError_t launch_attn_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, const bf16_t *v,
-                           const bf16_t *go, const float *lse2, const float *dsum, int Np,
-                           const int32_t *idx, const int32_t *inv_off, const int32_t *inv_list,
+                           const bf16_t *go, const bf16_t *qd, const bf16_t *kd, const bf16_t *vd,
+                           const bf16_t *god, const uint64_t work[4], const float *lse2, const float *dsum,
+                           int Np, const int32_t *idx, const int32_t *inv_off, const int32_t *inv_list,
                            const BwdOut &out, hipStream_t st) {
   if (g.D != kD) return hipErrorInvalidValue;
   BwdArgs a = {};
@@ -741,6 +776,11 @@ hipError_t launch_attn_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, cons
   a.k = k;
   a.v = v;
   a.go = go;
+  a.qd = qd;
+  a.kd = kd;
+  a.vd = vd;
+  a.god = god;
+  for (int i = 0; i < 4; ++i) a.work[i] = work[i];
   a.lse2 = lse2;
   a.dsum = dsum;
   a.Np = Np;

@@ -105,6 +105,11 @@ __device__ __forceinline__ bool bit(const uint64_t *m, int h) {
   return (m[h >> 6] >> (h & 63)) & 1ull;
 }
 
+// A set of heads passed by value to a kernel (bit h: head h).
+struct HeadSet {
+  uint64_t w[4];
+};
+
 // Working position p of a temporal head holds this token.
 __device__ __forceinline__ int st_token(const Geom &g, int p) {
   const int q = int(fdiv(g.fdF, uint32_t(p)));

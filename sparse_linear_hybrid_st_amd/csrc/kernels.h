@@ -37,8 +37,10 @@ inline size_t gate_ws_bytes(const Geom &g) { return size_t(g.B) * gate_splits(g)
 int rope_table_entries(const Geom &g);
 hipError_t launch_rope_table(const Geom &g, double2 *table, hipStream_t st);
 // table: optional RoPE table (NULL: angles computed per element; same values).
+// heads: optional set of heads to move (NULL: all).
 hipError_t launch_permute(const Geom &g, int bf16, int rope, int inverse, const void *src,
-                          void *dst, hipStream_t st, const double2 *table = nullptr);
+                          void *dst, hipStream_t st, const double2 *table = nullptr,
+                          const uint64_t *heads = nullptr);
 // RoPE without reordering: src and dst both [B,N,H,d] (bf16 or f32).
 hipError_t launch_rope_rows(const Geom &g, int bf16, const void *src, void *dst,
                             const double2 *table, hipStream_t st);
@@ -74,13 +76,20 @@ hipError_t launch_attn_fused(const Geom &g, View qv, View kw, View vw, View kd, 
                              const uint64_t work[4], const int32_t *idx, const bf16_t *hp,
                              const float *z, const float *s_gate, View outv, View outl, float *lse_out,
                              hipStream_t st);
-// Backward preparation (bf16, d = 128, working-layout views): the forward
-// sparse attention per row, reduced to lse2 (log2 of the softmax
-// normaliser in units of scale*log2(e) scores) and D = dO . O_s, with dO
-// (go) in working layout; lse2 / dsum rows are `stride` apart per head.
-hipError_t launch_attn_bwd_prep(const Geom &g, View qv, View kv, View vv, const int32_t *idx,
-                                const bf16_t *go, float *lse2, float *dsum, int stride, hipStream_t st);
-// ---- backward (bf16, d = 128, working layout) ------------------------------
+// Backward preparation (bf16, d = 128): the forward sparse attention per
+// row, reduced to lse2 (log2 of the softmax normaliser in units of
+// scale*log2(e) scores) and D = dO . O_s; lse2 / dsum rows are `stride`
+// apart per head.  K, V and dO of the heads in `work` come from working
+// copies (kw, vw, go [B*H][N][128]), the other heads' in place (kd, vd, god
+// in the boundary layout), as in launch_attn_fused.
+hipError_t launch_attn_bwd_prep(const Geom &g, View qv, View kw, View vw, View kd, View vd,
+                                const uint64_t work[4], const int32_t *idx, const bf16_t *go,
+                                const bf16_t *god, float *lse2, float *dsum, int stride, hipStream_t st);
+// ---- backward (bf16, d = 128) ------------------------------------------------
+// Every backward kernel reads the rows of a head in `work` (the temporal
+// heads) from working copies [B*H][N][128] and the other heads' rows in
+// place from the boundary layout [B,N,H,128], where they already sit in
+// their working order (the token order), H*128 elements apart.
 // Fixed-order sum of S split partials [B*H][S][D*D + D] into h and z.
 hipError_t launch_linear_reduce(const Geom &g, int S, const float *partial, float *h, float *z,
                                 hipStream_t st);
@@ -103,8 +112,10 @@ struct LinBwdScratch {
 // W_p (mb), A and Bz = dZ (bz), dH and dH^T (dhb, dhtb), dw_p [d][d] and
 // ws.ds_part (16 partial sums of dL/ds per head; zero for dropped samples).
 // outv.base non-NULL (the forward's output, boundary layout): also each
-// working row's D = dO . O_s into dsum (rows Np apart per head).
-hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *go, const float *hm,
+// working row's D = dO . O_s into dsum (rows Np apart per head).  Q and dO:
+// q, go (working copies) for heads in `work`, qd, god (boundary) otherwise.
+hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *go, const bf16_t *qd,
+                             const bf16_t *god, const uint64_t work[4], const float *hm,
                              const float *zv, const bf16_t *w_p, const float *s_gate,
                              const LinBwdScratch &w, float *dw_p, View outv, float *dsum, int Np,
                              hipStream_t st);
@@ -120,9 +131,12 @@ struct BwdOut {
   const double2 *rope_tab;        // NULL: no RoPE
   bf16_t *dq, *dk, *dv;           // boundary layout
 };
+// q, k, v, go: working copies of the heads in `work`; qd, kd, vd, god: the
+// boundary layout (Q, K rotated when RoPE is on) for the other heads.
 hipError_t launch_attn_bwd(const Geom &g, const bf16_t *q, const bf16_t *k, const bf16_t *v,
-                           const bf16_t *go, const float *lse2, const float *dsum, int Np,
-                           const int32_t *idx, const int32_t *inv_off, const int32_t *inv_list,
+                           const bf16_t *go, const bf16_t *qd, const bf16_t *kd, const bf16_t *vd,
+                           const bf16_t *god, const uint64_t work[4], const float *lse2, const float *dsum,
+                           int Np, const int32_t *idx, const int32_t *inv_off, const int32_t *inv_list,
                            const BwdOut &out, hipStream_t st);
 // Gate backward.  colsum: partial column sums of X [B][splits][C] fp32;
 // final: ds_b = sum of the heads' partials, dt_b = ds_b s_b (1 - s_b) (0 for

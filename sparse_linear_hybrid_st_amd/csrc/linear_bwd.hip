@@ -101,8 +101,10 @@ __global__ void __launch_bounds__(256) lin_bwd_prep_kernel(Geom g, const float *
 // registers during the step before, so the global loads overlap the MFMA
 // work (one wave per SIMD here: nothing else hides them).  Fixed order
 // throughout.
-__global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16_t *__restrict__ q,
-                                                              const bf16_t *__restrict__ go,
+__global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16_t *__restrict__ qw,
+                                                              const bf16_t *__restrict__ gw,
+                                                              const bf16_t *__restrict__ qd,
+                                                              const bf16_t *__restrict__ god, HeadSet work,
                                                               const bf16_t *__restrict__ mb,
                                                               const float *__restrict__ zv,
                                                               const float *__restrict__ s_gate,
@@ -120,10 +122,16 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
   const int n0 = s * chunk, n1 = min(g.N, n0 + chunk);
   const int h = bh % g.H;
   const bf16_t *outb = (const bf16_t *)outv.base;
+  // this head's Q and dO rows: working copies (rows D apart) or, for heads
+  // outside `work`, the boundary layout in place (rows H*D apart)
+  const bool fw = bit(work.w, h);
+  const long long hoff = fw ? (long long)bh * g.N * D : ((long long)b * g.N * g.H + h) * D;
+  const bf16_t *q = (fw ? qw : qd) + hoff, *go = (fw ? gw : god) + hoff;
+  const int rs = fw ? D : g.H * D;
   // dO . out over this lane's features f = 32db + 8r4 + 4hl + e of row n,
   // completed across the two half-waves (same row); dropped samples only
   auto go_out = [&](int n) __attribute__((always_inline)) {
-    const bf16_t *gr = go + ((long long)bh * g.N + n) * D;
+    const bf16_t *gr = go + (long long)n * rs;
     const bf16_t *orow = outb + row_offset(g, outv, b, h, n);
     float acc = 0.f;
 #pragma unroll
@@ -148,7 +156,6 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
     return;
   }
   const float sb = s_gate[b];
-  const long long hrow = (long long)bh * g.N;
   stage_swizzled(Ms, mb + (long long)bh * D * D, t);
   if (t < D) Zs[t] = zv[(long long)bh * D + t];
   RowOp ro;
@@ -184,13 +191,13 @@ __global__ void __launch_bounds__(256, 1) lin_bwd_rows_kernel(Geom g, const bf16
   };
   auto load_rows = [&](int base, Rows &R) __attribute__((always_inline)) {
     const int n = base + 32 * w + l32;
-    const long long nc = hrow + (n < n1 ? n : n0);
+    const long long nc = (long long)(n < n1 ? n : n0) * rs;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) R.gf[ks] = *(const bf16x8 *)(go + nc * D + (2 * ks + hl) * 8);
+    for (int ks = 0; ks < 8; ++ks) R.gf[ks] = *(const bf16x8 *)(go + nc + (2 * ks + hl) * 8);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) R.qv[db][r4] = *(const bf16x4 *)(q + nc * D + 32 * db + 8 * r4 + 4 * hl);
+      for (int r4 = 0; r4 < 4; ++r4) R.qv[db][r4] = *(const bf16x4 *)(q + nc + 32 * db + 8 * r4 + 4 * hl);
   };
   auto step = [&](int base, Rows &R) __attribute__((always_inline)) {
     const int rl = 32 * w + l32, n = base + rl;
@@ -413,7 +420,8 @@ __global__ void __launch_bounds__(256) lin_bwd_wp_kernel(int BH, const float *__
   dw_p[e] = acc;
 }
 
-hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *go, const float *hm,
+hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *go, const bf16_t *qd,
+                             const bf16_t *god, const uint64_t work[4], const float *hm,
                              const float *zv, const bf16_t *w_p, const float *s_gate,
                              const LinBwdScratch &w, float *dw_p, View outv, float *dsum, int Np,
                              hipStream_t st) {
@@ -430,8 +438,10 @@ hipError_t launch_linear_bwd(const Geom &g, const bf16_t *q, const bf16_t *go, c
   chunk = (chunk + 127) / 128 * 128;
   S = (g.N + chunk - 1) / chunk;
   lin_bwd_prep_kernel<<<dim3(16, BH), 256, 0, st>>>(g, hm, w_p, s_gate, w.mf, w.mb);
-  lin_bwd_rows_kernel<<<dim3(S, BH), 256, 0, st>>>(g, q, go, w.mb, zv, s_gate, w.partial, S, chunk, outv,
-                                                    dsum, Np);
+  HeadSet hs;
+  for (int i = 0; i < 4; ++i) hs.w[i] = work[i];
+  lin_bwd_rows_kernel<<<dim3(S, BH), 256, 0, st>>>(g, q, go, qd, god, hs, w.mb, zv, s_gate, w.partial, S, chunk,
+                                                    outv, dsum, Np);
   hipError_t e = launch_linear_reduce(g, S, w.partial, w.a_red, w.bz, st);
   if (e != hipSuccess) return e;
   lin_bwd_head_kernel<<<dim3(16, BH), 256, 0, st>>>(g, w.a_red, hm, w.mf, w_p, s_gate, w.dhb, w.dhtb,

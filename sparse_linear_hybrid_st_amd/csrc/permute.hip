@@ -44,12 +44,12 @@ __global__ void __launch_bounds__(256) rope_table_kernel(Geom g, double2 *__rest
 // copies (forward or inverse), MODE 1 rotates with the (cos, sin) table,
 // MODE 2 rotates computing (cos, sin) in place (no table).  keep_layout = 1
 // (rotation only) writes each row back to its own place in a [B,N,H,d]
-// destination.
+// destination.  Heads outside `heads` are skipped.
 template <typename T, int MODE, int D>
 __global__ void __launch_bounds__(256) permute_kernel(Geom g, const T *__restrict__ src,
                                                       T *__restrict__ dst, int inverse,
                                                       const double2 *__restrict__ table,
-                                                      int keep_layout) {
+                                                      int keep_layout, HeadSet heads) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int PER_ROW = D / VEC;
   constexpr int TOK = 256 / PER_ROW;
@@ -96,6 +96,7 @@ __global__ void __launch_bounds__(256) permute_kernel(Geom g, const T *__restric
 
 #pragma unroll 4
   for (int h = 0; h < g.H; ++h) {
+    if (!bit(heads.w, h)) continue;
     const int p = bit(g.temporal, h) ? p_temporal : tok;
     const uint64_t boff = brow + uint32_t(h * D);
     const uint64_t woff =
@@ -121,14 +122,17 @@ __global__ void __launch_bounds__(256) permute_kernel(Geom g, const T *__restric
 
 template <typename T, int D>
 static void permute_launch(const Geom &g, int mode, int inverse, const void *src, void *dst,
-                           hipStream_t st, const double2 *table, int keep_layout = 0) {
+                           hipStream_t st, const double2 *table, int keep_layout = 0,
+                           const uint64_t *heads = nullptr) {
   constexpr int TOK = 256 / (D / (16 / sizeof(T)));
   const dim3 grid(((g.N + TOK - 1) / TOK) * g.B);
   const T *s = (const T *)src;
   T *d = (T *)dst;
-  if (mode == 1) permute_kernel<T, 1, D><<<grid, 256, 0, st>>>(g, s, d, 0, table, keep_layout);
-  else if (mode == 2) permute_kernel<T, 2, D><<<grid, 256, 0, st>>>(g, s, d, 0, nullptr, keep_layout);
-  else permute_kernel<T, 0, D><<<grid, 256, 0, st>>>(g, s, d, inverse, nullptr, 0);
+  HeadSet hs;
+  for (int i = 0; i < 4; ++i) hs.w[i] = heads ? heads[i] : ~0ull;
+  if (mode == 1) permute_kernel<T, 1, D><<<grid, 256, 0, st>>>(g, s, d, 0, table, keep_layout, hs);
+  else if (mode == 2) permute_kernel<T, 2, D><<<grid, 256, 0, st>>>(g, s, d, 0, nullptr, keep_layout, hs);
+  else permute_kernel<T, 0, D><<<grid, 256, 0, st>>>(g, s, d, inverse, nullptr, 0, hs);
 }
 
 int rope_table_entries(const Geom &g) {
@@ -142,15 +146,15 @@ hipError_t launch_rope_table(const Geom &g, double2 *table, hipStream_t st) {
 }
 
 hipError_t launch_permute(const Geom &g, int dtype_bf16, int rope, int inverse, const void *src,
-                          void *dst, hipStream_t st, const double2 *table) {
+                          void *dst, hipStream_t st, const double2 *table, const uint64_t *heads) {
   const int mode = rope ? (table ? 1 : 2) : 0;
   if (dtype_bf16) {
     if (g.D != 128) return hipErrorInvalidValue;
-    permute_launch<bf16_t, 128>(g, mode, inverse, src, dst, st, table);
+    permute_launch<bf16_t, 128>(g, mode, inverse, src, dst, st, table, 0, heads);
   } else if (g.D == 128) {
-    permute_launch<float, 128>(g, mode, inverse, src, dst, st, table);
+    permute_launch<float, 128>(g, mode, inverse, src, dst, st, table, 0, heads);
   } else if (g.D == 64) {
-    permute_launch<float, 64>(g, mode, inverse, src, dst, st, table);
+    permute_launch<float, 64>(g, mode, inverse, src, dst, st, table, 0, heads);
   } else {
     return hipErrorInvalidValue;
   }
