@@ -19,8 +19,10 @@ inline size_t select_ws_bytes(const Geom &g) {
 
 // Token chunks per (b, h) used by the split-N linear-state reduction.
 inline int linear_splits(const Geom &g) {
+  // at most 512 workgroups (two per CU at the state kernel's register use),
+  // so they all run in one round
   int chunks = (g.N + 127) / 128;
-  int want = (512 + g.B * g.H - 1) / (g.B * g.H);
+  int want = 512 / (g.B * g.H);
   return want < 1 ? 1 : (want > chunks ? chunks : want);
 }
 
