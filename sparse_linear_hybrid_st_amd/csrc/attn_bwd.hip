@@ -55,69 +55,78 @@ struct BwdArgs {
 
 // ---------------------------------------------------------------------------
 // Top-K inverse lists.  For key block kb of head (b, h): the query blocks
-// whose selection contains kb, in ascending order.  One wave per (bh, kb)
-// scans every query block's (ascending) selection with a binary search;
-// ballots compact the hits in order.  Pass 0 counts, pass 1 writes at the
-// offsets of a per-head exclusive scan of the counts.
+// whose selection contains kb, in ascending order.  One workgroup per head
+// transposes the head's selection through a bitmap in LDS (row kb, bit qb),
+// a chunk of key-block rows at a time: every selection entry sets its bit
+// (LDS atomic OR, so the result does not depend on the order), each row's
+// population count gives the counts, a workgroup scan the offsets (carried
+// across chunks), and the set bits read in ascending order give the list.
 // ---------------------------------------------------------------------------
-template <bool FILL>
-__global__ void __launch_bounds__(64) topk_inverse_kernel(Geom g, const int32_t *__restrict__ idx,
-                                                          int32_t *__restrict__ off,
-                                                          int32_t *__restrict__ list) {
-  const int kb = blockIdx.x, bh = blockIdx.y, h = bh % g.H, lane = threadIdx.x;
-  if (!bit(g.topk, h)) return;
-  const long long hb = (long long)bh * g.nb;
-  int n = FILL ? off[bh * (g.nb + 1) + kb] : 0;
-  for (int base = 0; base < g.nb; base += 64) {
-    const int qb = base + lane;
-    bool hit = false;
-    if (qb < g.nb) {
-      const int32_t *sel = idx + (hb + qb) * g.k;
-      int lo = 0, hi = g.k;  // first position with sel[pos] >= kb
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sel[mid] < kb) lo = mid + 1;
-        else hi = mid;
-      }
-      hit = lo < g.k && sel[lo] == kb;
-    }
-    const unsigned long long m = __ballot(hit);
-    if (FILL && hit) {
-      const int before = __popcll(m & ((1ull << lane) - 1ull));
-      list[hb * g.k + n + before] = qb;
-    }
-    n += __popcll(m);
-  }
-  if (!FILL && lane == 0) off[bh * (g.nb + 1) + kb] = n;
+constexpr int kInvThreads = 256;
+constexpr int kInvLdsWords = 16384;  // 64 KB of bitmap per chunk
+
+__host__ __device__ inline int inv_words(const Geom &g) { return (g.nb + 31) / 32; }
+__host__ __device__ inline int inv_chunk_rows(const Geom &g) {
+  const int r = kInvLdsWords / inv_words(g);
+  return r < g.nb ? r : g.nb;
 }
 
-// Exclusive scan of the nb counts of one head (in place), total at [nb].
-__global__ void __launch_bounds__(256) topk_inverse_scan_kernel(Geom g, int32_t *__restrict__ off) {
+__global__ void __launch_bounds__(kInvThreads) topk_inverse_kernel(Geom g, const int32_t *__restrict__ idx,
+                                                                   int32_t *__restrict__ off,
+                                                                   int32_t *__restrict__ list) {
+  extern __shared__ uint32_t bm[];  // [rows of the chunk][W]
+  __shared__ int part[kInvThreads];
   const int bh = blockIdx.x, h = bh % g.H, t = threadIdx.x;
   if (!bit(g.topk, h)) return;
+  const int W = inv_words(g), KC = inv_chunk_rows(g), nk = g.nb * g.k;
+  const int32_t *sel = idx + (long long)bh * nk;
   int32_t *o = off + (long long)bh * (g.nb + 1);
-  __shared__ int part[256];
-  const int per = (g.nb + 255) / 256, s0 = t * per, s1 = min(g.nb, s0 + per);
-  int sum = 0;
-  for (int i = s0; i < s1; ++i) sum += o[i];
-  part[t] = sum;
-  __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int c = part[i];
-      part[i] = run;
-      run += c;
+  int32_t *lst = list + (long long)bh * nk;
+  int carry = 0;  // entries in the chunks before this one
+  for (int kc0 = 0; kc0 < g.nb; kc0 += KC) {
+    const int rows = min(KC, g.nb - kc0);
+    for (int i = t; i < rows * W; i += kInvThreads) bm[i] = 0u;
+    __syncthreads();
+    for (int e = t; e < nk; e += kInvThreads) {
+      const int kb = sel[e] - kc0, qb = e / g.k;
+      if (kb >= 0 && kb < rows) atomicOr(&bm[kb * W + (qb >> 5)], 1u << (qb & 31));
     }
-    o[g.nb] = run;
+    __syncthreads();
+    // thread t owns rows [r0, r1) of the chunk, in order
+    const int per = (rows + kInvThreads - 1) / kInvThreads;
+    const int r0 = min(rows, t * per), r1 = min(rows, r0 + per);
+    int mine = 0;
+    for (int r = r0; r < r1; ++r)
+      for (int i = 0; i < W; ++i) mine += __popc(bm[r * W + i]);
+    part[t] = mine;
+    __syncthreads();
+    if (t == 0) {
+      int run = carry;
+      for (int i = 0; i < kInvThreads; ++i) {
+        const int c = part[i];
+        part[i] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+    int n = part[t];
+    for (int r = r0; r < r1; ++r) {
+      o[kc0 + r] = n;
+      for (int i = 0; i < W; ++i) {
+        uint32_t word = bm[r * W + i];
+        while (word) {
+          lst[n++] = i * 32 + (__ffs(word) - 1);
+          word &= word - 1u;
+        }
+      }
+    }
+    __syncthreads();  // every thread has read `part` and the bitmap
+    if (t == kInvThreads - 1) part[0] = n;
+    __syncthreads();
+    carry = part[0];
+    __syncthreads();
   }
-  __syncthreads();
-  int run = part[t];
-  for (int i = s0; i < s1; ++i) {
-    const int c = o[i];
-    o[i] = run;
-    run += c;
-  }
+  if (t == 0) o[g.nb] = carry;
 }
 
 // Rows of one (b, h): the working copy (rows 128 apart) for heads in
@@ -757,10 +766,10 @@ attn_bwd_dkv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 hipError_t launch_topk_inverse(const Geom &g, const int32_t *idx, int32_t *off, int32_t *list,
                                hipStream_t st) {
-  const dim3 grid(g.nb, g.B * g.H);
-  topk_inverse_kernel<false><<<grid, 64, 0, st>>>(g, idx, off, list);
-  topk_inverse_scan_kernel<<<g.B * g.H, 256, 0, st>>>(g, off);
-  topk_inverse_kernel<true><<<grid, 64, 0, st>>>(g, idx, off, list);
+  const size_t lds = size_t(inv_chunk_rows(g)) * inv_words(g) * sizeof(uint32_t);
+  if (lds > 48 * 1024)
+    hipFuncSetAttribute((const void *)topk_inverse_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  topk_inverse_kernel<<<g.B * g.H, kInvThreads, lds, st>>>(g, idx, off, list);
   return hipGetLastError();
 }
 
