@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(256) block_score_kernel(Geom g, const double *
     }
 }
 
-// Selection, one wave per query block (4 per workgroup): the k best key
+// Selection, one single-wave workgroup per query block: the k best key
 // blocks under the order "higher score first, equal scores lower block
 // first", written ascending.
 //
@@ -161,28 +161,26 @@ __global__ void __launch_bounds__(256) block_score_kernel(Geom g, const double *
 // digits from the top, each counting in an LDS histogram the digits of the
 // keys that still match the prefix found so far and picking the digit where
 // the running count from the top reaches the number still to be chosen.
-// After the last pass the prefix is T, the k-th largest key, and `rem` of
-// the keys equal to T are to be kept; a last sweep in index order keeps the
-// keys above T and the first `rem` keys equal to T, and compacts them with
-// ballot prefix counts.  Exact, and independent of the schedule.
+// The passes stop as soon as every key matching the prefix is to be kept
+// (usually after two or three digits); otherwise after the last pass the
+// prefix is T, the k-th largest key.  Then `rem` of the keys whose top bits
+// equal the prefix are to be kept: a last sweep in index order keeps the
+// keys above the prefix and the first `rem` keys equal to it, and compacts
+// them with ballot prefix counts.  Exact, and independent of the schedule.
 __device__ __forceinline__ unsigned long long score_key(double s) {
   const unsigned long long u = (unsigned long long)__double_as_longlong(s + 0.0);
   return (u >> 63) ? ~u : (u | (1ull << 63));
 }
 
-__global__ void __launch_bounds__(256) topk_select_kernel(Geom g, const double *__restrict__ scores,
-                                                          int32_t *__restrict__ idx) {
-  extern __shared__ unsigned long long sel_keys[];  // [4][nb]
-  __shared__ unsigned hist_all[4][256];
+__global__ void __launch_bounds__(64) topk_select_kernel(Geom g, const double *__restrict__ scores,
+                                                         int32_t *__restrict__ idx) {
+  extern __shared__ unsigned long long key[];  // [nb]
+  __shared__ unsigned hist[256];
   const int bh = blockIdx.y, h = bh % g.H;
   if (!bit(g.topk, h)) return;
-  const int nb = g.nb, k = g.k, lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-  const int qb = blockIdx.x * 4 + wv;
-  const bool live = qb < nb;  // dead waves still take part in the barriers
-  unsigned long long *key = sel_keys + (long long)wv * nb;
-  unsigned *hist = hist_all[wv];
-  const double *row = scores + ((long long)bh * nb + (live ? qb : 0)) * nb;
+  const int nb = g.nb, k = g.k, lane = threadIdx.x;
+  const int qb = blockIdx.x;
+  const double *row = scores + ((long long)bh * nb + qb) * nb;
   for (int j = lane; j < nb; j += 64) key[j] = score_key(row[j]);
 
   unsigned long long prefix = 0, mask = 0;
@@ -209,18 +207,20 @@ __global__ void __launch_bounds__(256) topk_select_kernel(Geom g, const double *
     const unsigned need = unsigned(rem);
     const bool mine = suf >= need && suf - c < need;  // exactly one lane
     int d;
-    unsigned greater;
-    if (suf - c0 - c1 - c2 >= need) { d = 4 * lane + 3; greater = suf - c; }
-    else if (suf - c0 - c1 >= need) { d = 4 * lane + 2; greater = suf - c0 - c1 - c2; }
-    else if (suf - c0 >= need) { d = 4 * lane + 1; greater = suf - c0 - c1; }
-    else { d = 4 * lane; greater = suf - c0; }
+    unsigned greater, in_bin;
+    if (suf - c0 - c1 - c2 >= need) { d = 4 * lane + 3; greater = suf - c; in_bin = c3; }
+    else if (suf - c0 - c1 >= need) { d = 4 * lane + 2; greater = suf - c0 - c1 - c2; in_bin = c2; }
+    else if (suf - c0 >= need) { d = 4 * lane + 1; greater = suf - c0 - c1; in_bin = c1; }
+    else { d = 4 * lane; greater = suf - c0; in_bin = c0; }
     const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
     d = __shfl(d, src);
     greater = __shfl(greater, src);
+    in_bin = __shfl(in_bin, src);
     prefix |= (unsigned long long)d << shift;
     mask |= 255ull << shift;
     rem -= int(greater);
     __syncthreads();  // histogram reads done before the next clear
+    if (in_bin == unsigned(rem)) break;  // every key with this prefix is kept
   }
 
   int32_t *dst = idx + ((long long)bh * nb + qb) * k;
@@ -228,13 +228,13 @@ __global__ void __launch_bounds__(256) topk_select_kernel(Geom g, const double *
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int j0 = 0; j0 < nb; j0 += 64) {
     const int j = j0 + lane;
-    const unsigned long long kk = j < nb ? key[j] : 0ull;
+    const unsigned long long kk = j < nb ? key[j] & mask : 0ull;
     const bool gt = j < nb && kk > prefix;
     const bool eq = j < nb && kk == prefix;
     const unsigned long long beq = __ballot(eq);
     const bool keep = gt || (eq && eq_seen + __popcll(beq & below) < rem);
     const unsigned long long bk = __ballot(keep);
-    if (live && keep) dst[taken + __popcll(bk & below)] = j;
+    if (keep) dst[taken + __popcll(bk & below)] = j;
     taken += __popcll(bk);
     eq_seen += __popcll(beq);
   }
@@ -253,12 +253,12 @@ hipError_t launch_block_select(const Geom &g, int dtype_bf16, View qv, View kv, 
   block_score_kernel<<<grid2, 256, 0, st>>>(g, qbar, kbar, scores);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = size_t(4) * g.nb * sizeof(unsigned long long);
+  const size_t lds = size_t(g.nb) * sizeof(unsigned long long);
   if (lds > 48 * 1024)
     hipFuncSetAttribute((const void *)topk_select_kernel,
                         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  dim3 grid3((g.nb + 3) / 4, g.B * g.H);
-  topk_select_kernel<<<grid3, 256, lds, st>>>(g, scores, idx);
+  dim3 grid3(g.nb, g.B * g.H);
+  topk_select_kernel<<<grid3, 64, lds, st>>>(g, scores, idx);
   return hipGetLastError();
 }
 
