@@ -272,17 +272,20 @@ __global__ void linear_reduce_kernel(int D, int S, const float *__restrict__ par
 
 // ---------------------------------------------------------------------------
 // Finalize, d = 128 (fused layer): sum the split-N partial states of 8 rows
-// of H (and, in block 0, of Z) in a fixed order, keep them in LDS and fold
-// the projection and the gate in: Hp[j][i] = bf16(s_b * (H W_p)[i][j]).
+// of H (and 8 of Z) in a fixed order, keep them in LDS and fold the
+// projection and the gate in: Hp[j][i] = bf16(s_b * (H W_p)[i][j]).
 // Samples dropped by the branch threshold (s_b < drop_tau) are skipped.
-// Grid (16, B*H); block blk owns rows 8*blk..+7.  W_p is staged once per
-// block as bf16 (16-byte loads); thread t computes row t/32 at columns
-// (t%32) + 32m, m < 4.  H and Z are also written out in fp32.
+// Grid (16, B*H), 1024 threads: thread t sums element t of the block's 8
+// rows over the splits (one element per thread keeps many loads in flight:
+// the kernel is bound by their latency); block blk owns rows 8*blk..+7.
+// W_p is staged once per block as bf16 (16-byte loads); thread t < 256 then
+// computes row t/32 at columns (t%32) + 32m, m < 4.  H and Z are also
+// written out in fp32.
 // FULL (full-width [C, C] projection, applied after the attention kernel
 // by a GEMM over whole token rows): Hp = bf16(H^T), no W_p and no gate.
 // ---------------------------------------------------------------------------
 template <typename T, bool FULL>
-__global__ void __launch_bounds__(256) linear_finalize_kernel(Geom g, int S,
+__global__ void __launch_bounds__(1024) linear_finalize_kernel(Geom g, int S,
                                                               const float *__restrict__ partial,
                                                               const T *__restrict__ w_p,
                                                               const float *__restrict__ s_gate,
@@ -298,31 +301,24 @@ __global__ void __launch_bounds__(256) linear_finalize_kernel(Geom g, int S,
   constexpr int VEC = 16 / sizeof(T);
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   if constexpr (!FULL)
-    for (int e = t * VEC; e < D * D; e += 256 * VEC)
+    for (int e = t * VEC; e < D * D; e += 1024 * VEC)
       *(u32x4 *)(Ws + e) = *(const u32x4 *)(w_p + e);
-  // reduce this block's 8 rows (elements t, t + 256, .. of the 1024), fixed order
-  const float *p = partial + (long long)bh * S * per + 8 * blk * D;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  // unrolled so that several splits' loads are in flight; the adds keep
-  // their order
+  // reduce element t of this block's 8 rows over the splits, fixed order
+  const float *p = partial + (long long)bh * S * per + 8 * blk * D + t;
+  float acc = 0.f;
 #pragma unroll 8
-  for (int s = 0; s < S; ++s) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += p[(long long)s * per + t + 256 * i];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    Hs[t + 256 * i] = acc[i];
-    hm[((long long)bh * D + 8 * blk) * D + t + 256 * i] = acc[i];
-  }
-  if (blk == 0 && t < D) {
-    const float *pz = partial + (long long)bh * S * per + D * D + t;
+  for (int s = 0; s < S; ++s) acc += p[(long long)s * per];
+  Hs[t] = acc;
+  hm[((long long)bh * D + 8 * blk) * D + t] = acc;
+  if (t < 8) {  // Z[8 blk + t]
+    const float *pz = partial + (long long)bh * S * per + D * D + 8 * blk + t;
     float az = 0.f;
 #pragma unroll 8
     for (int s = 0; s < S; ++s) az += pz[(long long)s * per];
-    zv[(long long)bh * D + t] = az;
+    zv[(long long)bh * D + 8 * blk + t] = az;
   }
   __syncthreads();
+  if (t >= 256) return;
   const int ii = t >> 5, jg = t & 31;
   float o[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (FULL) {
@@ -351,11 +347,11 @@ hipError_t launch_linear_finalize(const Geom &g, int bf16, const float *partial,
   const int S = linear_splits(g);
   dim3 grid(16, g.B * g.H);
   if (!w_p)  // full-width projection: the GEMM after the attention kernel applies W_p and s
-    linear_finalize_kernel<bf16_t, true><<<grid, 256, 0, st>>>(g, S, partial, nullptr, s, h, z, hp);
+    linear_finalize_kernel<bf16_t, true><<<grid, 1024, 0, st>>>(g, S, partial, nullptr, s, h, z, hp);
   else if (bf16)
-    linear_finalize_kernel<bf16_t, false><<<grid, 256, 0, st>>>(g, S, partial, (const bf16_t *)w_p, s, h, z, hp);
+    linear_finalize_kernel<bf16_t, false><<<grid, 1024, 0, st>>>(g, S, partial, (const bf16_t *)w_p, s, h, z, hp);
   else
-    linear_finalize_kernel<float, false><<<grid, 256, 0, st>>>(g, S, partial, (const float *)w_p, s, h, z, hp);
+    linear_finalize_kernel<float, false><<<grid, 1024, 0, st>>>(g, S, partial, (const float *)w_p, s, h, z, hp);
   return hipGetLastError();
 }
 
