@@ -158,6 +158,92 @@ def calibrate_bench(args, w, inp, p):
     return 0
 
 
+def stages_bench(args, w, inp, p):
+    """--stages: each C-ABI stage entry point alone on the workload (inputs
+    resident, warm), its average time over the timed calls from HIP events,
+    and its algorithmic bytes (or flops) per call: the staged layer, stage by
+    stage.  Prints one JSON line."""
+    import torch
+
+    import sparse_linear_hybrid_st_amd as S
+
+    B, N, H, d = w.batch, w.N, w.n_heads, w.head_dim
+    esz = 2 if w.io_dtype == "bf16" else 4
+    dev = {n: inp[n].cuda() for n in ("q", "k", "v", "x", "w_p", "gate_w")}
+    tensor = B * N * H * d                              # elements of Q, K, V or out
+    qw, kw, vw = (torch.empty_like(dev["q"]) for _ in range(3))
+    o_s = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    o_l = torch.empty_like(o_s)
+    hs = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+    zs = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+    s = torch.empty(B, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(dev["q"])
+    ws = S.workspace(p)
+    topk = 2 in w.head_kinds
+    idx = torch.zeros((B, H, p.n_blocks, w.topk), dtype=torch.int32, device="cuda") if topk else None
+    n_topk = sum(1 for k in w.head_kinds if k == 2)
+    rope = int(w.rope)
+    stages = [
+        ("a2 permute Q into working order" + (" with RoPE" if rope else ""),
+         lambda: S.salad_permute(p, rope, 0, dev["q"], qw), "GB/s", 2.0 * tensor * esz),
+        ("a2 permute K", lambda: S.salad_permute(p, rope, 0, dev["k"], kw), "GB/s", 2.0 * tensor * esz),
+        ("a2 permute V", lambda: S.salad_permute(p, 0, 0, dev["v"], vw), "GB/s", 2.0 * tensor * esz),
+    ]
+    if topk:
+        stages.append(("a3-a4 block means, scores, Top-K selection",
+                       lambda: S.salad_block_select(p, qw, kw, idx, ws), "GB/s",
+                       2.0 * B * n_topk * N * d * esz))
+    pairs = pair_count(w)
+    stages += [
+        ("a6 linear state", lambda: S.salad_linear_state(p, kw, vw, hs, zs, ws), "GB/s", 2.0 * tensor * esz),
+        ("a8 gate", lambda: S.salad_gate(p, dev["x"], dev["gate_w"], inp["gate_b"], s, ws), "GB/s",
+         1.0 * tensor * esz),
+    ]
+    results = []
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for name, fn, unit, amount in stages:
+        ms = timed(fn, args.steps)
+        results.append({"stage": name, "ms": ms, "unit": unit, "achieved": amount / (ms * 1e-3) / 1e9,
+                        "frac_of_peak": amount / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    # a5 needs the selection (made above) for Top-K heads; the window pairs
+    # are counted in closed form, the Top-K pairs from the selection
+    if topk:
+        pairs += topk_pairs_from_idx(w, idx.cpu().numpy())
+    ms = timed(lambda: S.salad_sparse_attn(p, qw, kw, vw, idx, o_s), args.steps)
+    results.append({"stage": "a5 sparse attention (staged: fp32 O_s in working order)", "ms": ms,
+                    "unit": "TFLOP/s", "achieved": 4.0 * d * pairs / (ms * 1e-3) / 1e12,
+                    "frac_of_peak": 4.0 * d * pairs / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS})
+    for name, fn, amount in (
+            ("a7 linear apply (fp32 O_l)", lambda: S.salad_linear_apply(p, qw, hs, zs, o_l),
+             1.0 * tensor * esz + 4.0 * tensor),
+            ("a9 combine + inverse permutation", lambda: S.salad_combine(p, o_s, o_l, dev["w_p"], s, out),
+             8.0 * tensor + 1.0 * tensor * esz)):
+        ms = timed(fn, args.steps)
+        results.append({"stage": name, "ms": ms, "unit": "GB/s", "achieved": amount / (ms * 1e-3) / 1e9,
+                        "frac_of_peak": amount / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    total = sum(r["ms"] for r in results)
+    print(json.dumps({
+        "metric": "per-stage ms of the staged layer (each C-ABI stage entry point alone)",
+        "value": total, "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": 2,
+        "ms_per_step": total, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.io_dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "bytes": "algorithmic: each stage's compulsory reads and writes"},
+        "stages": results}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +268,13 @@ def main():
     ap.add_argument("--calibrate", default=None, metavar="R1,R2,...",
                     help="time salad_window_calibrate (dense attention plus one window pass per "
                          "radius in this comma-separated list) instead of the forward")
+    ap.add_argument("--stages", action="store_true",
+                    help="time each C-ABI stage entry point alone (the staged layer) instead of the "
+                         "fused forward")
+    ap.add_argument("--cold-runs", type=int, default=20,
+                    help="forward only: after the timed steps, this many more layer calls, each after "
+                         "writing a 512 MiB buffer (L2 and MALL flushed), timed one by one; median and "
+                         "min reported as cold_cache (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size reference for the HBM byte counters)")
@@ -212,6 +305,8 @@ def main():
 
     if args.calibrate:
         sys.exit(calibrate_bench(args, w, inp, p))
+    if args.stages:
+        sys.exit(stages_bench(args, w, inp, p))
 
     def fwd():
         S.salad_attn_forward(p, dev["q"], dev["k"], dev["v"], dev["x"], dev["w_p"], dev["gate_w"],
@@ -265,6 +360,24 @@ def main():
     attn_avg = attn_ms / max(calls, 1)
     achieved = flops / (attn_avg * 1e-3) / 1e12
 
+    cold = None
+    if not args.backward and args.cold_runs > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        times = []
+        for _ in range(args.cold_runs):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del flush
+        times.sort()
+        cold = {"median_ms": times[len(times) // 2], "min_ms": times[0], "runs": len(times),
+                "flush_mib": 512,
+                "median_effective_tflops": flops / (times[len(times) // 2] * 1e-3) / 1e12}
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -307,6 +420,8 @@ def main():
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
                      "avg_launch_ms": attn_avg, "launches": calls},
     }
+    if cold is not None:
+        rec["cold_cache"] = cold
     if w.io_dtype != "bf16":
         rec["dtype"] = "f32"
     if traffic is not None and args.backward:

@@ -13,6 +13,7 @@
 // sigmoid -- a fixed summation order throughout.
 #include "common.h"
 #include "kernels.h"
+#include "mfma_util.h"
 
 namespace salad {
 
@@ -148,8 +149,88 @@ __global__ void __launch_bounds__(256) combine_kernel(Geom g, const float *__res
   }
 }
 
+// Combine, bf16, d = 128, on MFMA.  Grid (ceil(N/128), B*H), 4 waves of 32
+// working rows.  (O_l W_p)^T = W_p^T O_l^T with W_p^T staged in LDS (bf16,
+// the K-tile swizzle) as A operands and each row's O_l as B operands, split
+// into bf16 hi + lo parts (O_l = hi + lo to about 2^-17 relative; the
+// products are exact and accumulate in fp32), so 2 MFMAs per step.  A lane
+// then holds its row's features 32db + 8r4 + 4hl + e and writes them as
+// bf16x4 next to the matching O_s.
+__global__ void __launch_bounds__(256) combine_bf16_kernel(Geom g, const float *__restrict__ o_s,
+                                                           const float *__restrict__ o_l,
+                                                           const bf16_t *__restrict__ w_p,
+                                                           const float *__restrict__ s,
+                                                           bf16_t *__restrict__ out) {
+  __shared__ __attribute__((aligned(16))) bf16_t Wt[kD * kD];  // Wt[j][k] = W_p[k][j]
+  const int bh = blockIdx.y, h = bh % g.H, b = bh / g.H;
+  const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  // W_p^T into LDS: thread t reads 8 consecutive columns j of row k
+  for (int u = t; u < kD * kD / 8; u += 256) {
+    const int k = u >> 4, j0 = (u & 15) * 8;
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_l;
+    const u32x4_l v = *(const u32x4_l *)(w_p + k * kD + j0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + e;
+      Wt[j * kD + (((k >> 3) ^ kv_swz(j)) << 3) + (k & 7)] = bf16_t((v[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+    }
+  }
+  const int p = blockIdx.x * 128 + 32 * w + l32, pc = min(p, g.N - 1);
+  const float *orow = o_l + ((long long)bh * g.N + pc) * kD;
+  bf16x8 hi[8], lo[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const f32x4 a = *(const f32x4 *)(orow + 16 * ks + 8 * hl);
+    const f32x4 c = *(const f32x4 *)(orow + 16 * ks + 8 * hl + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = e < 4 ? a[e] : c[e - 4];
+      const __bf16 xh = (__bf16)x;
+      hi[ks][e] = xh;
+      lo[ks][e] = (__bf16)(x - float(xh));
+    }
+  }
+  __syncthreads();
+  const int kswz = kv_swz(l32);
+  const int k_lane = l32 * kD + 8 * (hl ^ (kswz & 1)), k_x = kswz >> 1;
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const bf16x8 a = *(const bf16x8 *)(Wt + db * 32 * kD + k_lane + 16 * (ks ^ k_x));
+      acc[db] = mfma_32x32x16(a, hi[ks], acc[db]);
+      acc[db] = mfma_32x32x16(a, lo[ks], acc[db]);
+    }
+  if (p >= g.N) return;
+  const float sb = s[b];
+  const float sl = sb < g.drop_tau ? 0.f : sb;  // branch dropping ([G] 2 C): out = O_s
+  const int tok = bit(g.temporal, h) ? st_token(g, p) : p;
+  const float *os = o_s + ((long long)bh * g.N + p) * kD;
+  bf16_t *dst = out + (((long long)b * g.N + tok) * g.H + h) * kD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int f = 32 * db + 8 * r4 + 4 * hl;
+      const f32x4 o = *(const f32x4 *)(os + f);
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[e] + sl * acc[db][4 * r4 + e]);
+      *(bf16x4 *)(dst + f) = v;
+    }
+}
+
 hipError_t launch_combine(const Geom &g, int bf16, const float *o_s, const float *o_l,
                           const void *w_p, const float *s, void *out, hipStream_t st) {
+  if (bf16 && g.D == 128) {
+    combine_bf16_kernel<<<dim3((g.N + 127) / 128, g.B * g.H), 256, 0, st>>>(
+        g, o_s, o_l, (const bf16_t *)w_p, s, (bf16_t *)out);
+    return hipGetLastError();
+  }
   dim3 grid((g.N + 63) / 64, g.B * g.H);
   const size_t lds = (size_t(g.D) * g.D + 64 * (g.D + 1)) * sizeof(float);
 #define SALAD_COMBINE(T, DD)                                                                 \

@@ -399,7 +399,9 @@ hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float 
 }
 
 // ---------------------------------------------------------------------------
-// Apply, bf16, d = 128.  Grid (ceil(N/128), B*H); 4 waves x 32 tokens.
+// Apply, bf16, d = 128.  Grid (up to 1024/(B*H) workgroups, B*H), each over
+// 128-token tiles tile, tile + gridDim.x, ... (the staged H is reused); 4
+// waves x 32 tokens per tile.
 // LDS holds H^T as bf16 hi and lo halves, [d_out][d_in], unit u of row j
 // at u ^ (j & 15).  Per wave: C[d_out][token] = sum_i H^T[d_out][i] relu(q)[i].
 // ---------------------------------------------------------------------------
@@ -435,50 +437,55 @@ __global__ void __launch_bounds__(256) linear_apply_bf16_kernel(Geom g, View qv,
     if (t < D) Zs[t] = zv[(long long)bh * D + t];
   }
   __syncthreads();
-  const int p = blockIdx.x * 128 + w * 32 + l32;
-  const bool valid = p < g.N;
-  const bf16_t *qb = (const bf16_t *)qv.base;
-  const long long qoff = row_offset(g, qv, b, h, valid ? p : g.N - 1);
-  bf16x8 q[8];
-  float den = 0.f;
+  // the staged H serves several 128-token tiles (tile, tile + gridDim.x, ...)
+  const int n_tiles = (g.N + 127) / 128;
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int p = tile * 128 + w * 32 + l32;
+    const bool valid = p < g.N;
+    const bf16_t *qb = (const bf16_t *)qv.base;
+    const long long qoff = row_offset(g, qv, b, h, valid ? p : g.N - 1);
+    bf16x8 q[8];
+    float den = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    u32x4 raw = relu_bf16x8(*(const u32x4 *)(qb + qoff + (2 * ks + hl) * 8));
-    q[ks] = *(bf16x8 *)&raw;
+    for (int ks = 0; ks < 8; ++ks) {
+      u32x4 raw = relu_bf16x8(*(const u32x4 *)(qb + qoff + (2 * ks + hl) * 8));
+      q[ks] = *(bf16x8 *)&raw;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t bits = (raw[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-      den = fmaf(bf16_to_f32(bf16_t(bits)), Zs[16 * ks + 8 * hl + e], den);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (raw[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        den = fmaf(bf16_to_f32(bf16_t(bits)), Zs[16 * ks + 8 * hl + e], den);
+      }
+    }
+    // add the other half-wave's partial denominator (lanes l and l^32)
+    den += __shfl_xor(den, 32);
+    den += g.eps;
+    f32x16 o[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int j = 32 * db + l32;
+        const int pu = (2 * ks + hl) ^ (j & 15);
+        const bf16x8 ahi = *(const bf16x8 *)(Hhi + j * D + pu * 8);
+        const bf16x8 alo = *(const bf16x8 *)(Hlo + j * D + pu * 8);
+        o[db] = mfma32(ahi, q[ks], o[db]);
+        o[db] = mfma32(alo, q[ks], o[db]);
+      }
+    if (valid) {
+      float *dst = o_l + (((long long)bh * g.N) + p) * D;
+      const float inv = 1.0f / den;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 v = {o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
+                     o[db][4 * r4 + 3] * inv};
+          *(f32x4 *)(dst + 32 * db + 8 * r4 + 4 * hl) = v;
+        }
     }
   }
-  // add the other half-wave's partial denominator (lanes l and l^32)
-  den += __shfl_xor(den, 32);
-  den += g.eps;
-  f32x16 o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int j = 32 * db + l32;
-      const int pu = (2 * ks + hl) ^ (j & 15);
-      const bf16x8 ahi = *(const bf16x8 *)(Hhi + j * D + pu * 8);
-      const bf16x8 alo = *(const bf16x8 *)(Hlo + j * D + pu * 8);
-      o[db] = mfma32(ahi, q[ks], o[db]);
-      o[db] = mfma32(alo, q[ks], o[db]);
-    }
-  if (!valid) return;
-  float *dst = o_l + (((long long)bh * g.N) + p) * D;
-  const float inv = 1.0f / den;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      f32x4 v = {o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
-                 o[db][4 * r4 + 3] * inv};
-      *(f32x4 *)(dst + 32 * db + 8 * r4 + 4 * hl) = v;
-    }
 }
 
 // Apply, f32.  Grid (ceil(N/64), B*H); thread t: token t/4, columns 32*(t%4)..+31
@@ -513,7 +520,9 @@ __global__ void __launch_bounds__(256) linear_apply_f32_kernel(Geom g, View qv, 
 hipError_t launch_linear_apply(const Geom &g, int bf16, View qv, const float *h, const float *z,
                                float *o_l, hipStream_t st) {
   if (bf16) {
-    dim3 grid((g.N + 127) / 128, g.B * g.H);
+    // about two rounds of workgroups (two per CU), each over several tiles
+    const int tiles = (g.N + 127) / 128, per_head = 1024 / (g.B * g.H);
+    dim3 grid(per_head < 1 ? 1 : (per_head < tiles ? per_head : tiles), g.B * g.H);
     linear_apply_bf16_kernel<<<grid, 256, 0, st>>>(g, qv, h, z, o_l);
   } else {
     dim3 grid((g.N + 63) / 64, g.B * g.H);
