@@ -1,6 +1,7 @@
 // Backward of the sparse branch: dQ, dK and dV of softmax attention
-// restricted to the kept query-key pairs, for the bf16 working layout
-// (d = 128).
+// restricted to the kept query-key pairs, bf16, d = 128.  Rows are read in
+// each head's working order: temporal heads from working copies, the other
+// heads in place from the boundary layout.
 //
 // The forward is the sparse branch of the SALAD structured summary
 // (paper.rainbus.top/paper/2601.16515), Prerequisites > Sparse Attention,

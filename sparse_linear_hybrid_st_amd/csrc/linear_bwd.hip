@@ -1,5 +1,5 @@
-// Backward of the linear branch and of the per-head projection, bf16
-// working layout, d = 128.
+// Backward of the linear branch and of the per-head projection, bf16,
+// d = 128 (rows in each head's working order, as in attn_bwd.hip).
 //
 // Forward (SALAD structured summary, paper.rainbus.top/paper/2601.16515,
 // Prerequisites > Linear Attention and method steps 4-6): per (b, h), with
