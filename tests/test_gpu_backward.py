@@ -31,6 +31,9 @@ CASES = [
     C.small("bwd-rope-cfg", (3, 4, 10), 4, 128, "bf16", [0, 1, 2, 2], 20, 64, 1, batch=2, rope=True,
             rope_dims=(44, 42, 42), x_sample_shift=True),
     C.small("bwd-short", (1, 1, 37), 1, 128, "bf16", [1], 5, 64, 1),
+    # more than 64 heads (the head masks' later words), RoPE and two samples
+    C.small("bwd-70-heads", (2, 4, 10), 70, 128, "bf16", [h % 3 for h in range(70)], 9, 64, 1, batch=2,
+            rope=True, rope_dims=(44, 42, 42)),
 ]
 
 

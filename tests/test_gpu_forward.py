@@ -62,6 +62,11 @@ SMALL = [
     C.small("single-frame", (1, 9, 11), 2, 128, "bf16", [0, 1], 13, 64, 1),
     C.small("short", (1, 1, 37), 1, 128, "bf16", [1], 5, 64, 1),
     C.small("f32-d128-mixed", (2, 5, 9), 3, 128, "f32", [0, 1, 2], 11, 16, 2, batch=2),
+    # one token: every window and every Top-K selection is that token
+    C.small("one-token", (1, 1, 1), 2, 128, "bf16", [0, 2], 3, 64, 1),
+    # more than 64 heads: the head masks' later words; 256 is the maximum
+    C.small("70-heads", (1, 4, 20), 70, 128, "bf16", [h % 3 for h in range(70)], 9, 64, 1),
+    C.small("256-heads", (1, 2, 8), 256, 128, "bf16", [h % 3 for h in range(256)], 5, 64, 1, batch=2),
 ]
 
 
