@@ -124,6 +124,28 @@ def test_backward_with_dropping_and_fixed_gate(saved):
     _compare(w, got, ref, names=("dq", "dk", "dv", "dw_p", "ds"))
 
 
+def test_backward_one_token():
+    """One token: softmax over one key gives P = 1 and dS = P (dP - D) = 0,
+    and the linear branch's output v a / (a + eps) hardly depends on q or k,
+    so the exact dQ and dK are (nearly) zero.  The device's are the rounding
+    residue of that cancellation (M = H W_p is bf16, relative 2^-9 on terms of
+    the gradient's size), so they are held to 4e-3 (2^-8, twice that step) of
+    the gradient's natural scale, max |dV|; a dropped term or a wrong sign
+    would show at that scale itself.  Every other gradient takes the usual
+    relative bar."""
+    w = C.small("bwd-one-token", (1, 1, 1), 2, 128, "bf16", [1, 2], 3, 64, 1)
+    inp = I.make_inputs(w)
+    dout = _dout(w)
+    for saved in (False, True):
+        got = run_backward(w, inp, dout, saved=saved)
+        ref = oracle_backward(w, inp, dout)
+        _compare(w, got, ref, names=("dv", "dw_p", "dx", "dgate_w", "ds"))
+        scale = float(np.abs(ref["dv"]).max())
+        for n in ("dq", "dk"):
+            assert float(np.abs(ref[n]).max()) <= 1e-6 * scale, n
+            assert float(np.abs(got[n]).max()) <= 4e-3 * scale, f"{n}: {np.abs(got[n]).max():.3g} vs {scale:.3g}"
+
+
 def test_backward_is_deterministic():
     w = CASES[0]
     inp = I.make_inputs(w)
