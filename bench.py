@@ -92,20 +92,23 @@ def cpu_baseline(w, inp, flops_total: float, target_s: float = 15.0, proj: str =
     t_fixed = time.perf_counter() - t0
     total_rows = w.batch * w.N * heads
     n_rows, t_rows = min(64, total_rows), 0.0
-    while True:                                                  # grow the sample to ~target_s
+    spent = t_fixed
+    while True:              # double the sample until one call takes half of target_s
         rows = base_rows + [(int(rng.integers(w.batch)), int(rng.integers(w.N)),
                              int(rng.integers(heads))) for _ in range(n_rows)]
         t0 = time.perf_counter()
         O.attn_forward(*args, inp["gate_b"], rows=rows, **kw)
-        t_rows = max(time.perf_counter() - t0 - t_fixed, 1e-9)
-        if t_rows + t_fixed >= target_s / 3 or n_rows >= total_rows:
+        dt = time.perf_counter() - t0
+        spent += dt
+        t_rows = max(dt - t_fixed, 1e-9)
+        if dt >= target_s / 2 or n_rows >= total_rows:
             break
-        n_rows = min(4 * n_rows, total_rows)
+        n_rows = min(2 * n_rows, total_rows)
     per_row = t_rows / n_rows
     t_layer = t_fixed + per_row * (total_rows - len(base_rows))
     return {
         "value": flops_total / t_layer / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-        "kind": "oracle", "ms_per_layer_extrapolated": t_layer * 1e3,
+        "kind": "oracle", "ms_per_layer_extrapolated": t_layer * 1e3, "cpu_seconds_spent": spent,
         "sample": (f"fp64 numpy oracle ({proj} projection): one output row per (sample, head), "
                    f"which includes every "
                    f"head's per-layer work (gate, RoPE, working order, linear state, Top-K "
@@ -360,6 +363,32 @@ def main():
     attn_avg = attn_ms / max(calls, 1)
     achieved = flops / (attn_avg * 1e-3) / 1e12
 
+    # measured ceilings on this GPU, the second denominator of the fractions:
+    # a large square bf16 GEMM through torch (hipBLASLt) and a 1 GiB device copy
+    ceilings = None
+    if not args.backward:
+        a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+        bm = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.matmul(a, bm)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        for _ in range(10):
+            torch.matmul(a, bm)
+        e1.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e2.record()
+        torch.cuda.synchronize()
+        gemm_tf = 2.0 * 8192 ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+        copy_gbs = 2.0 * (1 << 30) / (e1.elapsed_time(e2) / 10 * 1e-3) / 1e9
+        ceilings = {"gemm_bf16_8192_tflops": gemm_tf, "copy_1gib_gbs": copy_gbs}
+        del a, bm, src, dst
+
     cold = None
     if not args.backward and args.cold_runs > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -422,6 +451,9 @@ def main():
     }
     if cold is not None:
         rec["cold_cache"] = cold
+    if ceilings is not None:
+        rec["ceilings"] = ceilings
+        rec["roofline"]["frac_of_measured_gemm"] = achieved / ceilings["gemm_bf16_8192_tflops"]
     if w.io_dtype != "bf16":
         rec["dtype"] = "f32"
     if traffic is not None and args.backward:
