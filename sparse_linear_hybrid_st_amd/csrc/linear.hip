@@ -400,8 +400,9 @@ hipError_t launch_linear_state(const Geom &g, int bf16, View kv, View vv, float 
 
 // ---------------------------------------------------------------------------
 // Apply, bf16, d = 128.  Grid (up to 1024/(B*H) workgroups, B*H), each over
-// 128-token tiles tile, tile + gridDim.x, ... (the staged H is reused); 4
-// waves x 32 tokens per tile.
+// 128-token tiles tile, tile + gridDim.x, ... (the staged H is reused, and
+// the next tile's Q rows load during this tile's MFMAs); 4 waves x 32
+// tokens per tile.
 // LDS holds H^T as bf16 hi and lo halves, [d_out][d_in], unit u of row j
 // at u ^ (j & 15).  Per wave: C[d_out][token] = sum_i H^T[d_out][i] relu(q)[i].
 // ---------------------------------------------------------------------------
@@ -415,40 +416,53 @@ __global__ void __launch_bounds__(256) linear_apply_bf16_kernel(Geom g, View qv,
   const int bh = blockIdx.y, h = bh % g.H, b = bh / g.H;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, hl = lane >> 5, l32 = lane & 31;
   const float *H = hm + (long long)bh * D * D;
-  // stage H^T: thread handles column j = t % 128 and units u = t/128 + 2*m
+  // stage H^T: thread handles column j = t % 128 and units u = t/128 + 2*m;
+  // all 64 loads are issued before the first conversion, so the staging
+  // pays one L2 round trip, not eight
   {
     const int j = t & 127;
-    for (int u = t >> 7; u < 16; u += 2) {
-      bf16x8 hi8, lo8;
+    float hv[8][8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[m][e] = H[((2 * m + (t >> 7)) * 8 + e) * D + j];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int u = 2 * m + (t >> 7);
       uint16_t his[8], los[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = H[(u * 8 + e) * D + j];
-        const bf16_t hi = f32_to_bf16(v);
+        const bf16_t hi = f32_to_bf16(hv[m][e]);
         his[e] = hi;
-        los[e] = f32_to_bf16(v - bf16_to_f32(hi));
+        los[e] = f32_to_bf16(hv[m][e] - bf16_to_f32(hi));
       }
-      hi8 = *(const bf16x8 *)his;
-      lo8 = *(const bf16x8 *)los;
       const int pu = u ^ (j & 15);
-      *(bf16x8 *)(Hhi + j * D + pu * 8) = hi8;
-      *(bf16x8 *)(Hlo + j * D + pu * 8) = lo8;
+      *(bf16x8 *)(Hhi + j * D + pu * 8) = *(const bf16x8 *)his;
+      *(bf16x8 *)(Hlo + j * D + pu * 8) = *(const bf16x8 *)los;
     }
     if (t < D) Zs[t] = zv[(long long)bh * D + t];
   }
   __syncthreads();
-  // the staged H serves several 128-token tiles (tile, tile + gridDim.x, ...)
+  // the staged H serves several 128-token tiles (tile, tile + gridDim.x, ...);
+  // the next tile's Q rows are loaded before this tile's MFMAs
   const int n_tiles = (g.N + 127) / 128;
+  const bf16_t *qb = (const bf16_t *)qv.base;
+  u32x4 qn[8];
+  auto load_q = [&](int tile) {
+    const int p = tile * 128 + w * 32 + l32;
+    const long long qoff = row_offset(g, qv, b, h, p < g.N ? p : g.N - 1);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qn[ks] = *(const u32x4 *)(qb + qoff + (2 * ks + hl) * 8);
+  };
+  if (int(blockIdx.x) < n_tiles) load_q(blockIdx.x);
   for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
     const int p = tile * 128 + w * 32 + l32;
     const bool valid = p < g.N;
-    const bf16_t *qb = (const bf16_t *)qv.base;
-    const long long qoff = row_offset(g, qv, b, h, valid ? p : g.N - 1);
     bf16x8 q[8];
     float den = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      u32x4 raw = relu_bf16x8(*(const u32x4 *)(qb + qoff + (2 * ks + hl) * 8));
+      u32x4 raw = relu_bf16x8(qn[ks]);
       q[ks] = *(bf16x8 *)&raw;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -456,6 +470,7 @@ __global__ void __launch_bounds__(256) linear_apply_bf16_kernel(Geom g, View qv,
         den = fmaf(bf16_to_f32(bf16_t(bits)), Zs[16 * ks + 8 * hl + e], den);
       }
     }
+    if (tile + int(gridDim.x) < n_tiles) load_q(tile + gridDim.x);
     // add the other half-wave's partial denominator (lanes l and l^32)
     den += __shfl_xor(den, 32);
     den += g.eps;
