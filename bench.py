@@ -311,9 +311,9 @@ def main():
     if args.stages:
         sys.exit(stages_bench(args, w, inp, p))
 
-    def fwd():
+    def fwd(events=None):
         S.salad_attn_forward(p, dev["q"], dev["k"], dev["v"], dev["x"], dev["w_p"], dev["gate_w"],
-                             inp["gate_b"], out, ws, s_out=s_out, idx_out=idx)
+                             inp["gate_b"], out, ws, s_out=s_out, idx_out=idx, events=events)
 
     step = fwd
     if args.backward:
@@ -330,11 +330,11 @@ def main():
         lse = None if args.recompute else torch.empty((w.batch, w.n_heads, w.N), dtype=torch.float32,
                                                       device="cuda")
 
-        def step():
+        def step(events=None):
             S.salad_attn_backward(p, dev["q"], dev["k"], dev["v"], dev["x"], dev["w_p"], dev["gate_w"],
                                   inp["gate_b"], g_out, grads["dq"], grads["dk"], grads["dv"], dwp, bws,
                                   dx=dx, dgate_w=dgw, dgate_b=dgb,
-                                  out_saved=None if args.recompute else out, lse_saved=lse)
+                                  out_saved=None if args.recompute else out, lse_saved=lse, events=events)
 
     # the forward once (its output and, for the backward, row normalisers)
     S.salad_attn_forward(p, dev["q"], dev["k"], dev["v"], dev["x"], dev["w_p"], dev["gate_w"],
@@ -350,17 +350,20 @@ def main():
     # dV, dK and dQ (the algorithmic count, not counting recomputation)
     flops = (10.0 if args.backward else 4.0) * w.head_dim * pairs
 
-    S.salad_profile_enable(True)
+    # HIP events the library records on its stream around the sparse-branch
+    # kernel(s) of every timed step (the *_timed entry points)
+    events = S.HipEvents(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(events=events.pairs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    calls, attn_ms = S.salad_profile_read()
-    S.salad_profile_enable(False)
+    attn_times = events.elapsed_ms(args.steps)
+    events.close()
+    calls = len(attn_times)
     ms = wall * 1e3 / args.steps
-    attn_avg = attn_ms / max(calls, 1)
+    attn_avg = sum(attn_times) / max(calls, 1)
     achieved = flops / (attn_avg * 1e-3) / 1e12
 
     # measured ceilings on this GPU, the second denominator of the fractions:

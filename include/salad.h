@@ -90,10 +90,12 @@ typedef struct {
   int32_t batch;                      /* B >= 1                                   */
   int32_t n_heads;                    /* H in [1, SALAD_MAX_HEADS]                */
   int32_t head_dim;                   /* d in {64, 128}                           */
-  int32_t grid_f, grid_h, grid_w;     /* latent F x Hg x Wg; N = F*Hg*Wg <= 2^28,
-                                         B*H*N < 2^31 rows, B*H*N*d <= 2^40      */
+  int32_t grid_f, grid_h, grid_w;     /* latent F x Hg x Wg; N = F*Hg*Wg <= 2^28
+                                         (bf16: N < 2^24), B*H*N < 2^31 rows,
+                                         B*H*N*d <= 2^40                         */
   uint8_t head_kind[SALAD_MAX_HEADS]; /* per head: SALAD_HEAD_* (first H used)    */
-  int32_t window_radius;              /* window heads keep key j iff |p-j| <= r   */
+  int32_t window_radius;              /* window heads keep key j iff |p-j| <= r;
+                                         r >= N-1 acts as N-1 (dense)            */
   int32_t block;                      /* Top-K block size (queries and keys)      */
   int32_t topk;                       /* Top-K: key blocks kept per query block   */
   float softmax_scale;                /* <= 0 selects 1/sqrt(d)                   */
@@ -260,17 +262,29 @@ salad_status salad_window_calibrate(const salad_problem *p, const void *qw, cons
 salad_status salad_output_projection(const salad_problem *p, const void *in, const void *w_o,
                                      void *out, hipStream_t stream);
 
-/* Measurement hook.  While enabled (on != 0), salad_attn_forward records a
- * pair of HIP events around its sparse-attention kernel launch(es) on the
- * caller's stream, and salad_attn_backward around its sparse-branch
- * gradient kernels (dQ, then dK and dV); the first 4096 calls after
- * enabling are recorded.
- * salad_profile_read waits for the recorded events, returns the number of
- * timed calls and their summed duration in milliseconds, and clears the
- * record.  Process-wide state; not thread-safe; not for use under graph
- * capture.  Errors: SALAD_ERR_NULL (read with NULL outputs), SALAD_ERR_HIP. */
-salad_status salad_profile_enable(int on);
-salad_status salad_profile_read(int *calls, double *total_ms);
+/* Measurement variants of salad_attn_forward and salad_attn_backward, for
+ * callers that time the sparse-branch kernels on their own stream (the
+ * forward's attention kernel(s); the backward's dQ, then dK and dV kernels):
+ * identical arguments and results, and in addition the caller-created
+ * events attn_begin and attn_end (either may be NULL) are recorded on
+ * `stream` immediately before the first and after the last of those
+ * kernels.  The library keeps no state and creates or waits for no event.
+ * Errors as for the plain calls; a failed event record is SALAD_ERR_HIP. */
+salad_status salad_attn_forward_timed(const salad_problem *p, const void *q, const void *k,
+                                      const void *v, const void *x, const void *w_p,
+                                      const void *gate_w, float gate_b, const float *s_override,
+                                      void *out, float *s_out, int32_t *idx_out, float *lse_out,
+                                      void *ws, size_t ws_bytes, hipStream_t stream,
+                                      hipEvent_t attn_begin, hipEvent_t attn_end);
+salad_status salad_attn_backward_timed(const salad_problem *p, const void *q, const void *k,
+                                       const void *v, const void *x, const void *w_p,
+                                       const void *gate_w, float gate_b, const float *s_override,
+                                       const void *dout, const void *out_saved,
+                                       const float *lse_saved, void *dq, void *dk, void *dv,
+                                       float *dw_p, void *dx, float *dgate_w, float *dgate_b,
+                                       float *ds_out, void *ws, size_t ws_bytes,
+                                       hipStream_t stream, hipEvent_t attn_begin,
+                                       hipEvent_t attn_end);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *salad_last_error(void);

@@ -32,7 +32,7 @@ EXPORTS = ("salad_workspace_size", "salad_permute", "salad_block_select", "salad
            "salad_linear_state", "salad_linear_apply", "salad_gate", "salad_combine",
            "salad_attn_forward", "salad_output_projection", "salad_backward_workspace_size",
            "salad_attn_backward", "salad_calibrate_workspace_size", "salad_window_calibrate",
-           "salad_profile_enable", "salad_profile_read", "salad_last_error")
+           "salad_attn_forward_timed", "salad_attn_backward_timed", "salad_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -109,10 +109,10 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
-        L.salad_profile_enable.argtypes = [i32]
-        L.salad_profile_enable.restype = ctypes.c_int
-        L.salad_profile_read.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
-        L.salad_profile_read.restype = ctypes.c_int
+        for name in ("salad_attn_forward", "salad_attn_backward"):
+            fn = getattr(L, name + "_timed")
+            fn.argtypes = sigs[name] + [vp, vp]
+            fn.restype = ctypes.c_int
         L.salad_last_error.argtypes = []
         L.salad_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -267,20 +267,26 @@ def salad_combine(p: Problem, o_s, o_l, w_p, s, out, stream=None):
 
 
 def salad_attn_forward(p: Problem, q, k, v, x, w_p, gate_w, gate_b: float, out, ws,
-                       s_override=None, s_out=None, idx_out=None, lse_out=None, stream=None):
+                       s_override=None, s_out=None, idx_out=None, lse_out=None, stream=None,
+                       events=None):
+    """The whole layer.  events: optional (begin, end) raw hipEvent_t handles
+    (see :class:`HipEvents`), recorded around the sparse-attention kernel
+    through salad_attn_forward_timed."""
     import torch
     n, _ = _sizes(p)
     dt = _io_dtype(p)
     C = p.n_heads * p.head_dim
     nidx = p.batch * p.n_heads * p.n_blocks * p.topk
-    _check(lib().salad_attn_forward(
+    fn, extra = (lib().salad_attn_forward, ()) if events is None else \
+        (lib().salad_attn_forward_timed, tuple(ctypes.c_void_p(e) for e in events))
+    _check(fn(
         ctypes.byref(p), _ptr(q, "q", n, dt), _ptr(k, "k", n, dt), _ptr(v, "v", n, dt),
         _ptr(x, "x", p.batch * p.N * C, dt), _ptr(w_p, "w_p", p.w_p_numel, dt),
         _ptr(gate_w, "gate_w", C, dt), float(gate_b),
         _ptr(s_override, "s_override", p.batch, torch.float32), _ptr(out, "out", n, dt),
         _ptr(s_out, "s_out", p.batch, torch.float32), _ptr(idx_out, "idx_out", nidx, torch.int32),
         _ptr(lse_out, "lse_out", p.batch * p.n_heads * p.N, torch.float32),
-        _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream), *extra))
 
 
 def salad_output_projection(p: Problem, x, w_o, out, stream=None):
@@ -300,16 +306,20 @@ def salad_backward_workspace_size(p: Problem) -> int:
 
 def salad_attn_backward(p: Problem, q, k, v, x, w_p, gate_w, gate_b: float, dout, dq, dk, dv, dw_p, ws,
                         dx=None, dgate_w=None, dgate_b=None, ds=None, s_override=None, out_saved=None,
-                        lse_saved=None, stream=None):
+                        lse_saved=None, stream=None, events=None):
     """Gradients of sum(dout * salad_attn_forward(...)): dq, dk, dv [B,N,H,d]
     and dx [B,N,C] in bf16; dw_p [d,d], dgate_w [C], dgate_b [1], ds [B] in
     float32 (dx, dgate_w, dgate_b, ds optional).  out_saved / lse_saved: the
-    forward's out and lse_out for the same inputs (skips the recompute)."""
+    forward's out and lse_out for the same inputs (skips the recompute).
+    events: optional (begin, end) hipEvent_t handles recorded around the
+    sparse-branch gradient kernels (salad_attn_backward_timed)."""
     import torch
     n, _ = _sizes(p)
     dt = _io_dtype(p)
     C = p.n_heads * p.head_dim
-    _check(lib().salad_attn_backward(
+    fn, extra = (lib().salad_attn_backward, ()) if events is None else \
+        (lib().salad_attn_backward_timed, tuple(ctypes.c_void_p(e) for e in events))
+    _check(fn(
         ctypes.byref(p), _ptr(q, "q", n, dt), _ptr(k, "k", n, dt), _ptr(v, "v", n, dt),
         _ptr(x, "x", p.batch * p.N * C, dt), _ptr(w_p, "w_p", p.w_p_numel, dt),
         _ptr(gate_w, "gate_w", C, dt), float(gate_b),
@@ -320,7 +330,7 @@ def salad_attn_backward(p: Problem, q, k, v, x, w_p, gate_w, gate_b: float, dout
         _ptr(dw_p, "dw_p", p.head_dim ** 2, torch.float32), _ptr(dx, "dx", p.batch * p.N * C, dt),
         _ptr(dgate_w, "dgate_w", C, torch.float32), _ptr(dgate_b, "dgate_b", 1, torch.float32),
         _ptr(ds, "ds", p.batch, torch.float32), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
-        _stream(stream)))
+        _stream(stream), *extra))
 
 
 def salad_calibrate_workspace_size(p: Problem) -> int:
@@ -361,12 +371,43 @@ def workspace(p: Problem, device="cuda"):
     return torch.empty(max(salad_workspace_size(p), 16), dtype=torch.uint8, device=device)
 
 
-def salad_profile_enable(on: bool):
-    _check(lib().salad_profile_enable(int(bool(on))))
+class HipEvents:
+    """Timing events from the HIP runtime (plumbing for measurement, not part
+    of the computation): ``count`` event pairs created up front, handed to
+    the ``*_timed`` entry points as raw handles, read back after a sync."""
 
+    def __init__(self, count: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(count):
+            pair = []
+            for _ in range(2):
+                e = ctypes.c_void_p()
+                if self._hip.hipEventCreate(ctypes.byref(e)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                pair.append(e.value)
+            self.pairs.append(tuple(pair))
 
-def salad_profile_read():
-    """(calls, total_ms) of the sparse-attention launches timed since enabling."""
-    c, ms = ctypes.c_int(0), ctypes.c_double(0.0)
-    _check(lib().salad_profile_read(ctypes.byref(c), ctypes.byref(ms)))
-    return c.value, ms.value
+    def elapsed_ms(self, n: int):
+        """Milliseconds between begin and end of the first n pairs (each end
+        event waited for)."""
+        out = []
+        for b, e in self.pairs[:n]:
+            if self._hip.hipEventSynchronize(ctypes.c_void_p(e)) != 0:
+                raise RuntimeError("hipEventSynchronize failed")
+            ms = ctypes.c_float(0.0)
+            if self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(b), ctypes.c_void_p(e)) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for pair in self.pairs:
+            for e in pair:
+                self._hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.pairs = []

@@ -61,6 +61,10 @@ salad_status validate(const salad_problem *p, Info *inf) {
   if ((long long)p->batch * p->n_heads * N * p->head_dim > (1ll << 40) ||
       (long long)p->batch * p->n_heads * N >= (1ll << 31))
     return fail(SALAD_ERR_SHAPE, "tensor too large (batch*n_heads*N must stay below 2^31 rows)");
+  // the bf16 attention kernels address one head's K/V rows with 32-bit byte
+  // offsets: N rows of 256 bytes in a contiguous working copy
+  if (p->io_dtype == SALAD_BF16 && N * 128 * 2 > (1ll << 32) - 1)
+    return fail(SALAD_ERR_UNSUPPORTED, "bf16 kernels take N < 2^24 tokens (got %lld)", N);
   Geom &g = inf->g;
   memset(&g, 0, sizeof g);
   g.B = p->batch;
@@ -80,7 +84,9 @@ salad_status validate(const salad_problem *p, Info *inf) {
   }
   if (inf->any_window && p->window_radius < 0)
     return fail(SALAD_ERR_SHAPE, "window_radius must be >= 0 (got %d)", p->window_radius);
-  g.r = p->window_radius < 0 ? 0 : p->window_radius;
+  // a radius past N - 1 keeps the same keys as N - 1; clamping it keeps the
+  // kernels' 32-bit window arithmetic (q0 + tile + r, 2r) in range
+  g.r = p->window_radius < 0 ? 0 : (int)std::min<long long>(p->window_radius, N - 1);
   if (inf->any_topk) {
     if (p->block < 1) return fail(SALAD_ERR_SHAPE, "block must be >= 1 (got %d)", p->block);
     g.block = p->block;
@@ -238,52 +244,17 @@ View working_view(const Geom &g, const void *base) {
   return v;
 }
 
-// Event pairs around the sparse-attention launch of salad_attn_forward.
-struct Profile {
-  int on = 0, used = 0;
-  hipEvent_t ev[2 * 4096];
-  int created = 0;
-} g_prof;
+// Optional caller-created events recorded around the sparse-branch kernels
+// (the measurement variants of the forward and backward); NULL: none.
+struct Marks {
+  hipEvent_t begin = nullptr, end = nullptr;
+};
 
-hipError_t prof_mark(int which, hipStream_t st) {
-  if (!g_prof.on || g_prof.used >= 4096) return hipSuccess;
-  const int i = 2 * g_prof.used + which;
-  while (g_prof.created <= i) {
-    hipError_t e = hipEventCreate(&g_prof.ev[g_prof.created]);
-    if (e != hipSuccess) return e;
-    ++g_prof.created;
-  }
-  hipError_t e = hipEventRecord(g_prof.ev[i], st);
-  if (which == 1) ++g_prof.used;
-  return e;
-}
+hipError_t mark(hipEvent_t ev, hipStream_t st) { return ev ? hipEventRecord(ev, st) : hipSuccess; }
 
 }  // namespace
 
 extern "C" {
-
-salad_status salad_profile_enable(int on) {
-  g_prof.on = on != 0;
-  g_prof.used = 0;
-  return SALAD_OK;
-}
-
-salad_status salad_profile_read(int *calls, double *total_ms) {
-  if (!calls || !total_ms) return fail(SALAD_ERR_NULL, "calls / total_ms is NULL");
-  double tot = 0.0;
-  for (int i = 0; i < g_prof.used; ++i) {
-    hipError_t e = hipEventSynchronize(g_prof.ev[2 * i + 1]);
-    if (e != hipSuccess) return hip_status(e, "salad_profile_read");
-    float ms = 0.f;
-    e = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
-    if (e != hipSuccess) return hip_status(e, "salad_profile_read");
-    tot += ms;
-  }
-  *calls = g_prof.used;
-  *total_ms = tot;
-  g_prof.used = 0;
-  return SALAD_OK;
-}
 
 salad_status salad_workspace_size(const salad_problem *p, size_t *bytes) {
   Info inf;
@@ -400,10 +371,14 @@ salad_status salad_combine(const salad_problem *p, const float *o_s, const float
   return hip_status(launch_combine(inf.g, inf.bf16, o_s, o_l, w_p, s, out, stream), "salad_combine");
 }
 
-salad_status salad_attn_forward(const salad_problem *p, const void *q, const void *k, const void *v,
-                                const void *x, const void *w_p, const void *gate_w, float gate_b,
-                                const float *s_override, void *out, float *s_out, int32_t *idx_out,
-                                float *lse_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+salad_status attn_forward(const salad_problem *p, const void *q, const void *k, const void *v, const void *x,
+                          const void *w_p, const void *gate_w, float gate_b, const float *s_override, void *out,
+                          float *s_out, int32_t *idx_out, float *lse_out, void *ws, size_t ws_bytes,
+                          hipStream_t stream, Marks marks) {
   Info inf;
   CHECK(validate(p, &inf));
   CHECK(need(q, "q"));
@@ -491,10 +466,10 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
     }
     View outl = boundary_view(g, w + pl.olt);  // s_b * O_l rows (full-width projection only)
     if (!inf.full) outl.base = nullptr;
-    if ((e = prof_mark(0, stream)) != hipSuccess ||
+    if ((e = mark(marks.begin, stream)) != hipSuccess ||
         (e = launch_attn_fused(g, qv, kw, vw, kd, vd, work, idx, hp, zv, s, boundary_view(g, out), outl,
                                lse_out, stream)) != hipSuccess ||
-        (e = prof_mark(1, stream)) != hipSuccess)
+        (e = mark(marks.end, stream)) != hipSuccess)
       return hip_status(e, "salad_attn_forward: attention");
     if (inf.full) return project_full(inf, w + pl.olt, w_p, out, stream);
     return SALAD_OK;
@@ -515,9 +490,9 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
     e = launch_block_select(g, inf.bf16, qv, kv, qm, km, sc, idx, stream);
     if (e != hipSuccess) return hip_status(e, "salad_attn_forward: block select");
   }
-  if ((e = prof_mark(0, stream)) != hipSuccess ||
+  if ((e = mark(marks.begin, stream)) != hipSuccess ||
       (e = launch_sparse_attn(g, inf.bf16, qv, kv, vv, idx, o_s, stream)) != hipSuccess ||
-      (e = prof_mark(1, stream)) != hipSuccess)
+      (e = mark(marks.end, stream)) != hipSuccess)
     return hip_status(e, "salad_attn_forward: sparse attention");
   if ((e = launch_linear_state(g, inf.bf16, kv, vv, (float *)scratch, hm, zv, stream)) != hipSuccess)
     return hip_status(e, "salad_attn_forward: linear state");
@@ -531,6 +506,30 @@ salad_status salad_attn_forward(const salad_problem *p, const void *q, const voi
   if ((e = launch_combine(g, inf.bf16, o_s, o_l, w_p, s, out, stream)) != hipSuccess)
     return hip_status(e, "salad_attn_forward: combine");
   return SALAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+salad_status salad_attn_forward(const salad_problem *p, const void *q, const void *k, const void *v,
+                                const void *x, const void *w_p, const void *gate_w, float gate_b,
+                                const float *s_override, void *out, float *s_out, int32_t *idx_out,
+                                float *lse_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return attn_forward(p, q, k, v, x, w_p, gate_w, gate_b, s_override, out, s_out, idx_out, lse_out, ws,
+                      ws_bytes, stream, Marks());
+}
+
+salad_status salad_attn_forward_timed(const salad_problem *p, const void *q, const void *k, const void *v,
+                                      const void *x, const void *w_p, const void *gate_w, float gate_b,
+                                      const float *s_override, void *out, float *s_out, int32_t *idx_out,
+                                      float *lse_out, void *ws, size_t ws_bytes, hipStream_t stream,
+                                      hipEvent_t attn_begin, hipEvent_t attn_end) {
+  Marks m;
+  m.begin = attn_begin;
+  m.end = attn_end;
+  return attn_forward(p, q, k, v, x, w_p, gate_w, gate_b, s_override, out, s_out, idx_out, lse_out, ws,
+                      ws_bytes, stream, m);
 }
 
 salad_status salad_output_projection(const salad_problem *p, const void *in, const void *w_o, void *out,
@@ -703,12 +702,15 @@ salad_status salad_backward_workspace_size(const salad_problem *p, size_t *bytes
   return SALAD_OK;
 }
 
-salad_status salad_attn_backward(const salad_problem *p, const void *q, const void *k, const void *v,
-                                 const void *x, const void *w_p, const void *gate_w, float gate_b,
-                                 const float *s_override, const void *dout, const void *out_saved,
-                                 const float *lse_saved, void *dq, void *dk, void *dv, float *dw_p, void *dx,
-                                 float *dgate_w, float *dgate_b, float *ds_out, void *ws, size_t ws_bytes,
-                                 hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+salad_status attn_backward(const salad_problem *p, const void *q, const void *k, const void *v, const void *x,
+                           const void *w_p, const void *gate_w, float gate_b, const float *s_override,
+                           const void *dout, const void *out_saved, const float *lse_saved, void *dq, void *dk,
+                           void *dv, float *dw_p, void *dx, float *dgate_w, float *dgate_b, float *ds_out,
+                           void *ws, size_t ws_bytes, hipStream_t stream, Marks marks) {
   Info inf;
   CHECK(validate_backward(p, &inf));
   CHECK(need(q, "q"));
@@ -837,11 +839,11 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
   bo.dv = (bf16_t *)dv;
   if ((!saved && (e = launch_attn_bwd_prep(g, qb, kv, vv, kd, vd, work, idx, wg, (const bf16_t *)dout, lse,
                                           dsum, pl.Np, stream)) != hipSuccess) ||
-      (e = prof_mark(0, stream)) != hipSuccess ||
+      (e = mark(marks.begin, stream)) != hipSuccess ||
       (e = launch_attn_bwd(g, wq, wk, wv, wg, (const bf16_t *)qsrc, (const bf16_t *)ksrc, (const bf16_t *)v,
                            (const bf16_t *)dout, work, lse, dsum, pl.Np, idx, inv_off, inv_list, bo, stream)) !=
           hipSuccess ||
-      (e = prof_mark(1, stream)) != hipSuccess)
+      (e = mark(marks.end, stream)) != hipSuccess)
     return hip_status(e, "salad_attn_backward: sparse attention");
   // gate
   float *dt = (float *)(w + pl.dt);
@@ -850,6 +852,34 @@ salad_status salad_attn_backward(const salad_problem *p, const void *q, const vo
       (has_gate && dx && (e = launch_gate_dx(g, dt, (const bf16_t *)gate_w, (bf16_t *)dx, stream)) != hipSuccess))
     return hip_status(e, "salad_attn_backward: gate");
   return SALAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+salad_status salad_attn_backward(const salad_problem *p, const void *q, const void *k, const void *v,
+                                 const void *x, const void *w_p, const void *gate_w, float gate_b,
+                                 const float *s_override, const void *dout, const void *out_saved,
+                                 const float *lse_saved, void *dq, void *dk, void *dv, float *dw_p, void *dx,
+                                 float *dgate_w, float *dgate_b, float *ds_out, void *ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  return attn_backward(p, q, k, v, x, w_p, gate_w, gate_b, s_override, dout, out_saved, lse_saved, dq, dk, dv,
+                       dw_p, dx, dgate_w, dgate_b, ds_out, ws, ws_bytes, stream, Marks());
+}
+
+salad_status salad_attn_backward_timed(const salad_problem *p, const void *q, const void *k, const void *v,
+                                       const void *x, const void *w_p, const void *gate_w, float gate_b,
+                                       const float *s_override, const void *dout, const void *out_saved,
+                                       const float *lse_saved, void *dq, void *dk, void *dv, float *dw_p,
+                                       void *dx, float *dgate_w, float *dgate_b, float *ds_out, void *ws,
+                                       size_t ws_bytes, hipStream_t stream, hipEvent_t attn_begin,
+                                       hipEvent_t attn_end) {
+  Marks m;
+  m.begin = attn_begin;
+  m.end = attn_end;
+  return attn_backward(p, q, k, v, x, w_p, gate_w, gate_b, s_override, dout, out_saved, lse_saved, dq, dk, dv,
+                       dw_p, dx, dgate_w, dgate_b, ds_out, ws, ws_bytes, stream, m);
 }
 
 const char *salad_last_error(void) { return g_err.c_str(); }

@@ -78,6 +78,7 @@ def test_size_limits():
     """Row indices are 32-bit inside the kernels: B*H*N must stay below 2^31
     (and N below 2^28); the largest accepted sizes pass."""
     p = S.problem_from_workload(configs.swa_480p())
+    p.io_dtype = S.SALAD_F32                                     # bf16 stops at N < 2^24 (below)
     p.grid_f, p.grid_h, p.grid_w = 1 << 10, 1 << 9, 1 << 9      # N = 2^28
     p.n_heads, p.batch = 4, 2                                    # B*H*N = 2^31
     p.window_radius = 64
@@ -131,3 +132,32 @@ def test_projection_mode_checks():
     assert b"overlap" in L.salad_last_error()
     with pytest.raises(ValueError):
         S.problem_from_workload(w, proj="rows")
+
+
+def test_bf16_token_limit_is_checked_before_any_launch():
+    """The bf16 attention kernels address one head's rows with 32-bit byte
+    offsets (N rows of 256 bytes): N = 2^24 is rejected up front with
+    SALAD_ERR_UNSUPPORTED, N = 2^24 - 2^10 is accepted."""
+    L = S.lib()
+    p = S.problem_from_workload(configs.swa_480p())
+    p.n_heads, p.batch = 1, 1
+    p.grid_f, p.grid_h, p.grid_w = 1 << 4, 1 << 10, 1 << 10      # N = 2^24
+    assert _status(p)[0] == 3 and b"2^24" in L.salad_last_error()
+    a = ctypes.c_void_p(0x10000)
+    assert L.salad_attn_forward(ctypes.byref(p), a, a, a, a, a, a, 0.0, None, a, None, None, None,
+                                a, 1 << 40, None) == 3
+    p.grid_f = (1 << 4) - 1
+    assert _status(p)[0] == 0, L.salad_last_error()
+
+
+def test_window_radius_past_the_sequence_is_accepted():
+    """r >= N - 1 keeps every key (the same set as N - 1): INT32_MAX is a
+    valid radius and needs the same workspace as N - 1."""
+    w = configs.swa_480p()
+    p = S.problem_from_workload(w)
+    p.window_radius = w.N - 1
+    st, n_dense = _status(p)
+    assert st == 0
+    p.window_radius = 2 ** 31 - 1
+    st, n_max = _status(p)
+    assert st == 0 and n_max == n_dense, S.lib().salad_last_error()

@@ -43,9 +43,13 @@ def _dout(w):
     return I.to_storage(g, w.io_dtype)
 
 
-def run_backward(w, inp, dout, s_override=None, branch_drop_tau=0.0, saved=False):
+def run_backward(w, inp, dout, s_override=None, branch_drop_tau=0.0, saved=False, repeat=False):
     """salad_attn_backward on the device; with saved=True the forward runs
-    first and its out and row normalisers are handed to the backward."""
+    first and its out and row normalisers are handed to the backward.  With
+    repeat=True the backward runs a second time into fresh buffers (same
+    workspace) and every output must equal the first call's bit for bit: a
+    race between waves or a read of memory the call did not write shows up
+    as a difference."""
     p = S.problem_from_workload(w, branch_drop_tau=branch_drop_tau)
     d = {n: dev(inp[n]) for n in ("q", "k", "v", "x", "w_p", "gate_w")}
     go = dev(dout)
@@ -62,10 +66,23 @@ def run_backward(w, inp, dout, s_override=None, branch_drop_tau=0.0, saved=False
     dgw = torch.empty(w.n_heads * w.head_dim, dtype=torch.float32, device="cuda")
     dgb = torch.empty(1, dtype=torch.float32, device="cuda")
     ds = torch.empty(w.batch, dtype=torch.float32, device="cuda")
+    bws = S.backward_workspace(p)
     S.salad_attn_backward(p, d["q"], d["k"], d["v"], d["x"], d["w_p"], d["gate_w"], inp["gate_b"], go,
-                          dq, dk, dv, dwp, S.backward_workspace(p), dx=dx, dgate_w=dgw, dgate_b=dgb, ds=ds,
+                          dq, dk, dv, dwp, bws, dx=dx, dgate_w=dgw, dgate_b=dgb, ds=ds,
                           s_override=so, out_saved=out, lse_saved=lse)
     torch.cuda.synchronize()
+    if repeat:
+        first = {"dq": dq, "dk": dk, "dv": dv, "dx": dx, "dw_p": dwp, "dgate_w": dgw, "dgate_b": dgb, "ds": ds}
+        again = {n: torch.full_like(t, float("nan")) for n, t in first.items()}
+        S.salad_attn_backward(p, d["q"], d["k"], d["v"], d["x"], d["w_p"], d["gate_w"], inp["gate_b"], go,
+                              again["dq"], again["dk"], again["dv"], again["dw_p"], bws, dx=again["dx"],
+                              dgate_w=again["dgate_w"], dgate_b=again["dgate_b"], ds=again["ds"],
+                              s_override=so, out_saved=out, lse_saved=lse)
+        torch.cuda.synchronize()
+        for n, t in first.items():
+            if not torch.equal(t, again[n]):
+                bad = (t != again[n]).reshape(t.shape[0], -1).any(dim=-1).nonzero()
+                raise AssertionError(f"{w.name}: second backward call differs in {n} ({len(bad)} leading rows)")
     return {"dq": host64(dq), "dk": host64(dk), "dv": host64(dv), "dx": host64(dx), "dw_p": host64(dwp),
             "dgate_w": host64(dgw), "dgate_b": float(dgb.item()), "ds": host64(ds)}
 
@@ -185,7 +202,8 @@ def test_backward_full_size_sampled_rows(name):
     w = C.all_workloads()[name]
     inp = I.make_inputs(w)
     dout = _dout(w)
-    got = run_backward(w, inp, dout, saved=True)
+    got = run_backward(w, inp, dout, saved=True, repeat=True)
+    print(f"{name}: two backward calls bitwise equal", flush=True)
     rows_q, rows_kv = _sample(w, 10, 4, seed=11)
     args = [inp[n].float().numpy() for n in ("q", "k", "v", "x")] + \
         [I.as_f64(inp[n]) for n in ("w_p", "gate_w")]

@@ -1,7 +1,9 @@
 """Parity at the workloads' full sizes, through salad_attn_forward exactly as
 bench.py launches it.  The oracle checks the gate values and every Top-K
-block selection in full, and a sample of output rows one by one (edge tokens,
-tile boundaries and random rows, over every head kind)."""
+block selection in full, one whole head of every head kind element by
+element (all N rows; the oracle's rows spread over CPU processes), and a
+sample of output rows over every head (edge tokens, tile boundaries and
+random rows)."""
 
 import time
 
@@ -15,6 +17,7 @@ from sparse_linear_hybrid_st_amd import configs as C
 from sparse_linear_hybrid_st_amd import inputs as I
 from tests.gpu_util import (assert_close, check_selection, host64, oracle_kwargs, rel_fro,
                             run_forward)
+from tests.oracle_pool import whole_head, workers
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(600)]
 
@@ -61,7 +64,8 @@ def _repeat_bitwise(w, inp, out, reps=4):
                                  f"first {bad[:4].tolist()}")
 
 
-def _check_workload(w, n_rand=24):
+def _check_workload(w, whole, n_rand=24):
+    """``whole``: (b, h) pairs whose entire output head is compared."""
     t0 = time.time()
     inp = I.make_inputs(w)
     _log(f"{w.name}: inputs {time.time() - t0:.1f}s; running salad_attn_forward")
@@ -73,9 +77,9 @@ def _check_workload(w, n_rand=24):
         [I.as_f64(inp[n]) for n in ("w_p", "gate_w")]
     kw = oracle_kwargs(w)
     # gate: every sample
+    s_ref = [O.gate(args[3][b], args[5], inp["gate_b"]) for b in range(w.batch)]
     for b in range(w.batch):
-        ref = O.gate(args[3][b], args[5], inp["gate_b"])
-        assert abs(float(s[b]) - ref) <= 1e-6, (b, float(s[b]), ref)
+        assert abs(float(s[b]) - s_ref[b]) <= 1e-6, (b, float(s[b]), s_ref[b])
     # Top-K selection: every query block of every Top-K head
     differ_blocks = {}
     for h, kind in enumerate(w.head_kinds):
@@ -105,12 +109,23 @@ def _check_workload(w, n_rand=24):
     _log(f"{w.name}: {len(errs)} rows, max abs {err.max():.3g}, mean abs {err.mean():.3g} "
          f"({time.time() - t0:.1f}s)")
     assert err.max() <= 2e-2 and err.mean() <= 2e-3
+    # whole heads, element by element
+    for (b, h) in whole:
+        t1 = time.time()
+        ref_h = whole_head(w, args, s_ref[b], b, h)
+        got_h = got[b, :, h]
+        if w.head_kinds[h] == 2 and differ_blocks.get((b, h)):
+            keep = np.array([(n // w.block) not in differ_blocks[(b, h)] for n in range(w.N)])
+            ref_h, got_h = ref_h[keep], got_h[keep]
+        mx, mn = assert_close(got_h, ref_h, w.io_dtype, f"{w.name} whole head b{b} h{h}")
+        _log(f"{w.name}: whole head b{b} h{h} (kind {w.head_kinds[h]}, {got_h.shape[0]} rows): max abs "
+             f"{mx:.3g}, mean abs {mn:.3g} ({time.time() - t1:.1f}s on {workers()} processes)")
     return inp, out
 
 
 def test_full_480p_window_12_heads():
     w = C.swa_480p()
-    inp, _ = _check_workload(w)
+    inp, _ = _check_workload(w, whole=[(0, 0), (0, 1)])
     # linear state at full size through the staged entry point
     p = S.problem_from_workload(w)
     kd, vd = inp["k"].cuda(), inp["v"].cuda()
@@ -129,12 +144,13 @@ def test_full_480p_window_12_heads():
 
 
 def test_full_480p_topk_40_heads():
-    _check_workload(C.topk_480p())
+    _check_workload(C.topk_480p(), whole=[(0, 17)])
 
 
 def test_full_720p_window_40_heads():
-    _check_workload(C.swa_720p(), n_rand=16)
+    _check_workload(C.swa_720p(), whole=[(0, 38), (0, 39)], n_rand=16)
 
 
 def test_full_480p_cfg_rope_mixed_heads():
-    _check_workload(C.cfg_rope_480p(), n_rand=16)
+    # spatial (h % 4 == 0), temporal (1) and Top-K (2, 3) heads, both samples
+    _check_workload(C.cfg_rope_480p(), whole=[(0, 0), (1, 5), (1, 2), (0, 39)], n_rand=16)

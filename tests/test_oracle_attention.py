@@ -143,3 +143,46 @@ def test_topk_matches_masked_dense():
             allowed[p, kb * bs:min(N, (kb + 1) * bs)] = True
     np.testing.assert_allclose(out, _sdpa(q, k_, v, allowed), rtol=0, atol=1e-12)
     assert O.topk_pair_count(idx, bs, N) == int(allowed.sum())
+
+
+def test_topk_gap_finite_values():
+    """The gap between the k-th and (k+1)-th best block scores ([I] 1.2 keeps
+    the k best; a smaller gap means the choice hangs on rounding), checked on
+    hand-built score rows: qbar = 1 and kbar = diag(values) make the scores of
+    row 0 the listed values exactly."""
+    vals = np.array([5.0, 3.0, 9.0, 3.5, 1.0])
+    qbar = np.ones((1, 5))
+    kbar = np.diag(vals)
+    # descending 9, 5, 3.5, 3, 1: k = 2 compares 5 with 3.5 -> 1.5 / 5
+    assert O.topk_gap(qbar, kbar, 2)[0] == 0.3
+    # k = 1 compares 9 with 5 -> 4 / 9; k = 4 compares 3 with 1 -> 2 / 3
+    assert O.topk_gap(qbar, kbar, 1)[0] == 4.0 / 9.0
+    assert O.topk_gap(qbar, kbar, 4)[0] == 2.0 / 3.0
+    # negative scores: the larger magnitude scales the gap
+    neg = np.diag(np.array([-1.0, -4.0, -2.0]))
+    assert O.topk_gap(np.ones((1, 3)), neg, 1)[0] == 0.5      # -1 vs -2 -> 1 / 2
+    assert O.topk_gap(np.ones((1, 3)), neg, 2)[0] == 0.5      # -2 vs -4 -> 2 / 4
+    # an exact tie at the boundary gives 0, whatever the other scores
+    tie = np.diag(np.array([7.0, 2.0, 7.0, 2.0]))
+    assert O.topk_gap(np.ones((1, 4)), tie, 1)[0] == 0.0
+    assert O.topk_gap(np.ones((1, 4)), tie, 3)[0] == 0.0
+    # several rows at once (row r scales the scores by r + 1: same gaps)
+    q3 = np.array([[1.0] * 5, [2.0] * 5, [3.0] * 5])
+    np.testing.assert_array_equal(O.topk_gap(q3, kbar, 2), [0.3, 0.3, 0.3])
+
+
+def test_topk_gap_matches_exact_rational_brute_force():
+    """Random small integer means: every score is an exact integer, so the
+    gap can be formed in exact rationals from a Python sort."""
+    from fractions import Fraction
+    rng = np.random.default_rng(31)
+    qbar = rng.integers(-4, 5, size=(9, 3)).astype(np.float64)
+    kbar = rng.integers(-4, 5, size=(11, 3)).astype(np.float64)
+    for k in (1, 3, 5, 10):
+        got = O.topk_gap(qbar, kbar, k)
+        for a in range(qbar.shape[0]):
+            sc = sorted((int(np.dot(qbar[a], kbar[b])) for b in range(kbar.shape[0])), reverse=True)
+            hi, lo = sc[k - 1], sc[k]
+            den = max(abs(hi), abs(lo))
+            ref = Fraction(hi - lo, den) if den else Fraction(0)
+            assert got[a] == float(ref), (k, a, got[a], ref)

@@ -50,6 +50,24 @@ def _topk_high_ties(qbar, kbar, k):    # equal scores resolved toward the higher
     return np.sort(nb - 1 - np.argsort(-S, axis=1, kind="stable")[:, :k], axis=1)
 
 
+def _topk_gap_next_ranks(qbar, kbar, k):   # compares ranks k+1 and k+2 (off by one)
+    S = so.block_scores(qbar, kbar)
+    if k + 1 >= S.shape[1]:
+        return np.full(S.shape[0], np.inf)
+    srt = -np.sort(-S, axis=1)
+    a, b = srt[:, k], srt[:, k + 1]
+    return (a - b) / np.maximum(np.maximum(np.abs(a), np.abs(b)), np.finfo(np.float64).tiny)
+
+
+def _topk_gap_min_scale(qbar, kbar, k):     # divides by the smaller magnitude
+    S = so.block_scores(qbar, kbar)
+    if k >= S.shape[1]:
+        return np.full(S.shape[0], np.inf)
+    srt = -np.sort(-S, axis=1)
+    a, b = srt[:, k - 1], srt[:, k]
+    return (a - b) / np.maximum(np.minimum(np.abs(a), np.abs(b)), np.finfo(np.float64).tiny)
+
+
 def _means_tail_by_bs(xw, bs):         # short last block divided by the full size
     N, d = xw.shape
     nb = -(-N // bs)
@@ -182,6 +200,9 @@ CASES = [
     ("topk_blocks", _topk_smallest, lambda: TA.test_topk_matches_brute_force(13, 5)),
     ("topk_blocks", _topk_high_ties, TA.test_topk_ties_prefer_lower_index_and_planted_block),
     ("block_means", _means_tail_by_bs, TA.test_block_means_even_and_tail),
+    ("topk_gap", _topk_gap_next_ranks, TA.test_topk_gap_finite_values),
+    ("topk_gap", _topk_gap_next_ranks, TA.test_topk_gap_matches_exact_rational_brute_force),
+    ("topk_gap", _topk_gap_min_scale, TA.test_topk_gap_finite_values),
     ("linear_apply", _linear_apply_no_relu, TL.test_linear_closed_form_equals_quadratic_expansion),
     ("linear_state", _linear_state_relu_v, TL.test_linear_closed_form_equals_quadratic_expansion),
     ("rope_3d", lambda x, F, Hg, Wg, dims=(44, 42, 42), base=10000.0: _rot(x, F, Hg, Wg, dims, base, -1.0),
