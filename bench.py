@@ -13,8 +13,10 @@ Also reported:
   roofline      the sparse-attention kernel's own launch time, read from
                 HIP events the library records on its stream during the
                 timed steps, against the bf16 dense MFMA peak;
-  cpu_baseline  the fp64 oracle on a bounded sample of the same layer on
-                this host's cores, extrapolated to the whole layer.
+  cpu_baseline  the fp64 oracle on whole heads of the same layer on this
+                host's cores (one head per head kind, scaled to the layer);
+  workloads     the other full-size workloads (480p Top-K, 720p window, CFG
+                pair with RoPE) timed the same way in the same run.
 """
 
 from __future__ import annotations
@@ -63,58 +65,67 @@ def source_sha() -> str:
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def cpu_baseline(w, inp, flops_total: float, target_s: float = 15.0, proj: str = "head"):
-    """Time the fp64 oracle on a bounded sample of the layer and extrapolate.
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    The oracle computes each head's per-layer work (RoPE, working order,
-    linear state, Top-K selection) once per call, on first use, and then
-    one output row at a time.  A call with one row per (sample, head) pays
-    all of the per-layer work; further calls add random rows on top, and the
-    difference gives the per-row cost.  With the full-width projection a
-    unit is a whole token row (all heads), so rows are drawn per token."""
+
+def cpu_baseline(w, inp, flops_total: float, full: bool = False):
+    """Time the fp64 oracle on whole heads of the layer on this host's cores.
+
+    One whole (sample, head) per head kind present (every one of its N
+    output rows, its linear state and, for Top-K heads, its selection),
+    each run by oracle.parallel over one single-threaded process per core;
+    the layer time is the sum over all heads of the time of a head of the
+    same kind (the heads of one kind cost the same).  With full=True every
+    head of every sample is run and nothing is extrapolated."""
     import numpy as np
-    import threadpoolctl
 
     import oracle as O
+    from oracle.parallel import whole_head, workers
     from sparse_linear_hybrid_st_amd import inputs as I
 
-    args = [I.as_f64(inp[n]) for n in ("q", "k", "v", "x", "w_p", "gate_w")]
-    kw = dict(grid=w.grid, head_kinds=w.head_kinds, window_radius=w.window_radius,
-              block=w.block, topk=w.topk, io_dtype=w.io_dtype, rope=w.rope,
-              rope_dims=w.rope_dims, rope_base=w.rope_base, proj=proj)
-    heads = 1 if proj == "full" else w.n_heads     # output units per token
-    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
-        if threadpoolctl.threadpool_info() else 1
-    rng = np.random.default_rng(0)
-    base_rows = [(b, int(rng.integers(w.N)), h) for b in range(w.batch) for h in range(heads)]
+    args = [inp[n].float().numpy() for n in ("q", "k", "v", "x")] + \
+        [I.as_f64(inp[n]) for n in ("w_p", "gate_w")]
+    procs = workers()
     t0 = time.perf_counter()
-    O.attn_forward(*args, inp["gate_b"], rows=base_rows, **kw)
-    t_fixed = time.perf_counter() - t0
-    total_rows = w.batch * w.N * heads
-    n_rows, t_rows = min(64, total_rows), 0.0
-    spent = t_fixed
-    while True:              # double the sample until one call takes half of target_s
-        rows = base_rows + [(int(rng.integers(w.batch)), int(rng.integers(w.N)),
-                             int(rng.integers(heads))) for _ in range(n_rows)]
+    s_ref = [O.gate(args[3][b], args[5], inp["gate_b"]) for b in range(w.batch)]
+    t_gate = time.perf_counter() - t0
+    units = [(b, h) for b in range(w.batch) for h in range(w.n_heads)]
+    if not full:
+        first = {}
+        for (b, h) in units:
+            first.setdefault(int(w.head_kinds[h]), (b, h))
+        run = sorted(first.values())
+    else:
+        run = units
+    t_kind = {}
+    spent = t_gate
+    for (b, h) in run:
         t0 = time.perf_counter()
-        O.attn_forward(*args, inp["gate_b"], rows=rows, **kw)
+        whole_head(w, args, s_ref[b], b, h, procs)
         dt = time.perf_counter() - t0
         spent += dt
-        t_rows = max(dt - t_fixed, 1e-9)
-        if dt >= target_s / 2 or n_rows >= total_rows:
-            break
-        n_rows = min(2 * n_rows, total_rows)
-    per_row = t_rows / n_rows
-    t_layer = t_fixed + per_row * (total_rows - len(base_rows))
+        t_kind.setdefault(int(w.head_kinds[h]), []).append(dt)
+    if full:
+        t_layer = spent
+    else:
+        t_layer = t_gate + sum(np.mean(t_kind[int(w.head_kinds[h])]) for (b, h) in units)
+    kinds = ", ".join(f"{'spatial temporal Top-K'.split()[k]} head {np.mean(v):.1f} s"
+                      for k, v in sorted(t_kind.items()))
     return {
-        "value": flops_total / t_layer / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-        "kind": "oracle", "ms_per_layer_extrapolated": t_layer * 1e3, "cpu_seconds_spent": spent,
-        "sample": (f"fp64 numpy oracle ({proj} projection): one output row per (sample, head), "
-                   f"which includes every "
-                   f"head's per-layer work (gate, RoPE, working order, linear state, Top-K "
-                   f"selection), in {t_fixed:.2f} s; then {n_rows} more random rows (sparse "
-                   f"attention, linear apply, combine) in {t_rows:.2f} s beyond that; "
-                   f"extrapolated to all {total_rows} " + ("token rows" if proj == "full" else "rows")),
+        "value": flops_total / t_layer / 1e12, "unit": "TFLOP/s", "cores": int(procs),
+        "kind": "oracle", "ms_per_layer": t_layer * 1e3, "cpu_seconds_spent": spent,
+        "extrapolated": not full, "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
+        "sample": ("the whole layer: every head of every sample, all rows" if full else
+                   f"one whole head per head kind ({kinds}; every output row, the head's linear state "
+                   f"and selection), scaled to the layer's {len(units)} (sample, head) pairs")
+                  + f", fp64 numpy oracle on {procs} single-threaded processes",
     }
 
 
@@ -247,6 +258,57 @@ def stages_bench(args, w, inp, p):
     return 0
 
 
+def measure_forward(w, steps: int, warmup: int) -> dict:
+    """One full-size forward workload in this process: inputs resident, one
+    forward, warm-up, then ``steps`` timed layer calls (wall clock around
+    them, and the library's HIP events around the attention kernel)."""
+    import torch
+
+    import sparse_linear_hybrid_st_amd as S
+    from sparse_linear_hybrid_st_amd import inputs as I
+
+    t0 = time.perf_counter()
+    inp = I.make_inputs(w)
+    p = S.problem_from_workload(w)
+    dev = {n: inp[n].cuda() for n in ("q", "k", "v", "x", "w_p", "gate_w")}
+    del inp
+    out = torch.empty_like(dev["q"])
+    s_out = torch.empty(w.batch, dtype=torch.float32, device="cuda")
+    idx = torch.zeros((w.batch, w.n_heads, p.n_blocks, w.topk), dtype=torch.int32, device="cuda")
+    ws = S.workspace(p)
+    print(f"[bench] {w.name}: inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    def fwd(events=None):
+        S.salad_attn_forward(p, dev["q"], dev["k"], dev["v"], dev["x"], dev["w_p"], dev["gate_w"], 0.0,
+                             out, ws, s_out=s_out, idx_out=idx, events=events)
+
+    fwd()
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    pairs = pair_count(w)
+    if 2 in w.head_kinds:
+        pairs += topk_pairs_from_idx(w, idx.cpu().numpy())
+    flops = 4.0 * w.head_dim * pairs
+    events = S.HipEvents(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fwd(events=events.pairs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    attn = events.elapsed_ms(steps)
+    events.close()
+    attn_ms = sum(attn) / len(attn)
+    del dev, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "description": w.description, "ms_per_layer": ms,
+            "effective_tflops": flops / (ms * 1e-3) / 1e12, "computed_pairs": pairs,
+            "attention_kernel_ms": attn_ms,
+            "attention_frac_of_mfma_peak": flops / (attn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "steps": steps, "warmup": warmup}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,7 +316,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="480p-stswa-h12")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="CPU baseline over every head of the layer (minutes) instead of one whole "
+                         "head per head kind")
     ap.add_argument("--branch-drop-tau", type=float, default=0.0,
                     help="post-tuning branch dropping threshold (samples whose gate value is "
                          "below it keep only the sparse branch); 0 never drops")
@@ -278,6 +342,9 @@ def main():
                     help="forward only: after the timed steps, this many more layer calls, each after "
                          "writing a 512 MiB buffer (L2 and MALL flushed), timed one by one; median and "
                          "min reported as cold_cache (0: skip)")
+    ap.add_argument("--workloads", default="480p-topk-h40,720p-stswa-h40,480p-cfg-rope-mixed-h40",
+                    help="plain forward runs only: the other full-size workloads timed after the "
+                         "headline one in the same run (comma-separated names; 'none' to skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size reference for the HBM byte counters)")
@@ -466,7 +533,13 @@ def main():
         rec["cpu_baseline"] = None  # the oracle's backward is timed in the test suite, not here
     elif not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, inp, flops, args.cpu_seconds, args.proj)
+        rec["cpu_baseline"] = cpu_baseline(w, inp, flops, args.cpu_full) if args.proj == "head" else None
+    if (not args.backward and args.proj == "head" and args.branch_drop_tau == 0.0
+            and args.workloads != "none"):
+        names = [n for n in args.workloads.split(",") if n and n != w.name]
+        del dev, out, ws
+        torch.cuda.empty_cache()
+        rec["workloads"] = [measure_forward(C.all_workloads()[n], args.steps, args.warmup) for n in names]
     print(json.dumps(rec), flush=True)
 
 

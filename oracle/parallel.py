@@ -1,5 +1,10 @@
 """Whole heads of the oracle's layer output at full size, on several CPU
-processes (not a test module).
+processes.
+
+TEST INFRASTRUCTURE ONLY, like the rest of this package: used by the
+full-size parity tests and by bench.py's CPU baseline.  It adds no
+arithmetic: it only splits the rows of one head into chunks and runs the
+oracle's own ``attn_forward`` on each chunk.
 
 The oracle computes output rows one at a time; one head of a 31,200-token
 layer is about forty seconds of that on one core.  Here the rows of one
@@ -19,7 +24,7 @@ import tempfile
 
 import numpy as np
 
-import oracle as O
+from . import salad_oracle as O
 
 
 def _chunk(args):

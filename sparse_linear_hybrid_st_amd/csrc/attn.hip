@@ -160,12 +160,10 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   // this wave's queries as MFMA B operands: lane -> query q0 + 32w + l32,
   // features 16ks + 8hl + e
   const int pq = q0 + 32 * w + l32;
+  const long long q_off = row_offset(g, a.q, b, h, min(pq, g.N - 1));
   bf16x8 qf[8];
-  {
-    const long long off = row_offset(g, a.q, b, h, min(pq, g.N - 1));
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8 *)(qbase + off + (2 * ks + hl) * 8);
-  }
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8 *)(qbase + q_off + (2 * ks + hl) * 8);
 
   int n_tiles, kt_first = 0;
   const int32_t *sel = nullptr;
@@ -270,10 +268,11 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;  // running offset (raw score units), partial row sum
-  float m_off = 0.f;                       // m_run * c2 (0 while m_run is -inf)
-  const float thr_gap = 8.f / c2;          // raise the offset past m_run + thr_gap
-  float m_thr = -INFINITY;                 // m_run + thr_gap
+  // Running offset m_off (log2 units) of this lane's query: probabilities are
+  // exp2(c2 * s - m_off).  l_run: this lane's partial row sum.  m_set: an
+  // offset has been taken from a real score (until then no key has counted).
+  float m_off = 0.f, l_run = 0.f;
+  bool m_set = false;
 
   // One key tile: S^T = K Q^T (qk), online softmax (softmax), O^T += V^T
   // P^T (pv).  classify tells whether the tile holds any key of this wave's
@@ -291,7 +290,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
       full = (k0 + kBN <= g.N) && (k0 >= wq_hi - g.r) && (k0 + kBN - 1 <= wq_lo + g.r);
     }
   };
-  // S^T[key][query] = K Q^T, two blocks of 32 keys
+  // S^T[key][query] = K Q^T, two blocks of 32 keys (raw scores: products of
+  // the stored values, accumulated in fp32)
   auto qk = [&](const bf16_t *__restrict__ Ks, f32x16 (&s)[2]) {
     s[0] = f32x16{};
     s[1] = f32x16{};
@@ -306,22 +306,47 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_32x32x16(ka[u][kb], qf[ks + u], s[kb]);
+        for (int kb = 0; kb < 2; ++kb)
+          s[kb] = mfma_32x32x16(ka[u][kb], qf[ks + u], s[kb]);
     }
   };
   // Softmax of one tile, in place.  Edge tiles mask first: key j is kept
   // iff j < N and, for window heads, |pq - j| <= r, i.e. the unsigned value
   // pq - j + r is at most 2r (one subtract and one compare per score).
-  // The running offset m_run only has to bound the row's scores loosely: O
-  // and l share it, so the final O / l is exact whatever its value.  It is
-  // raised (and O, l rescaled) only when a score exceeds it by more than 8
-  // in log2 units, so probabilities stay below 2^8 (no overflow in fp32
-  // sums or in bf16).  Each lane tests its own 32 scores against that
-  // threshold; only when some lane of the wave crosses it is the row max
-  // combined across the two half-waves (which hold the other 32 keys of the
-  // same query), so both halves always share one offset.  The row sum l
-  // adds the bf16-rounded probabilities in pairs (v_dot2 with (1, 1)): the
-  // same values the PV product weighs V with.
+  // The offset m_off only has to bound the row's scores loosely: O and l
+  // share it, so the final O / l is exact whatever its value.  Each lane
+  // exponentiates its 32 scores under the current offset (one FMA and one
+  // exp2 per score: the scores stay exact products), packs them to bf16
+  // and sums the packed values (v_dot2 with (1, 1): the same values the PV
+  // product weighs V with).  A lane whose tile sum exceeds 2^8 may hold a
+  // probability above 2^8 (every term is at most the sum); only then, or
+  // while no offset has been taken, is the tile's true maximum formed,
+  // combined with the other half-wave (which holds the other 32 keys of the
+  // same query, so both halves keep one offset), the offset raised to it, O
+  // and l rescaled and the tile's probabilities recomputed.  So probabilities
+  // stay below 2^8 (no overflow in fp32 sums or in bf16), and an ordinary
+  // tile costs one exp2, half a pack and half a dot2 per score.
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto exp_pack = [&](const f32x16 (&s)[2], float shift, bf16x8 (&pb)[4]) -> float {
+    float lt = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          // v_exp_f32 directly: tiny results flush to 0; large ones (even inf)
+          // are caught by the tile-sum test below and recomputed
+          pv[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e], c2, -shift));
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          lt = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, lt, false);
+        pb[2 * kb + half] = pv;
+      }
+    return lt;
+  };
   auto softmax = [&](int k0, bool full, f32x16 (&s)[2], bf16x8 (&pb)[4]) {
     if (!full) {
       int jl = k0 + 4 * hl;                              // j = jl + c below
@@ -341,42 +366,38 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
           s[kb][r] = keep ? s[kb][r] : -INFINITY;
         }
     }
-    float mx = s[0][0];
+    float lt = exp_pack(s, m_off, pb);
+    const bool need = !(lt <= 256.f) || !m_set;
+    if (__any(need)) {
+      float mx = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    if (__any(mx > m_thr)) {
-      const unsigned um = __float_as_uint(mx);
-      const auto sw = __builtin_amdgcn_permlane32_swap(um, um, false, false);
-      const float mxa = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const float m_new = fmaxf(m_run, mxa);
-      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-      l_run *= alpha;
+        for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaf(mx, c2, -m_off);  // relative to the current offset (c2 > 0)
+      // both half-waves of a query column agree on the maximum and on
+      // whether to move the offset
+      // (the swap of x with itself gives lanes 0-31's x in [0] and lanes
+      // 32-63's in [1], on every lane)
+      const unsigned um = __float_as_uint(mx), un = need ? 1u : 0u;
+      const auto sm = __builtin_amdgcn_permlane32_swap(um, um, false, false);
+      const auto sn = __builtin_amdgcn_permlane32_swap(un, un, false, false);
+      const float mxa = fmaxf(__uint_as_float(sm[0]), __uint_as_float(sm[1]));
+      const bool need_q = (sn[0] | sn[1]) != 0u;
+      const float delta = (need_q && mxa != -INFINITY) ? mxa : 0.f;
+      if (delta != 0.f) {
+        const float alpha = m_set ? __builtin_amdgcn_exp2f(-delta) : 1.f;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_run = m_new;
-      m_off = m_run == -INFINITY ? 0.f : m_run * c2;
-      m_thr = m_run + thr_gap;
-    }
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          // v_exp_f32 directly: arguments are <= 8, tiny results flush to 0
-          pv[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e], c2, -m_off));
-#pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, l_run, false);
-        pb[2 * kb + half] = pv;
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m_off += delta;
       }
+      m_set = m_set || (mxa != -INFINITY);
+      if (__any(delta != 0.f)) lt = exp_pack(s, m_off, pb);
+    }
+    l_run += lt;
   };
   auto pv = [&](const bf16_t *__restrict__ Vs, const bf16x8 (&pb)[4]) {
     // O^T[d][q] += V^T[d][keys] P^T[keys][q].  k-step kk, half hl, element

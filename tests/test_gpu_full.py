@@ -17,7 +17,7 @@ from sparse_linear_hybrid_st_amd import configs as C
 from sparse_linear_hybrid_st_amd import inputs as I
 from tests.gpu_util import (assert_close, check_selection, host64, oracle_kwargs, rel_fro,
                             run_forward)
-from tests.oracle_pool import whole_head, workers
+from oracle.parallel import whole_head, workers
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(600)]
 
