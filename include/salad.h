@@ -160,6 +160,20 @@ salad_status salad_linear_state(const salad_problem *p, const void *kw, const vo
                                 float *h, float *z, void *ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* salad_linear_state without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops and harnesses
+ * that forbid allocation): identical arguments and results, except that the
+ * split-N partial states live in a fixed 36 MiB device array inside the
+ * library (one per GPU, kept until the process ends) instead of ws.  It
+ * allocates nothing.  Problems whose partial states need more than 36 MiB
+ * (B*H above about 570 at d = 128) are rejected with SALAD_ERR_WORKSPACE.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * device (other streams or threads) race and must be serialised by the
+ * caller.  The first call on a device looks the array's address up
+ * (SALAD_ERR_HIP if that fails).  Errors otherwise as salad_linear_state. */
+salad_status salad_linear_state_noalloc(const salad_problem *p, const void *kw, const void *vw,
+                                        float *h, float *z, hipStream_t stream);
+
 /* Linear-attention output ([S] Prerequisites > Linear Attention):
  * o_l[b,h,p,:] = relu(q_p)^T H / (relu(q_p) . Z + linear_eps), working layout,
  * float32 out. */

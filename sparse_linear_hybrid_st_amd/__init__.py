@@ -32,7 +32,8 @@ EXPORTS = ("salad_workspace_size", "salad_permute", "salad_block_select", "salad
            "salad_linear_state", "salad_linear_apply", "salad_gate", "salad_combine",
            "salad_attn_forward", "salad_output_projection", "salad_backward_workspace_size",
            "salad_attn_backward", "salad_calibrate_workspace_size", "salad_window_calibrate",
-           "salad_attn_forward_timed", "salad_attn_backward_timed", "salad_last_error")
+           "salad_attn_forward_timed", "salad_attn_backward_timed", "salad_linear_state_noalloc",
+           "salad_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -94,6 +95,7 @@ def lib() -> ctypes.CDLL:
             "salad_block_select": [P, vp, vp, vp, vp, vp, vp, sz, vp],
             "salad_sparse_attn": [P, vp, vp, vp, vp, vp, vp],
             "salad_linear_state": [P, vp, vp, vp, vp, vp, sz, vp],
+            "salad_linear_state_noalloc": [P, vp, vp, vp, vp, vp],
             "salad_linear_apply": [P, vp, vp, vp, vp, vp],
             "salad_gate": [P, vp, vp, f32, vp, vp, sz, vp],
             "salad_combine": [P, vp, vp, vp, vp, vp, vp],
@@ -234,6 +236,19 @@ def salad_linear_state(p: Problem, kw, vw, h, z, ws, stream=None):
         ctypes.byref(p), _ptr(kw, "kw", n, dt), _ptr(vw, "vw", n, dt),
         _ptr(h, "h", bh * p.head_dim ** 2, torch.float32), _ptr(z, "z", bh * p.head_dim, torch.float32),
         _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def salad_linear_state_noalloc(p: Problem, kw, vw, h, z, stream=None):
+    """salad_linear_state with the library's own fixed device scratch (no
+    workspace; allocates nothing)."""
+    import torch
+    n, _ = _sizes(p)
+    dt = _io_dtype(p)
+    bh = p.batch * p.n_heads
+    _check(lib().salad_linear_state_noalloc(
+        ctypes.byref(p), _ptr(kw, "kw", n, dt), _ptr(vw, "vw", n, dt),
+        _ptr(h, "h", bh * p.head_dim ** 2, torch.float32), _ptr(z, "z", bh * p.head_dim, torch.float32),
+        _stream(stream)))
 
 
 def salad_linear_apply(p: Problem, qw, h, z, o_l, stream=None):

@@ -329,6 +329,29 @@ salad_status salad_linear_state(const salad_problem *p, const void *kw, const vo
                     "salad_linear_state");
 }
 
+salad_status salad_linear_state_noalloc(const salad_problem *p, const void *kw, const void *vw, float *h,
+                                        float *z, hipStream_t stream) {
+  Info inf;
+  CHECK(validate(p, &inf));
+  CHECK(need(kw, "kw"));
+  CHECK(need(vw, "vw"));
+  CHECK(need(h, "h"));
+  CHECK(need(z, "z"));
+  const Geom &g = inf.g;
+  const size_t needed = up(size_t(g.B) * g.H * linear_splits(g) * (size_t(g.D) * g.D + g.D) * sizeof(float));
+  if (needed > noalloc_scratch_bytes())
+    return fail(SALAD_ERR_WORKSPACE,
+                "salad_linear_state_noalloc: the split-N partial states need %zu bytes, more than the "
+                "library's fixed %zu-byte device scratch (use salad_linear_state with a workspace)",
+                needed, noalloc_scratch_bytes());
+  void *scratch = nullptr;
+  hipError_t e = noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "salad_linear_state_noalloc: scratch address");
+  return hip_status(launch_linear_state(g, inf.bf16, working_view(g, kw), working_view(g, vw),
+                                        (float *)scratch, h, z, stream),
+                    "salad_linear_state_noalloc");
+}
+
 salad_status salad_linear_apply(const salad_problem *p, const void *qw, const float *h, const float *z,
                                 float *o_l, hipStream_t stream) {
   Info inf;

@@ -17,6 +17,12 @@ inline size_t select_ws_bytes(const Geom &g) {
          ((BH * g.nb * g.nb * sizeof(double) + 255) & ~size_t(255));
 }
 
+// File-scope device scratch of salad_linear_state_noalloc (noalloc.hip):
+// this device's address of it (looked up on first use per device) and its
+// fixed size in bytes.
+hipError_t noalloc_scratch(void **out);
+size_t noalloc_scratch_bytes();
+
 // Token chunks per (b, h) used by the split-N linear-state reduction.
 inline int linear_splits(const Geom &g) {
   // at most 512 workgroups (two per CU at the state kernel's register use),
