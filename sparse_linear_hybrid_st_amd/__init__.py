@@ -18,7 +18,9 @@ import math
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsalad.so")
+# SALAD_LIB: another build of the same library (the sanitizer test's
+# host-instrumented build); by default the in-tree libsalad.so.
+LIB_PATH = os.environ.get("SALAD_LIB") or os.path.join(HERE, "libsalad.so")
 
 SALAD_F32, SALAD_BF16 = 0, 1
 HEAD_SPATIAL, HEAD_TEMPORAL, HEAD_TOPK = 0, 1, 2

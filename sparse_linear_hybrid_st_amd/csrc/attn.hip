@@ -8,16 +8,19 @@
 // blocks).  Window reading: keep key j for query p iff |p - j| <= r.
 //
 // bf16 path (d = 128): flash-style on v_mfma_f32_32x32x16_bf16.
-//   * A workgroup owns a query tile (128 queries for window heads, one
-//     64-query block for Top-K heads); each wave owns 32 queries and keeps
-//     them in registers as MFMA B operands.
-//   * Key tiles of 64 rows are staged in LDS: K row-major (XOR-swizzled
-//     16-byte units), V transposed to [d][key] (swizzled 8-byte granules) so
-//     that both MFMA operand reads are contiguous.  The next tile's global
-//     loads are issued before the current tile's MFMAs.
+//   * A workgroup of four waves owns a query tile: 128 queries of a window
+//     head (each wave 32 queries over every key), or one 64-query block of
+//     a Top-K head (two query groups of 32 times the two 32-key halves of
+//     every key tile; the halves are merged after the last tile).  A wave
+//     keeps its queries in registers as MFMA B operands.
+//   * Key tiles of 64 rows are staged in LDS, double-buffered (two
+//     workgroups per CU): K row-major (XOR-swizzled 16-byte units), read
+//     transposed for V, so that both MFMA operand reads are contiguous.
+//     The next tile's DMA is issued before the current tile's MFMAs.
 //   * S^T = K Q^T puts one query per lane column, so the online softmax
-//     (max, exp2, running sum) is lane-local except for one exchange between
-//     the two half-waves; P^T then feeds O^T += V^T P^T directly from
+//     (exp2, running sum, and the rare offset update) is lane-local except
+//     for one exchange between the two half-waves; P^T then feeds
+//     O^T += V^T P^T directly from
 //     registers (the key order inside an MFMA k-step is free, so P needs no
 //     shuffle).
 //   * Window heads skip key tiles outside the window, and tiles that lie
@@ -114,30 +117,37 @@ struct AttnArgs {
 // epilogue (linear branch, projection, gate, scatter to token order).
 // MODE 2: backward preparation -- per row, the log2-domain normaliser
 // lse2 (P = exp2(scale*log2(e)*s - lse2)) and D = dO . O_s.
-template <int NW, int MODE>
-__global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
+// TOPK: the heads of this launch are Top-K heads.  Key-split workgroups
+// (Top-K heads): 64 queries, four waves as two query groups of 32 (qg) times
+// the two 32-key halves of every key tile (kg); the halves of a query group
+// are merged after the last tile.  Otherwise (window heads): 128 queries,
+// wave w the query group w over every key of each tile.
+template <int MODE, bool TOPK>
+__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   constexpr bool FUSED = MODE == 1;
-  constexpr int BM = NW * 32;
+  constexpr bool KS = TOPK;
+  constexpr int NW = 4;                          // waves per workgroup
+  constexpr int BM = KS ? 64 : 128;              // queries per workgroup
+  constexpr int NKB = KS ? 1 : 2;                // 32-key blocks of a tile per wave
   constexpr int TILE = kBN * kD;                 // elements per K or V tile
   constexpr int DMA_PER_WAVE = (TILE * 2 / 1024) / NW;  // 1-KB DMA ops per tensor per wave
   // Two named buffers per tensor (not one indexed array): with distinct LDS
   // objects the compiler can tell that the DMA into one buffer does not
   // feed the reads of the other, so it does not wait for the next tile's
-  // DMA before computing on the current one.
-  // Top-K workgroups (2 waves) use one buffer: 32 KB of LDS lets four of
-  // them share a CU (2 waves per SIMD), and the other workgroups cover each
-  // one's DMA wait; window workgroups (4 waves) double-buffer.
-  constexpr bool SINGLE = (NW == 2);
-  constexpr bool TOPK = (NW == 2);  // the launcher runs Top-K heads with 2 waves, window heads with 4
+  // DMA before computing on the current one.  64 KB per workgroup: two
+  // workgroups (eight waves) share a CU.
   __shared__ __attribute__((aligned(1024))) bf16_t K0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16_t K1[SINGLE ? 8 : TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t K1[TILE];
   __shared__ __attribute__((aligned(1024))) bf16_t V0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16_t V1[SINGLE ? 8 : TILE];
+  __shared__ __attribute__((aligned(1024))) bf16_t V1[TILE];
   const Geom &g = a.g;
   // the wave index is uniform per wave; readfirstlane lets the compiler use
   // it as a scalar (the DMA destination in M0 must be wave-uniform)
   const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int qg = KS ? (w & 1) : w;   // query group of 32
+  const int kg = KS ? (w >> 1) : 0;  // key half of each tile (key-split)
+  const int kb0 = KS ? kg : 0;       // first 32-key block of a tile this wave takes
 
   const int tile = xcd_order(blockIdx.x, a.n_blocks);
   const int qt = tile % a.tiles_per_head;
@@ -157,9 +167,9 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   const long long kv_sB = from_work ? a.k.sB : a.kd.sB;
   const long long kv_sH = from_work ? a.k.sH : a.kd.sH;
 
-  // this wave's queries as MFMA B operands: lane -> query q0 + 32w + l32,
+  // this wave's queries as MFMA B operands: lane -> query q0 + 32qg + l32,
   // features 16ks + 8hl + e
-  const int pq = q0 + 32 * w + l32;
+  const int pq = q0 + 32 * qg + l32;
   const long long q_off = row_offset(g, a.q, b, h, min(pq, g.N - 1));
   bf16x8 qf[8];
 #pragma unroll
@@ -176,7 +186,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     kt_first = lo / kBN;
     n_tiles = hi / kBN - kt_first + 1;
   }
-  const int wq_lo = q0 + 32 * w, wq_hi = min(q0 + 32 * w + 31, g.N - 1);
+  const int wq_lo = q0 + 32 * qg, wq_hi = min(q0 + 32 * qg + 31, g.N - 1);
 
   // First key row of tile `it`.  An out-of-range block index (only possible
   // if idx was not produced by the selection) maps past the end, where every
@@ -217,19 +227,6 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     dma_row[i] = 4 * (i * NW + w) + (lane >> 4);
     dma_off[i] = 2 * (dma_row[i] * sN + (((lane & 15) ^ kv_swz(dma_row[i])) << 3));
   }
-  // one tensor's DMA of the tile starting at key k0 into buffer Dd
-  // one tensor's DMA of the tile starting at key k0 into buffer Dd
-  auto issue_one = [&](const __amdgpu_buffer_rsrc_t &rs, int k0, bf16_t *__restrict__ Dd) {
-    const bool tail = k0 + kBN > g.N;
-    const unsigned soff = unsigned(k0) * unsigned(sN) * 2u;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      int off = dma_off[i];
-      if (tail) off -= 2 * (k0 + dma_row[i] - min(k0 + dma_row[i], g.N - 1)) * sN;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(Dd + (4 * (i * NW + w)) * kD), 16,
-                                               unsigned(off), soff, 0, 0);
-    }
-  };
   auto issue_tile = [&](int k0, bf16_t *__restrict__ Kd, bf16_t *__restrict__ Vd) {
     const bool tail = k0 + kBN > g.N;
     const unsigned soff = unsigned(k0) * unsigned(sN) * 2u;
@@ -275,38 +272,40 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   bool m_set = false;
 
   // One key tile: S^T = K Q^T (qk), online softmax (softmax), O^T += V^T
-  // P^T (pv).  classify tells whether the tile holds any key of this wave's
-  // queries and whether it needs no mask.  The phases are separate so the
-  // single-buffered loop can free the K buffer right after qk; each takes
+  // P^T (pv), over this wave's NKB blocks of 32 keys of the tile (blocks
+  // kb0 .. kb0 + NKB - 1).  classify tells whether those keys hold any key
+  // of this wave's queries and whether they need no mask.  Each phase takes
   // its LDS buffer as a restrict parameter, which lets the compiler tell its
   // reads apart from DMAs into the other buffers.
   auto classify = [&](int k0, bool &any, bool &full) {
-    const int k1 = min(k0 + kBN, g.N) - 1;
+    const int ku = k0 + 32 * kb0;                  // first key of this wave's part
+    const int ke = ku + 32 * NKB;                  // one past its last
+    const int k1 = min(ke, g.N) - 1;
     if (TOPK) {
-      any = k0 < g.N;
-      full = (k0 + kBN) <= g.N;
+      any = ku < g.N;
+      full = ke <= g.N;
     } else {
-      any = (k0 <= wq_hi + g.r) && (k1 >= wq_lo - g.r) && (wq_lo <= wq_hi);
-      full = (k0 + kBN <= g.N) && (k0 >= wq_hi - g.r) && (k0 + kBN - 1 <= wq_lo + g.r);
+      any = (ku <= wq_hi + g.r) && (k1 >= wq_lo - g.r) && (wq_lo <= wq_hi);
+      full = (ke <= g.N) && (ku >= wq_hi - g.r) && (ke - 1 <= wq_lo + g.r);
     }
   };
-  // S^T[key][query] = K Q^T, two blocks of 32 keys (raw scores: products of
+  // S^T[key][query] = K Q^T per block of 32 keys (raw scores: products of
   // the stored values, accumulated in fp32)
-  auto qk = [&](const bf16_t *__restrict__ Ks, f32x16 (&s)[2]) {
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+  auto qk = [&](const bf16_t *__restrict__ Ks, f32x16 (&s)[NKB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ks += 2) {
-      bf16x8 ka[2][2];
+      bf16x8 ka[2][NKB];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          ka[u][kb] = *(const bf16x8 *)(Ks + kb * 32 * kD + k_lane + 16 * ((ks + u) ^ k_x));
+        for (int kb = 0; kb < NKB; ++kb)
+          ka[u][kb] = *(const bf16x8 *)(Ks + (kb0 + kb) * 32 * kD + k_lane + 16 * ((ks + u) ^ k_x));
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
           s[kb] = mfma_32x32x16(ka[u][kb], qf[ks + u], s[kb]);
     }
   };
@@ -315,23 +314,23 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   // pq - j + r is at most 2r (one subtract and one compare per score).
   // The offset m_off only has to bound the row's scores loosely: O and l
   // share it, so the final O / l is exact whatever its value.  Each lane
-  // exponentiates its 32 scores under the current offset (one FMA and one
+  // exponentiates its scores under the current offset (one FMA and one
   // exp2 per score: the scores stay exact products), packs them to bf16
   // and sums the packed values (v_dot2 with (1, 1): the same values the PV
   // product weighs V with).  A lane whose tile sum exceeds 2^8 may hold a
   // probability above 2^8 (every term is at most the sum); only then, or
   // while no offset has been taken, is the tile's true maximum formed,
-  // combined with the other half-wave (which holds the other 32 keys of the
+  // combined with the other half-wave (which holds the other keys of the
   // same query, so both halves keep one offset), the offset raised to it, O
   // and l rescaled and the tile's probabilities recomputed.  So probabilities
   // stay below 2^8 (no overflow in fp32 sums or in bf16), and an ordinary
   // tile costs one exp2, half a pack and half a dot2 per score.
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  auto exp_pack = [&](const f32x16 (&s)[2], float shift, bf16x8 (&pb)[4]) -> float {
+  auto exp_pack = [&](const f32x16 (&s)[NKB], float shift, bf16x8 (&pb)[2 * NKB]) -> float {
     float lt = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         bf16x8 pv;
@@ -347,7 +346,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
       }
     return lt;
   };
-  auto softmax = [&](int k0, bool full, f32x16 (&s)[2], bf16x8 (&pb)[4]) {
+  auto softmax = [&](int k0, bool full, f32x16 (&s)[NKB], bf16x8 (&pb)[2 * NKB]) {
     if (!full) {
       int jl = k0 + 4 * hl;                              // j = jl + c below
       // opaque to the optimiser: otherwise it carries the 32 per-score
@@ -357,10 +356,10 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
       const unsigned wb = unsigned(pq - jl + g.r);        // pq - j + r = wb - c
       const int lim = g.N - jl;                          // j < N  <=>  c < lim
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const int c = (kb0 + kb) * 32 + 8 * (r >> 2) + (r & 3);
           // bitwise, not short-circuit: keeps the mask a select, not a branch
           const bool keep = (c < lim) & (TOPK | (wb - unsigned(c) <= unsigned(2 * g.r)));
           s[kb][r] = keep ? s[kb][r] : -INFINITY;
@@ -371,7 +370,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     if (__any(need)) {
       float mx = s[0][0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = fmaf(mx, c2, -m_off);  // relative to the current offset (c2 > 0)
@@ -399,19 +398,21 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     }
     l_run += lt;
   };
-  auto pv = [&](const bf16_t *__restrict__ Vs, const bf16x8 (&pb)[4]) {
+  auto pv = [&](const bf16_t *__restrict__ Vs, const bf16x8 (&pb)[2 * NKB]) {
     // O^T[d][q] += V^T[d][keys] P^T[keys][q].  k-step kk, half hl, element
-    // e = 4r + e' covers key 32*(kk/2) + 8*(2*(kk%2) + r) + 4*hl + e'; the
+    // e = 4r + e' covers key 32*(kk/2) + 8*(2*(kk%2) + r) + 4*hl + e' of
+    // this wave's part of the tile (which starts at row 32*kb0); the
     // matching V^T operand comes from two transposing reads (r = 0, 1).
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2 * NKB; ++kk) {
       // all four d-blocks' operands of this k-step first, then the MFMAs
       typedef __attribute__((ext_vector_type(8))) short s16x8;
       s16x8 va[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Vs + 16 * kk * kD + v_off[0][db]));
-        const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Vs + 16 * kk * kD + v_off[1][db]));
+        const bf16_t *vk = Vs + 16 * (2 * kb0 + kk) * kD;
+        const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vk + v_off[0][db]));
+        const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vk + v_off[1][db]));
         va[db] = s16x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       }
 #pragma unroll
@@ -422,8 +423,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     bool any, full;
     classify(k0, any, full);
     if (!any) return;
-    f32x16 s[2];
-    bf16x8 pb[4];
+    f32x16 s[NKB];
+    bf16x8 pb[2 * NKB];
     qk(Ks, s);
     softmax(k0, full, s, pb);
     pv(Vs, pb);
@@ -435,47 +436,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   // last n issued have landed; a barrier after such a wait makes every
   // wave's share visible.
   int k_cur = n_tiles > 0 ? tile_start(0) : 0;
-  if constexpr (SINGLE) {
-    // One buffer per tensor, split phases: the K buffer is refilled with
-    // tile it+1 as soon as every wave has finished QK of tile it, and the V
-    // buffer once PV of tile it is done, so K(it+1) lands during softmax and
-    // PV of tile it.  (The compiler makes the K reads of QK wait for V(it)
-    // too, as it cannot tell the two buffers apart there; issuing the DMAs
-    // out of its sight to overlap V as well measured no faster.)  Issue
-    // order per wave: K(0) V(0) K(1) V(1) ...
-    // The barriers here are wg_barrier (no fence, so no wait for the DMAs
-    // in flight); DMA completion is handled by the explicit vmcnt waits.
-    constexpr int VM_ONE = DMA_PER_WAVE;  // DMA ops of one tensor per wave
-    static_assert(VM_ONE < 16, "vmcnt immediate below");
-    if (n_tiles > 0) {
-      issue_one(krs, k_cur, K0);
-      issue_one(vrs, k_cur, V0);
-    }
-    for (int it = 0; it < n_tiles; ++it) {
-      const bool more = it + 1 < n_tiles;
-      const int k_nxt = more ? tile_start(it + 1) : 0;
-      // Top-K tiles are never skipped: a block past the end (only from an
-      // invalid index) has every key masked and adds nothing
-      bool any, full;
-      classify(k_cur, any, full);
-      (void)any;
-      f32x16 s[2];
-      bf16x8 pb[4];
-      __builtin_amdgcn_s_waitcnt(0x0F70 | VM_ONE);  // K(it) landed, V(it) may be in flight
-      wg_barrier();
-      qk(K0, s);
-      wg_barrier();  // every wave is done reading K(it)
-      if (more) issue_one(krs, k_nxt, K0);
-      softmax(k_cur, full, s, pb);
-      if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | VM_ONE);  // V(it) landed, K(it+1) may not
-      else __builtin_amdgcn_s_waitcnt(0x0F70);
-      wg_barrier();
-      pv(V0, pb);
-      wg_barrier();  // every wave is done reading V(it)
-      if (more) issue_one(vrs, k_nxt, V0);
-      k_cur = k_nxt;
-    }
-  } else {
+  {
     // Double-buffered, unrolled by two so each half names its buffers
     // statically.  Before computing tile it: wait for this wave's DMA of
     // tile it (vmcnt 0), barrier (every wave's DMA landed and every wave is
@@ -497,16 +458,49 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     }
   }
 
+  if constexpr (KS) {
+    // Merge the key halves of each query group: the waves with kg = 1 hand
+    // their offset, partial sums and O to the kg = 0 wave of the same query
+    // group through LDS (the tile buffers are free now); O and l are scaled
+    // to the larger offset.  A half that saw no key (no offset) adds nothing.
+    __syncthreads();                       // every wave is done with the tile buffers
+    float *xo = (float *)(qg ? K1 : K0);  // [64 values][64 lanes]
+    float *xm = (float *)V0 + qg * 192;    // [3][64 lanes]
+    if (kg == 1) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = o[db][r];
+      xm[lane] = m_off;
+      xm[64 + lane] = l_run;
+      xm[128 + lane] = m_set ? 1.f : 0.f;
+    }
+    __syncthreads();
+    if (kg == 0 && xm[128 + lane] != 0.f) {
+      const float m_b = xm[lane], l_b = xm[64 + lane];
+      const float m_new = m_set ? fmaxf(m_off, m_b) : m_b;
+      const float a0 = m_set ? __builtin_amdgcn_exp2f(m_off - m_new) : 0.f;
+      const float a1 = __builtin_amdgcn_exp2f(m_b - m_new);
+      l_run = l_run * a0 + l_b * a1;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[(db * 16 + r) * 64 + lane] * a1;
+      m_off = m_new;
+      m_set = true;
+    }
+  }
+
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
 
   if constexpr (FUSED) {
     // For a later backward: each row's normaliser in log2 units ([B*H][N])
-    if (a.lse2 && hl == 0 && pq < g.N) a.lse2[(long long)bh * g.N + pq] = m_off + log2f(l_tot);
+    if (a.lse2 && hl == 0 && kg == 0 && pq < g.N) a.lse2[(long long)bh * g.N + pq] = m_off + log2f(l_tot);
     // Branch dropping ([G] 2 C): a sample whose gate value is below the
     // threshold keeps only the sparse branch (its state was not computed).
     if (a.s_gate[b] < g.drop_tau) {
-      if (pq >= g.N) return;
+      if (kg != 0 || pq >= g.N) return;
       bf16_t *orow = (bf16_t *)a.out.base + row_offset(g, a.out, b, h, pq);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -528,8 +522,9 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     }
     // Linear branch, projection, gate and combine for this wave's queries:
     //   out = O_s + relu(q) Hp / (relu(q) . Z + eps),  Hp = s_b (H W_p)^T
-    // Hp rows 0..63 go to K0 and rows 64..127 to V0 (same swizzle as K).
-    __syncthreads();  // every wave is done with the last key tile
+    // Hp rows 0..63 go to K0 and rows 64..127 to V0 (same swizzle as K);
+    // every wave loads its share, the waves holding the queries use it.
+    __syncthreads();  // every wave is done with the tile buffers
     const bf16_t *hsrc = a.hp + (long long)bh * kD * kD;
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
@@ -560,6 +555,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     const float inv_den = 1.f / (den + g.eps);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
+    if (kg != 0) return;
     f32x16 lin[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) lin[db] = f32x16{};
@@ -606,6 +602,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     return;
   }
 
+  if (kg != 0) return;
   if constexpr (MODE == 2) {
     // both half-waves of a query column return together, so the exchange
     // below sees its partner
@@ -642,8 +639,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
 }
 
 namespace {
-// One launch per head kind: window heads use 128-query tiles (4 waves),
-// Top-K heads one 64-query block per workgroup (2 waves).
+// One launch per head kind: window heads in 128-query tiles, Top-K heads one
+// 64-query block per workgroup; four waves each.
 template <int MODE>
 hipError_t launch_bf16(AttnArgs a, hipStream_t st) {
   const Geom &g = a.g;
@@ -659,9 +656,9 @@ hipError_t launch_bf16(AttnArgs a, hipStream_t st) {
     const unsigned grid = unsigned(a.tiles_per_head) * a.n_heads_sel * g.B;
     a.n_blocks = int(grid);
     if (mode)
-      attn_bf16_kernel<2, MODE><<<grid, 128, size_t(g.k) * sizeof(int32_t), st>>>(a);
+      attn_bf16_kernel<MODE, true><<<grid, 256, size_t(g.k) * sizeof(int32_t), st>>>(a);
     else
-      attn_bf16_kernel<4, MODE><<<grid, 256, 0, st>>>(a);
+      attn_bf16_kernel<MODE, false><<<grid, 256, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
