@@ -290,28 +290,20 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     }
   };
   // S^T[key][query] = K Q^T per block of 32 keys (raw scores: products of
-  // the stored values, accumulated in fp32)
-  auto qk = [&](const bf16_t *__restrict__ Ks, f32x16 (&s)[NKB]) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ks += 2) {
-      bf16x8 ka[2][NKB];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          ka[u][kb] = *(const bf16x8 *)(Ks + (kb0 + kb) * 32 * kD + k_lane + 16 * ((ks + u) ^ k_x));
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          s[kb] = mfma_32x32x16(ka[u][kb], qf[ks + u], s[kb]);
-    }
+  // the stored values, accumulated in fp32).  kop: the K operand of block kb
+  // of this wave's part of the tile for feature step ks.
+  auto kop = [&](const bf16_t *__restrict__ Ks, int kb, int ks) -> bf16x8 {
+    return *(const bf16x8 *)(Ks + (kb0 + kb) * 32 * kD + k_lane + 16 * (ks ^ k_x));
   };
-  // Softmax of one tile, in place.  Edge tiles mask first: key j is kept
+  // Feature steps 1..7 of block kb (step 0 starts the accumulator; below).
+  auto qk_rest = [&](const bf16_t *__restrict__ Ks, int kb, f32x16 &s) {
+#pragma unroll
+    for (int ks = 1; ks < 8; ++ks) s = mfma_32x32x16(kop(Ks, kb, ks), qf[ks], s);
+  };
+  // Softmax.  Key j is kept
   // iff j < N and, for window heads, |pq - j| <= r, i.e. the unsigned value
-  // pq - j + r is at most 2r (one subtract and one compare per score).
+  // pq - j + r is at most 2r (one subtract and one compare per score); the
+  // mask is applied where the scores start (qk_first).
   // The offset m_off only has to bound the row's scores loosely: O and l
   // share it, so the final O / l is exact whatever its value.  Each lane
   // exponentiates its scores under the current offset (one FMA and one
@@ -324,55 +316,72 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   // same query, so both halves keep one offset), the offset raised to it, O
   // and l rescaled and the tile's probabilities recomputed.  So probabilities
   // stay below 2^8 (no overflow in fp32 sums or in bf16), and an ordinary
-  // tile costs one exp2, half a pack and half a dot2 per score.
+  // tile costs one exp2, half a pack and half a dot2 per score.  (The test
+  // is per block of 32 keys: with 16 scores per lane it bounds each one the
+  // same way.)
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  auto exp_pack = [&](const f32x16 (&s)[NKB], float shift, bf16x8 (&pb)[2 * NKB]) -> float {
+  auto exp_pack = [&](const f32x16 &s, float shift, bf16x8 &p0, bf16x8 &p1) -> float {
     float lt = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 pv;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 pv;
+      for (int e = 0; e < 8; ++e)
+        // v_exp_f32 directly: tiny results flush to 0; large ones (even inf)
+        // are caught by the block-sum test below and recomputed
+        pv[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * half + e], c2, -shift));
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          // v_exp_f32 directly: tiny results flush to 0; large ones (even inf)
-          // are caught by the tile-sum test below and recomputed
-          pv[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + e], c2, -shift));
-#pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          lt = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, lt, false);
-        pb[2 * kb + half] = pv;
-      }
+      for (int e = 0; e < 8; e += 2)
+        lt = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, lt, false);
+      (half ? p1 : p0) = pv;
+    }
     return lt;
   };
-  auto softmax = [&](int k0, bool full, f32x16 (&s)[NKB], bf16x8 (&pb)[2 * NKB]) {
-    if (!full) {
+  // First feature step of every block.  The accumulator starts at 0; on
+  // edge tiles a masked key's starts at -inf instead, which the products
+  // (finite) leave at -inf, so the mask costs nothing after the scores
+  // exist and the tile's VALU work needs no second, masked copy.
+  auto qk_first = [&](const bf16_t *__restrict__ Ks, int k0, bool full, f32x16 (&s)[NKB]) {
+    bf16x8 ka[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) ka[kb] = kop(Ks, kb, 0);
+    if (full) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma_32x32x16(ka[kb], qf[0], f32x16{});
+    } else {
       int jl = k0 + 4 * hl;                              // j = jl + c below
-      // opaque to the optimiser: otherwise it carries the 32 per-score
+      // opaque to the optimiser: otherwise it carries the per-score
       // differences below across tiles as induction variables, updating
       // them on every tile although only edge tiles use them
       asm volatile("" : "+v"(jl));
       const unsigned wb = unsigned(pq - jl + g.r);        // pq - j + r = wb - c
       const int lim = g.N - jl;                          // j < N  <=>  c < lim
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb) {
+        f32x16 init;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int c = (kb0 + kb) * 32 + 8 * (r >> 2) + (r & 3);
           // bitwise, not short-circuit: keeps the mask a select, not a branch
           const bool keep = (c < lim) & (TOPK | (wb - unsigned(c) <= unsigned(2 * g.r)));
-          s[kb][r] = keep ? s[kb][r] : -INFINITY;
+          init[r] = keep ? 0.f : -INFINITY;
         }
+        s[kb] = mfma_32x32x16(ka[kb], qf[0], init);
+      }
     }
-    float lt = exp_pack(s, m_off, pb);
+  };
+  // Softmax of block kb of the tile, in place (its masked scores are -inf
+  // already).  sched: scheduling hints for the straight-line code up to the
+  // rare rescale branch.
+  auto softmax = [&](int kb, f32x16 &s, bf16x8 &p0, bf16x8 &p1, auto sched) {
+    float lt = exp_pack(s, m_off, p0, p1);
     const bool need = !(lt <= 256.f) || !m_set;
+    sched();
     if (__any(need)) {
-      float mx = s[0][0];
+      float mx = s[0];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
       mx = fmaf(mx, c2, -m_off);  // relative to the current offset (c2 > 0)
       // both half-waves of a query column agree on the maximum and on
       // whether to move the offset
@@ -394,17 +403,18 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
         m_off += delta;
       }
       m_set = m_set || (mxa != -INFINITY);
-      if (__any(delta != 0.f)) lt = exp_pack(s, m_off, pb);
+      if (__any(delta != 0.f)) lt = exp_pack(s, m_off, p0, p1);
     }
     l_run += lt;
   };
-  auto pv = [&](const bf16_t *__restrict__ Vs, const bf16x8 (&pb)[2 * NKB]) {
-    // O^T[d][q] += V^T[d][keys] P^T[keys][q].  k-step kk, half hl, element
-    // e = 4r + e' covers key 32*(kk/2) + 8*(2*(kk%2) + r) + 4*hl + e' of
-    // this wave's part of the tile (which starts at row 32*kb0); the
-    // matching V^T operand comes from two transposing reads (r = 0, 1).
+  auto pv = [&](const bf16_t *__restrict__ Vs, int kb, const bf16x8 &p0, const bf16x8 &p1) {
+    // O^T[d][q] += V^T[d][keys] P^T[keys][q] over block kb of 32 keys.
+    // k-step kk, half hl, element e = 4r + e' covers key
+    // 32*(kk/2) + 8*(2*(kk%2) + r) + 4*hl + e' of this wave's part of the
+    // tile (which starts at row 32*kb0); the matching V^T operand comes from
+    // two transposing reads (r = 0, 1).
 #pragma unroll
-    for (int kk = 0; kk < 2 * NKB; ++kk) {
+    for (int kk = 2 * kb; kk < 2 * kb + 2; ++kk) {
       // all four d-blocks' operands of this k-step first, then the MFMAs
       typedef __attribute__((ext_vector_type(8))) short s16x8;
       s16x8 va[4];
@@ -416,7 +426,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
         va[db] = s16x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       }
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(*(const bf16x8 *)&va[db], pb[kk], o[db]);
+      for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(*(const bf16x8 *)&va[db], (kk & 1) ? p1 : p0, o[db]);
     }
   };
   auto compute = [&](int k0, const bf16_t *__restrict__ Ks, const bf16_t *__restrict__ Vs) {
@@ -425,9 +435,43 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     if (!any) return;
     f32x16 s[NKB];
     bf16x8 pb[2 * NKB];
-    qk(Ks, s);
-    softmax(k0, full, s, pb);
-    pv(Vs, pb);
+    qk_first(Ks, k0, full, s);
+    if constexpr (NKB == 2) {
+      // Ordered so that each block's softmax (VALU) has independent MFMAs
+      // to issue beside it: block 0's scores, then block 1's products with
+      // block 0's softmax, block 0's PV products with block 1's softmax,
+      // then block 1's PV products.
+      qk_rest(Ks, 0, s[0]);
+      qk_rest(Ks, 1, s[1]);
+      softmax(0, s[0], pb[0], pb[1], [] {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 7; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 7; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+        }
+      });
+      pv(Vs, 0, pb[0], pb[1]);
+      softmax(1, s[1], pb[2], pb[3], [] {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+      });
+      pv(Vs, 1, pb[2], pb[3]);
+    } else {
+      qk_rest(Ks, 0, s[0]);
+      softmax(0, s[0], pb[0], pb[1], [] {});
+      pv(Vs, 0, pb[0], pb[1]);
+    }
   };
 
   // Tile starts are read before each DMA is issued and carried along, so no
