@@ -36,11 +36,8 @@
  *  pointers must be 16-byte aligned and contiguous in the stated layout.
  *  Scratch memory comes only from the caller's workspace (ws, ws_bytes),
  *  sized by salad_workspace_size, and the library keeps no pointer after a
- *  call returns.  The library's own kernels allocate no device memory; the
- *  two calls that run a GEMM (SALAD_PROJ_FULL forwards and
- *  salad_output_projection) use one hipBLASLt handle per device, created on
- *  first use and kept until the process ends, with GEMM algorithms that
- *  need no workspace (those calls are serialised by a lock around it).
+ *  call returns.  The library allocates no device memory and creates no
+ *  handles or streams.
  *
  *  Execution: calls enqueue kernels on `stream` and return without
  *  synchronising.  Results are deterministic (no floating-point atomics).
@@ -199,8 +196,8 @@ salad_status salad_combine(const salad_problem *p, const float *o_s, const float
  * v [B,N,H,d], x [B,N,C], w_p ([d,d] for SALAD_PROJ_HEAD, [C,C] for
  * SALAD_PROJ_FULL), gate_w [C] in io_dtype -> out [B,N,H,d] in io_dtype.
  * With SALAD_PROJ_FULL, out[b,n,:] = O_s[b,n,:] + s_b * (O_l[b,n,:] W_p) over
- * the token's C-wide rows; the [B*N, C] x [C, C] product runs as one hipBLASLt
- * GEMM (float32 accumulation) on `stream`, accumulating into out; the
+ * the token's C-wide rows; the [B*N, C] x [C, C] product runs as one GEMM
+ * kernel (float32 accumulation) on `stream`, accumulating into out; the
  * workspace then also holds s_b * O_l in token rows (B*N*C io_dtype
  * elements, zero for dropped samples).
  * s_override (device float [B]) replaces the gate when non-NULL; s_out
@@ -271,7 +268,7 @@ salad_status salad_window_calibrate(const salad_problem *p, const void *qw, cons
 
 /* Output projection ([S] step 7): out[b,n,:] = in[b,n,:] W_o, a row vector
  * times W_o [C, C] row-major, no bias; in, out [B, N, C] (equivalently
- * [B,N,H,d]) and W_o in io_dtype.  One hipBLASLt GEMM, float32 accumulation.
+ * [B,N,H,d]) and W_o in io_dtype.  One GEMM kernel, float32 accumulation.
  * in and out must not overlap.  Errors: NULL, ALIGN, SHAPE, HIP. */
 salad_status salad_output_projection(const salad_problem *p, const void *in, const void *w_o,
                                      void *out, hipStream_t stream);

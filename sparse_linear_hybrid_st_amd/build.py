@@ -45,7 +45,7 @@ def build(verbose: bool = False) -> str:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
-           f"-L{ROCM_LIB}", "-lhipblaslt", f"-Wl,-rpath,{ROCM_LIB}"]
+           f"-L{ROCM_LIB}", f"-Wl,-rpath,{ROCM_LIB}"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -7,10 +7,10 @@
 // section 2.3 and news.axiwang.com section 六 (token average, then a linear
 // layer and a sigmoid).
 //
-// Both are HBM-bound.  The gate reads X once: per sample, row chunks reduce
-// to partial dot products w . sum X[n] (fp32 inside a thread, fp64 across
-// threads and chunks) and one workgroup per sample finishes the mean and the
-// sigmoid -- a fixed summation order throughout.
+// Both are HBM-bound.  The gate reads X once: per sample, tiles of (row
+// chunk, column band) reduce to partial dot products w . sum X[n] (fp32
+// inside a lane, fp64 across lanes and tiles) and one workgroup per sample
+// finishes the mean and the sigmoid -- a fixed summation order throughout.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_util.h"
@@ -18,54 +18,70 @@
 namespace salad {
 
 // The gate is linear before the sigmoid: w . mean_n X[n] = (1/N) sum_n w . X[n],
-// so each workgroup reduces its row chunk straight to one number.
-// Grid (splits, B); thread t owns 8-column groups t, t+256, ...: it
-// accumulates sum_rows w[c] * X[n][c] in fp32 (one 16-byte load per row),
-// then the workgroup adds the 256 thread sums in fp64 (fixed-order tree).
+// so each workgroup reduces its share of X straight to one number.
+// Grid (column bands, row chunks, B), 256 threads.  A column band is 64
+// groups of 8 columns (one per lane); a chunk is kGateRows = 64 rows, and
+// wave w of the workgroup takes rows n0 + w, n0 + w + 4, ..., so each wave
+// reads 64 consecutive 8-column groups of a row (1 KB of bf16) per load.
+// A lane issues all 16 of its row loads before it adds any (one memory
+// latency per workgroup), accumulates w[c] * X[n][c] in fp32, and the
+// workgroup adds the 256 lane sums in fp64 in a fixed order (within each
+// wave, then the four waves).
 template <typename T>
 __global__ void __launch_bounds__(256) gate_partial_kernel(Geom g, const T *__restrict__ x,
                                                            const T *__restrict__ w,
-                                                           double *__restrict__ partial, int splits) {
-  const int s = blockIdx.x, b = blockIdx.y, C = g.H * g.D;
-  const int rows = (g.N + splits - 1) / splits;
-  const int n0 = s * rows, n1 = min(g.N, n0 + rows);
+                                                           double *__restrict__ partial) {
+  const int band = blockIdx.x, ch = blockIdx.y, b = blockIdx.z;
+  const int C = g.H * g.D, groups = C / 8;
+  const int n0 = ch * kGateRows, n1 = min(g.N, n0 + kGateRows);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int cg = band * 64 + lane;
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   float acc = 0.f;
-  for (int cg = threadIdx.x; cg * 8 < C; cg += 256) {
-    float wv[8], cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (cg < groups) {
+    float wv8[8], cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) wv[e] = io<T>::ld(w + cg * 8 + e);
-    // unrolled so that several rows' loads are in flight per thread
-#pragma unroll 8
-    for (int n = n0; n < n1; ++n) {
-      const T *src = x + ((long long)b * g.N + n) * C + cg * 8;
-      T v[8];
-      *(u32x4 *)v = *(const u32x4 *)src;
-      if (sizeof(T) == 4) *(u32x4 *)(v + 4) = *(const u32x4 *)(src + 4);
+    for (int e = 0; e < 8; ++e) wv8[e] = io<T>::ld(w + cg * 8 + e);
+    const T *src = x + ((long long)b * g.N + n0 + wv) * C + cg * 8;
+    constexpr int R = kGateRows / 4;  // rows per lane
+    T v[R][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cs[e] += io<T>::ld(v + e);
+    for (int i = 0; i < R; ++i) {
+      if (n0 + wv + 4 * i < n1) {
+        *(u32x4 *)v[i] = *(const u32x4 *)(src + 4ll * i * C);
+        if (sizeof(T) == 4) *(u32x4 *)(v[i] + 4) = *(const u32x4 *)(src + 4ll * i * C + 4);
+      } else {
+        *(u32x4 *)v[i] = u32x4{0, 0, 0, 0};
+        if (sizeof(T) == 4) *(u32x4 *)(v[i] + 4) = u32x4{0, 0, 0, 0};
+      }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(wv[e], cs[e], acc);
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cs[e] += io<T>::ld(v[i] + e);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(wv8[e], cs[e], acc);
   }
-  __shared__ double red[256];
-  red[threadIdx.x] = double(acc);
+  // fixed-order fp64 sums: a butterfly within the wave, then the four waves
+  double d = double(acc);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o);
+  __shared__ double red[4];
+  if (lane == 0) red[wv] = d;
   __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) partial[(long long)b * splits + s] = red[0];
+  if (threadIdx.x == 0)
+    partial[((long long)b * gridDim.y + ch) * gridDim.x + band] = ((red[0] + red[1]) + red[2]) + red[3];
 }
 
-// s_b = sigmoid(sum_s partial[b][s] / N + bias): one workgroup per sample,
-// thread t adds splits t, t+256, ... in order, then a fixed-order tree.
-__global__ void __launch_bounds__(256) gate_final_kernel(int N, int splits, const double *__restrict__ partial,
+// s_b = sigmoid(sum_i partial[b][i] / N + bias) over the n partial sums of
+// sample b: one workgroup per sample, thread t adds partials t, t+256, ...
+// in order, then a fixed-order tree.
+__global__ void __launch_bounds__(256) gate_final_kernel(int N, int n, const double *__restrict__ partial,
                                                          float bias, float *__restrict__ s_out) {
   const int b = blockIdx.x;
   __shared__ double red[256];
   double acc = 0.0;
-  for (int i = threadIdx.x; i < splits; i += 256) acc += partial[(long long)b * splits + i];
+  for (int i = threadIdx.x; i < n; i += 256) acc += partial[(long long)b * n + i];
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int st = 128; st > 0; st >>= 1) {
@@ -80,14 +96,14 @@ __global__ void __launch_bounds__(256) gate_final_kernel(int N, int splits, cons
 
 hipError_t launch_gate(const Geom &g, int bf16, const void *x, const void *w, float bias,
                        void *ws, float *s, hipStream_t st) {
-  const int splits = gate_splits(g);
+  const int bands = gate_bands(g), chunks = gate_chunks(g);
   double *partial = (double *)ws;
-  dim3 grid(splits, g.B);
+  dim3 grid(bands, chunks, g.B);
   if (bf16)
-    gate_partial_kernel<bf16_t><<<grid, 256, 0, st>>>(g, (const bf16_t *)x, (const bf16_t *)w, partial, splits);
+    gate_partial_kernel<bf16_t><<<grid, 256, 0, st>>>(g, (const bf16_t *)x, (const bf16_t *)w, partial);
   else
-    gate_partial_kernel<float><<<grid, 256, 0, st>>>(g, (const float *)x, (const float *)w, partial, splits);
-  gate_final_kernel<<<g.B, 256, 0, st>>>(g.N, splits, partial, bias, s);
+    gate_partial_kernel<float><<<grid, 256, 0, st>>>(g, (const float *)x, (const float *)w, partial);
+  gate_final_kernel<<<g.B, 256, 0, st>>>(g.N, bands * chunks, partial, bias, s);
   return hipGetLastError();
 }
 

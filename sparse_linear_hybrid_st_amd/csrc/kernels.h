@@ -32,14 +32,16 @@ inline int linear_splits(const Geom &g) {
   return want < 1 ? 1 : (want > chunks ? chunks : want);
 }
 
-// Row chunks per sample used by the gate's token mean.
-inline int gate_splits(const Geom &g) {
-  int want = 1024;
-  return want > g.N ? g.N : want;
-}
+// The gate's token mean runs over tiles of (row chunk, column band): a band
+// is 64 groups of 8 columns, a chunk kGateRows token rows.
+constexpr int kGateRows = 64;
+inline int gate_bands(const Geom &g) { return (g.H * g.D / 8 + 63) / 64; }
+inline int gate_chunks(const Geom &g) { return (g.N + kGateRows - 1) / kGateRows; }
 
-// Workspace bytes of the gate: one double per (sample, row chunk).
-inline size_t gate_ws_bytes(const Geom &g) { return size_t(g.B) * gate_splits(g) * sizeof(double); }
+// Workspace bytes of the gate: one double per (sample, row chunk, band).
+inline size_t gate_ws_bytes(const Geom &g) {
+  return size_t(g.B) * gate_chunks(g) * gate_bands(g) * sizeof(double);
+}
 
 // RoPE (cos, sin) table in fp64: rope_table_entries(g) double2 entries.
 int rope_table_entries(const Geom &g);
@@ -185,8 +187,10 @@ hipError_t launch_sparse_attn(const Geom &g, int bf16, View qv, View kv, View vv
 // olt (same layout) = s_b * o_l[b,h,p,:] (zero for dropped samples).
 hipError_t launch_split_full(const Geom &g, int bf16, const float *o_s, const float *o_l,
                              const float *s, void *out, void *olt, hipStream_t st);
-// Row-major out[rows, C] = a[rows, C] W[C, C] + beta * out (hipBLASLt,
-// float32 accumulation, storage type bf16 or f32).  a must not overlap out.
+// Row-major out[rows, C] = a[rows, C] W[C, C] + beta * out (one MFMA GEMM
+// kernel for bf16, a tiled fp32 kernel for f32; float32 accumulation; C a
+// multiple of 128 for bf16, of 64 for f32; beta 0 or 1).  a must not
+// overlap out.
 // Returns NULL on success, else a message.
 const char *gemm_rows(int bf16, long long rows, int C, const void *a, const void *w, float beta,
                       void *out, hipStream_t st);

@@ -57,7 +57,8 @@ __device__ __forceinline__ u32x4 relu_bf16x8(u32x4 v) {
 // tokens of one feature per lane, come from ds_read_b64_tr_b16: each 16-lane
 // group reads 4 rows x 64 bytes, which lin_swz spreads over distinct banks.
 // Wave w accumulates the 64x64 quadrant (i0, j0) = (64*(w/2), 64*(w%2)) of H.
-// The next tile's global loads are issued before the current tile's MFMAs.
+// The loads of the tile after next are issued before the current tile's MFMAs
+// (two tiles of rows in flight per thread).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int lin_swz(int j) { return ((j & 3) << 2) | ((j >> 2) & 3); }
 
@@ -125,8 +126,11 @@ __global__ void __launch_bounds__(256, 2) linear_state_bf16_kernel(Geom g, View 
         toff[op][bi][r] = row * D + (((f >> 3) ^ lin_swz(row)) << 3) + (f & 4);
       }
 
-  u32x4 kr[4], vr[4];
-  auto load = [&](int base) {
+  // Two tiles of K and V rows in flight: the loads of tile i+2 are issued
+  // while tile i's MFMAs run, with tile i+1 already in registers, so each
+  // load has two tiles of work to land in.
+  u32x4 kr0[4], vr0[4], kr1[4], vr1[4];
+  auto load = [&](int base, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int n = base + rg + 16 * i;
@@ -139,8 +143,8 @@ __global__ void __launch_bounds__(256, 2) linear_state_bf16_kernel(Geom g, View 
       }
     }
   };
-  if (n0 < n1) load(n0);
-  for (int base = n0; base < n1; base += TT) {
+  // working copies, relu(K), Z and the LDS tiles of the rows in kr / vr
+  auto stage = [&](int base, const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
     __syncthreads();  // previous tile's operand reads are done
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -158,7 +162,8 @@ __global__ void __launch_bounds__(256, 2) linear_state_bf16_kernel(Geom g, View 
       *(u32x4 *)(Vs + row * D + unit * 8) = vr[i];
     }
     __syncthreads();
-    if (base + TT < n1) load(base + TT);
+  };
+  auto mma = [&]() {
 #pragma unroll
     for (int ks = 0; ks < TT / 16; ++ks) {
       bf16x8 a[2], bb[2];
@@ -179,6 +184,17 @@ __global__ void __launch_bounds__(256, 2) linear_state_bf16_kernel(Geom g, View 
 #pragma unroll
         for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma32(a[bi], bb[bj], acc[bi][bj]);
     }
+  };
+  if (n0 < n1) load(n0, kr0, vr0);
+  if (n0 + TT < n1) load(n0 + TT, kr1, vr1);
+  for (int base = n0; base < n1; base += 2 * TT) {
+    stage(base, kr0, vr0);
+    if (base + 2 * TT < n1) load(base + 2 * TT, kr0, vr0);
+    mma();
+    if (base + TT >= n1) break;
+    stage(base + TT, kr1, vr1);
+    if (base + 3 * TT < n1) load(base + 3 * TT, kr1, vr1);
+    mma();
   }
 
   float *out = partial + ((long long)bh * S + s) * (D * D + D);
@@ -275,9 +291,12 @@ __global__ void linear_reduce_kernel(int D, int S, const float *__restrict__ par
 // of H (and 8 of Z) in a fixed order, keep them in LDS and fold the
 // projection and the gate in: Hp[j][i] = bf16(s_b * (H W_p)[i][j]).
 // Samples dropped by the branch threshold (s_b < drop_tau) are skipped.
-// Grid (16, B*H), 1024 threads: thread t sums element t of the block's 8
-// rows over the splits (one element per thread keeps many loads in flight:
-// the kernel is bound by their latency); block blk owns rows 8*blk..+7.
+// Grid (16, B*H), 1024 threads; block blk owns rows 8*blk..+7.  The kernel
+// is bound by the latency of its loads, so the splits are spread over four
+// thread groups: thread 256q + u sums the 16-byte unit u of the block's
+// 1024 H elements (and, for u < 2, of its 8 Z elements) over the splits
+// q, q+4, q+8, ... in order, and the four group sums are added in the order
+// q = 0..3 through LDS.
 // W_p is staged once per block as bf16 (16-byte loads); thread t < 256 then
 // computes row t/32 at columns (t%32) + 32m, m < 4.  H and Z are also
 // written out in fp32.
@@ -294,7 +313,8 @@ __global__ void __launch_bounds__(1024) linear_finalize_kernel(Geom g, int S,
                                                               bf16_t *__restrict__ hp) {
   constexpr int D = 128, per = D * D + D;
   __shared__ __attribute__((aligned(16))) T Ws[FULL ? 8 : D * D];
-  __shared__ float Hs[8 * D];
+  __shared__ __attribute__((aligned(16))) float Hs[8 * D];
+  __shared__ f32x4 red[4][258];
   const int blk = blockIdx.x, bh = blockIdx.y, b = bh / g.H, t = threadIdx.x;
   if (s_gate[b] < g.drop_tau) return;  // dropped sample: no linear branch (its state was skipped)
   // stage W_p (16-byte chunks)
@@ -303,19 +323,29 @@ __global__ void __launch_bounds__(1024) linear_finalize_kernel(Geom g, int S,
   if constexpr (!FULL)
     for (int e = t * VEC; e < D * D; e += 1024 * VEC)
       *(u32x4 *)(Ws + e) = *(const u32x4 *)(w_p + e);
-  // reduce element t of this block's 8 rows over the splits, fixed order
-  const float *p = partial + (long long)bh * S * per + 8 * blk * D + t;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) acc += p[(long long)s * per];
-  Hs[t] = acc;
-  hm[((long long)bh * D + 8 * blk) * D + t] = acc;
-  if (t < 8) {  // Z[8 blk + t]
-    const float *pz = partial + (long long)bh * S * per + D * D + 8 * blk + t;
-    float az = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < S; ++s) az += pz[(long long)s * per];
-    zv[(long long)bh * D + 8 * blk + t] = az;
+  // this block's 1024 H elements and 8 Z elements over the splits: group q
+  // takes splits q, q+4, ...; then the groups in order
+  {
+    const int q = t >> 8, u = t & 255;
+    const float *p = partial + (long long)bh * S * per;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = q; s < S; s += 4) {
+      acc += *(const f32x4 *)(p + (long long)s * per + 8 * blk * D + 4 * u);
+      if (u < 2) accz += *(const f32x4 *)(p + (long long)s * per + D * D + 8 * blk + 4 * u);
+    }
+    red[q][u] = acc;
+    if (u < 2) red[q][256 + u] = accz;
+  }
+  __syncthreads();
+  if (t < 258) {
+    const f32x4 v = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
+    if (t < 256) {
+      *(f32x4 *)(Hs + 4 * t) = v;
+      *(f32x4 *)(hm + ((long long)bh * D + 8 * blk) * D + 4 * t) = v;
+    } else {
+      *(f32x4 *)(zv + (long long)bh * D + 8 * blk + 4 * (t - 256)) = v;
+    }
   }
   __syncthreads();
   if (t >= 256) return;

@@ -28,6 +28,8 @@ FULL_CASES = [
     C.small("full-f32-d64", (3, 4, 8), 3, 64, "f32", [0, 1, 2], 9, 16, 2, batch=2,
             x_sample_shift=True, qk_channel_scale=False),
     C.small("full-f32-d128", (2, 5, 9), 3, 128, "f32", [0, 1, 2], 11, 16, 2, batch=2),
+    # 1,056 token rows: the GEMM's 256-row bands, the last one ragged
+    C.small("full-bf16-1056rows", (4, 6, 11), 4, 128, "bf16", [0, 1, 2, 2], 9, 64, 2, batch=4),
 ]
 
 
@@ -79,11 +81,12 @@ def test_full_width_gate_zero_and_dropping(w):
     assert_close(host64(out), ref["out"], w.io_dtype, f"{w.name}: full-width, one sample dropped")
 
 
-@pytest.mark.parametrize("io_dtype", ["bf16", "f32"])
-def test_output_projection(io_dtype):
+@pytest.mark.parametrize("io_dtype,grid,head_dim", [("bf16", (3, 5, 7), 128), ("f32", (3, 5, 7), 64),
+                                                   ("bf16", (6, 7, 9), 128)],
+                         ids=["bf16-c384", "f32-c192", "bf16-c384-756rows"])
+def test_output_projection(io_dtype, grid, head_dim):
     bf16 = io_dtype == "bf16"
-    w = C.small("wo", (3, 5, 7), 3, 128 if bf16 else 64, io_dtype, [0, 1, 2], 9, 64 if bf16 else 16, 2,
-                batch=2)
+    w = C.small("wo", grid, 3, head_dim, io_dtype, [0, 1, 2], 9, 64 if bf16 else 16, 2, batch=2)
     p = S.problem_from_workload(w)
     x = I.make_inputs(w)["v"]                       # any [B, N, C] storage-type tensor
     w_o = I.make_w_o(w)

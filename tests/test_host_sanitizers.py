@@ -46,7 +46,7 @@ def test_c_abi_host_code_under_asan_and_ubsan(tmp_path):
     lib = str(tmp_path / "libsalad_asan.so")
     others = [o for o in objs if not o.endswith("api.hip.o")]
     link_cmd = [CLANG, "-shared", "-fPIC", "-shared-libasan", "-fsanitize=address", "-o", lib, api_o,
-                *others, "-L/opt/rocm/lib", "-lamdhip64", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
+                *others, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(link_cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     env = dict(os.environ, SALAD_LIB=lib, LD_PRELOAD=rt,
