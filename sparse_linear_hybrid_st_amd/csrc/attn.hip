@@ -295,10 +295,17 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   auto kop = [&](const bf16_t *__restrict__ Ks, int kb, int ks) -> bf16x8 {
     return *(const bf16x8 *)(Ks + (kb0 + kb) * 32 * kD + k_lane + 16 * (ks ^ k_x));
   };
-  // Feature steps 1..7 of block kb (step 0 starts the accumulator; below).
-  auto qk_rest = [&](const bf16_t *__restrict__ Ks, int kb, f32x16 &s) {
+  // K operands of feature steps 1..7 of block kb (step 0 starts the
+  // accumulator; below), and their products.  The operands are read as a
+  // batch, one phase before the products that use them, so no product
+  // waits for its own LDS read.
+  auto kread = [&](const bf16_t *__restrict__ Ks, int kb, bf16x8 (&ka)[7]) {
 #pragma unroll
-    for (int ks = 1; ks < 8; ++ks) s = mfma_32x32x16(kop(Ks, kb, ks), qf[ks], s);
+    for (int ks = 1; ks < 8; ++ks) ka[ks - 1] = kop(Ks, kb, ks);
+  };
+  auto qk_rest = [&](const bf16x8 (&ka)[7], f32x16 &s) {
+#pragma unroll
+    for (int ks = 1; ks < 8; ++ks) s = mfma_32x32x16(ka[ks - 1], qf[ks], s);
   };
   // Softmax.  Key j is kept
   // iff j < N and, for window heads, |pq - j| <= r, i.e. the unsigned value
@@ -407,27 +414,30 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     }
     l_run += lt;
   };
-  auto pv = [&](const bf16_t *__restrict__ Vs, int kb, const bf16x8 &p0, const bf16x8 &p1) {
-    // O^T[d][q] += V^T[d][keys] P^T[keys][q] over block kb of 32 keys.
-    // k-step kk, half hl, element e = 4r + e' covers key
-    // 32*(kk/2) + 8*(2*(kk%2) + r) + 4*hl + e' of this wave's part of the
-    // tile (which starts at row 32*kb0); the matching V^T operand comes from
-    // two transposing reads (r = 0, 1).
+  // O^T[d][q] += V^T[d][keys] P^T[keys][q] over block kb of 32 keys.
+  // k-step kk, half hl, element e = 4r + e' covers key
+  // 32*(kk/2) + 8*(2*(kk%2) + r) + 4*hl + e' of this wave's part of the
+  // tile (which starts at row 32*kb0); the matching V^T operand comes from
+  // two transposing reads (r = 0, 1).  vread reads block kb's eight
+  // operands (two k-steps x four d-blocks) as a batch ahead of pv.
+  typedef __attribute__((ext_vector_type(8))) short s16x8;
+  auto vread = [&](const bf16_t *__restrict__ Vs, int kb, s16x8 (&va)[8]) {
 #pragma unroll
-    for (int kk = 2 * kb; kk < 2 * kb + 2; ++kk) {
-      // all four d-blocks' operands of this k-step first, then the MFMAs
-      typedef __attribute__((ext_vector_type(8))) short s16x8;
-      s16x8 va[4];
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16_t *vk = Vs + 16 * (2 * kb0 + kk) * kD;
+        const bf16_t *vk = Vs + 16 * (2 * kb0 + 2 * kb + k2) * kD;
         const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vk + v_off[0][db]));
         const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vk + v_off[1][db]));
-        va[db] = s16x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        va[4 * k2 + db] = s16x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       }
+  };
+  auto pv = [&](const s16x8 (&va)[8], const bf16x8 &p0, const bf16x8 &p1) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(*(const bf16x8 *)&va[db], (kk & 1) ? p1 : p0, o[db]);
-    }
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = mfma_32x32x16(*(const bf16x8 *)&va[4 * k2 + db], k2 ? p1 : p0, o[db]);
   };
   auto compute = [&](int k0, const bf16_t *__restrict__ Ks, const bf16_t *__restrict__ Vs) {
     bool any, full;
@@ -436,15 +446,23 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     f32x16 s[NKB];
     bf16x8 pb[2 * NKB];
     qk_first(Ks, k0, full, s);
+    bf16x8 ka[7];
+    s16x8 va[8];
+    kread(Ks, 0, ka);
     if constexpr (NKB == 2) {
       // Ordered so that each block's softmax (VALU) has independent MFMAs
-      // to issue beside it: block 0's scores, then block 1's products with
-      // block 0's softmax, block 0's PV products with block 1's softmax,
-      // then block 1's PV products.
-      qk_rest(Ks, 0, s[0]);
-      qk_rest(Ks, 1, s[1]);
+      // to issue beside it, and every batch of operands is read one phase
+      // ahead: block 0's products (block 1's K operands read meanwhile),
+      // block 1's products with block 0's softmax (block 0's V operands
+      // read meanwhile), block 0's PV products with block 1's softmax
+      // (block 1's V operands read meanwhile), block 1's PV products.
+      qk_rest(ka, s[0]);
+      bf16x8 kb1[7];
+      kread(Ks, 1, kb1);
+      qk_rest(kb1, s[1]);
+      vread(Vs, 0, va);
       softmax(0, s[0], pb[0], pb[1], [] {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
 #pragma unroll
         for (int i = 0; i < 7; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -453,12 +471,14 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 7; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
         }
       });
-      pv(Vs, 0, pb[0], pb[1]);
+      pv(va, pb[0], pb[1]);
+      s16x8 vb[8];
+      vread(Vs, 1, vb);
       softmax(1, s[1], pb[2], pb[3], [] {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -466,11 +486,21 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
         }
       });
-      pv(Vs, 1, pb[2], pb[3]);
+      pv(vb, pb[2], pb[3]);
     } else {
-      qk_rest(Ks, 0, s[0]);
-      softmax(0, s[0], pb[0], pb[1], [] {});
-      pv(Vs, 0, pb[0], pb[1]);
+      // block 0's products with its V operands read meanwhile, its
+      // softmax, its PV products
+      qk_rest(ka, s[0]);
+      vread(Vs, 0, va);
+      softmax(0, s[0], pb[0], pb[1], [] {
+        __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
+#pragma unroll
+        for (int i = 0; i < 7; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      });
+      pv(va, pb[0], pb[1]);
     }
   };
 
