@@ -266,10 +266,12 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   // Running offset m_off (log2 units) of this lane's query: probabilities are
-  // exp2(c2 * s - m_off).  l_run: this lane's partial row sum.  m_set: an
-  // offset has been taken from a real score (until then no key has counted).
+  // exp2(c2 * s - m_off).  l_run: this lane's partial row sum.  m_set_w:
+  // the lanes whose offset has been taken from a real score (until then no
+  // key has counted), kept as a wave mask so the per-block test below is
+  // one compare and scalar logic.
   float m_off = 0.f, l_run = 0.f;
-  bool m_set = false;
+  unsigned long long m_set_w = 0ull;
 
   // One key tile: S^T = K Q^T (qk), online softmax (softmax), O^T += V^T
   // P^T (pv), over this wave's NKB blocks of 32 keys of the tile (blocks
@@ -383,9 +385,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   // rare rescale branch.
   auto softmax = [&](int kb, f32x16 &s, bf16x8 &p0, bf16x8 &p1, auto sched) {
     float lt = exp_pack(s, m_off, p0, p1);
-    const bool need = !(lt <= 256.f) || !m_set;
+    const unsigned long long need_w = __ballot(!(lt <= 256.f)) | ~m_set_w;
     sched();
-    if (__any(need)) {
+    if (need_w) {
+      const bool need = (need_w >> lane) & 1ull, m_set = (m_set_w >> lane) & 1ull;
       float mx = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -409,7 +412,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
           for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
         m_off += delta;
       }
-      m_set = m_set || (mxa != -INFINITY);
+      m_set_w |= __ballot(mxa != -INFINITY);
       if (__any(delta != 0.f)) lt = exp_pack(s, m_off, p0, p1);
     }
     l_run += lt;
@@ -538,6 +541,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     // group through LDS (the tile buffers are free now); O and l are scaled
     // to the larger offset.  A half that saw no key (no offset) adds nothing.
     __syncthreads();                       // every wave is done with the tile buffers
+    bool m_set = (m_set_w >> lane) & 1ull;
     float *xo = (float *)(qg ? K1 : K0);  // [64 values][64 lanes]
     float *xm = (float *)V0 + qg * 192;    // [3][64 lanes]
     if (kg == 1) {
