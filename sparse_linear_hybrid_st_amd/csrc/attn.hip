@@ -317,35 +317,39 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   // share it, so the final O / l is exact whatever its value.  Each lane
   // exponentiates its scores under the current offset (one FMA and one
   // exp2 per score: the scores stay exact products), packs them to bf16
-  // and sums the packed values (v_dot2 with (1, 1): the same values the PV
-  // product weighs V with).  A lane whose tile sum exceeds 2^8 may hold a
-  // probability above 2^8 (every term is at most the sum); only then, or
+  // for the PV product and sums them in fp32 (plain adds: the dot-product
+  // instructions that could sum the packed pairs share the matrix unit's
+  // issue and cost more than the adds).  A lane whose block sum exceeds 2^8
+  // may hold a probability above 2^8 (every term is at most the sum); only then, or
   // while no offset has been taken, is the tile's true maximum formed,
   // combined with the other half-wave (which holds the other keys of the
   // same query, so both halves keep one offset), the offset raised to it, O
   // and l rescaled and the tile's probabilities recomputed.  So probabilities
   // stay below 2^8 (no overflow in fp32 sums or in bf16), and an ordinary
-  // tile costs one exp2, half a pack and half a dot2 per score.  (The test
+  // tile costs one FMA, one exp2, half a pack and one add per score.  (The test
   // is per block of 32 keys: with 16 scores per lane it bounds each one the
   // same way.)
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   auto exp_pack = [&](const f32x16 &s, float shift, bf16x8 &p0, bf16x8 &p1) -> float {
-    float lt = 0.f;
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      // v_exp_f32 directly: tiny results flush to 0; large ones (even inf)
+      // are caught by the block-sum test below and recomputed
+      x[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -shift));
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       bf16x8 pv;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        // v_exp_f32 directly: tiny results flush to 0; large ones (even inf)
-        // are caught by the block-sum test below and recomputed
-        pv[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * half + e], c2, -shift));
-#pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        lt = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, lt, false);
+      for (int e = 0; e < 8; ++e) pv[e] = (__bf16)x[8 * half + e];
       (half ? p1 : p0) = pv;
     }
-    return lt;
+    // the row sum in fp32 (a pairwise tree: v_add, not the dot-product
+    // instructions, which share the matrix unit's issue)
+#pragma unroll
+    for (int w2 = 1; w2 < 16; w2 *= 2)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2 * w2) x[e] += x[e + w2];
+    return x[0];
   };
   // First feature step of every block.  The accumulator starts at 0; on
   // edge tiles a masked key's starts at -inf instead, which the products
