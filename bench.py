@@ -120,7 +120,9 @@ def cpu_baseline(w, inp, flops_total: float, full: bool = False):
                       for k, v in sorted(t_kind.items()))
     return {
         "value": flops_total / t_layer / 1e12, "unit": "TFLOP/s", "cores": int(procs),
-        "kind": "oracle", "ms_per_layer": t_layer * 1e3, "cpu_seconds_spent": spent,
+        "kind": "oracle", "ms_per_layer": t_layer * 1e3,
+        # wall time of the sample, and the core time it held (every process busy)
+        "wall_seconds_spent": spent, "core_seconds_spent": t_gate + (spent - t_gate) * procs,
         "extrapolated": not full, "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
         "sample": ("the whole layer: every head of every sample, all rows" if full else
                    f"one whole head per head kind ({kinds}; every output row, the head's linear state "
