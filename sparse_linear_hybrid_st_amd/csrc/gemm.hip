@@ -113,6 +113,28 @@ __global__ void __launch_bounds__(64 * NWV, 1) gemm_bf16_kernel(const bf16_t *__
     const int u = (lane & 31) ^ kv_swz(kr);
     w_voff[par] = ((kr - 2 * par * NWV) * C + n0 + ((n0 + kGN <= C ? u : (u & 15)) << 3)) * 2;
   }
+  // The last stage computes from one buffer while the other (A0, W0: the
+  // number of stages is even) is free.  Then each wave that stores copies
+  // the old out values of its first 32-row block (32 rows x its 128
+  // columns, 8 KB) into its own part of that buffer (waves 0-3 in A0, 4-7
+  // in W0), so the read-modify-write below finds half of them in LDS
+  // instead of waiting for HBM.  Row r of a copy holds its 16-byte unit u
+  // at u ^ (r mod 16); rows past m_valid re-read row m_valid - 1 (never
+  // stored).
+  const bool opf = accumulate && NST == 2 && n0 + 128 * wn < C;
+  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(out + (long long)m0 * C), 0, unsigned(m_valid) * unsigned(C) * 2u, 0x00020000);
+  auto prefetch_out = [&](bf16_t *__restrict__ Ad, bf16_t *__restrict__ Wd) {
+    bf16_t *reg = (wv < 4 ? Ad : Wd) + (wv & 3) * 4096;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      const int u = (lane & 15) ^ (row & 15);
+      const int grow = min(32 * MB * wm + row, m_valid - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_void *)(reg + 512 * i), 16,
+                                               unsigned((grow * C + n0 + 128 * wn + u * 8) * 2), 0, 0, 0);
+    }
+  };
   auto issue = [&](int k0, bf16_t *__restrict__ Ad, bf16_t *__restrict__ Wd) {
 #pragma unroll
     for (int i = 0; i < A_OPS; ++i) {
@@ -202,7 +224,10 @@ __global__ void __launch_bounds__(64 * NWV, 1) gemm_bf16_kernel(const bf16_t *__
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
     wg_barrier();
-    if (kt + NST - 1 < n_k) issue((kt + NST - 1) * KGK, An, Wn);
+    if (kt + NST - 1 < n_k)
+      issue((kt + NST - 1) * KGK, An, Wn);
+    else if (NST == 2 && opf)
+      prefetch_out(An, Wn);
     compute(As, Ws);
   };
   issue(0, A0, W0);
@@ -242,7 +267,13 @@ __global__ void __launch_bounds__(64 * NWV, 1) gemm_bf16_kernel(const bf16_t *__
         bf16_t *dst = orow + 32 * nb + 8 * r4 + 4 * hl;
         float add[4] = {0.f, 0.f, 0.f, 0.f};
         if (accumulate) {
-          const bf16x4 o = *(const bf16x4 *)dst;
+          bf16x4 o;
+          if (opf && mb == 0) {  // the copy made during the last stage
+            const bf16_t *reg = (wv < 4 ? A0 : W0) + (wv & 3) * 4096;
+            o = *(const bf16x4 *)(reg + lr * 128 + (((4 * nb + r4) ^ (lr & 15)) << 3) + 4 * hl);
+          } else {
+            o = *(const bf16x4 *)dst;
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) add[e] = float(o[e]);
         }
