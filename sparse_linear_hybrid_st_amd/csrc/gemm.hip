@@ -255,6 +255,30 @@ __global__ void __launch_bounds__(64 * NWV, 1) gemm_bf16_kernel(const bf16_t *__
   if (n0 + 128 * wn >= C) return;
   int lr = l32;
   asm volatile("" : "+v"(lr));
+  // Old values: the reads from HBM (blocks not copied to LDS) are issued
+  // first, then the copied block is read from LDS, so those reads overlap
+  // the LDS work.
+  bf16x4 old[MB][NB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int mr = 32 * MB * wm + 32 * mb + lr;
+    const bf16_t *orow = out + (long long)(m0 + min(mr, m_valid - 1)) * C + n0 + 128 * wn;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        old[mb][nb][r4] = bf16x4{};
+        if (accumulate && !(opf && mb == 0)) old[mb][nb][r4] = *(const bf16x4 *)(orow + 32 * nb + 8 * r4 + 4 * hl);
+      }
+  }
+  if (opf) {  // the copy made during the last stage
+    const bf16_t *reg = (wv < 4 ? A0 : W0) + (wv & 3) * 4096;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        old[0][nb][r4] = *(const bf16x4 *)(reg + lr * 128 + (((4 * nb + r4) ^ (lr & 15)) << 3) + 4 * hl);
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int mr = 32 * MB * wm + 32 * mb + lr;
@@ -264,23 +288,10 @@ __global__ void __launch_bounds__(64 * NWV, 1) gemm_bf16_kernel(const bf16_t *__
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        bf16_t *dst = orow + 32 * nb + 8 * r4 + 4 * hl;
-        float add[4] = {0.f, 0.f, 0.f, 0.f};
-        if (accumulate) {
-          bf16x4 o;
-          if (opf && mb == 0) {  // the copy made during the last stage
-            const bf16_t *reg = (wv < 4 ? A0 : W0) + (wv & 3) * 4096;
-            o = *(const bf16x4 *)(reg + lr * 128 + (((4 * nb + r4) ^ (lr & 15)) << 3) + 4 * hl);
-          } else {
-            o = *(const bf16x4 *)dst;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) add[e] = float(o[e]);
-        }
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[nb][mb][4 * r4 + e] + add[e]);
-        *(bf16x4 *)dst = v;
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[nb][mb][4 * r4 + e] + float(old[mb][nb][r4][e]));
+        *(bf16x4 *)(orow + 32 * nb + 8 * r4 + 4 * hl) = v;
       }
     }
   }
