@@ -30,6 +30,9 @@ FULL_CASES = [
     C.small("full-f32-d128", (2, 5, 9), 3, 128, "f32", [0, 1, 2], 11, 16, 2, batch=2),
     # 1,056 token rows: the GEMM's 256-row bands, the last one ragged
     C.small("full-bf16-1056rows", (4, 6, 11), 4, 128, "bf16", [0, 1, 2, 2], 9, 64, 2, batch=4),
+    # C = 640: the last 256-column tile is half wide (its upper waves store
+    # nothing); 378 rows: two row bands, the second ragged
+    C.small("full-bf16-c640-ragged", (3, 7, 9), 5, 128, "bf16", [0, 1, 2, 0, 1], 20, 64, 2, batch=2),
 ]
 
 
