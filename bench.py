@@ -87,12 +87,13 @@ def cpu_baseline(w, inp, flops_total: float, full: bool = False):
     import numpy as np
 
     import oracle as O
-    from oracle.parallel import whole_head, workers
+    from oracle.parallel import warm, whole_head, workers
     from sparse_linear_hybrid_st_amd import inputs as I
 
     args = [inp[n].float().numpy() for n in ("q", "k", "v", "x")] + \
         [I.as_f64(inp[n]) for n in ("w_p", "gate_w")]
     procs = workers()
+    warm(procs)  # the first start of the worker interpreters is not part of the oracle's time
     t0 = time.perf_counter()
     s_ref = [O.gate(args[3][b], args[5], inp["gate_b"]) for b in range(w.batch)]
     t_gate = time.perf_counter() - t0

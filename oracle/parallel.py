@@ -35,6 +35,19 @@ def _chunk(args):
     return np.stack([res[(0, int(n), 0)] for n in rows])
 
 
+def _ready(_):
+    return np.float64(O.gate(np.ones((2, 2)), np.ones(2), 0.0))
+
+
+def warm(n_proc: int | None = None) -> None:
+    """Start and stop one pool of workers that import numpy and the oracle,
+    so that a timed run does not pay the first, cold start of the
+    interpreters and their imports."""
+    n_proc = n_proc or workers()
+    with cf.ProcessPoolExecutor(n_proc, mp_context=mp.get_context("spawn")) as pool:
+        list(pool.map(_ready, range(n_proc)))
+
+
 def workers() -> int:
     """CPU processes to use: the host's cores, at most 16."""
     return max(1, min(16, os.cpu_count() or 1))
