@@ -121,6 +121,7 @@ __global__ void __launch_bounds__(64 * NWV, 1) gemm_bf16_kernel(const bf16_t *__
   // instead of waiting for HBM.  Row r of a copy holds its 16-byte unit u
   // at u ^ (r mod 16); rows past m_valid re-read row m_valid - 1 (never
   // stored).
+  static_assert(NST != 2 || (NWV <= 8 && SA >= 4 * 4096 && SW >= 4 * 4096), "out copies fit the free buffer");
   const bool opf = accumulate && NST == 2 && n0 + 128 * wn < C;
   const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(out + (long long)m0 * C), 0, unsigned(m_valid) * unsigned(C) * 2u, 0x00020000);
