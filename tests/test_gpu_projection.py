@@ -33,6 +33,8 @@ FULL_CASES = [
     # C = 640: the last 256-column tile is half wide (its upper waves store
     # nothing); 378 rows: two row bands, the second ragged
     C.small("full-bf16-c640-ragged", (3, 7, 9), 5, 128, "bf16", [0, 1, 2, 0, 1], 20, 64, 2, batch=2),
+    # one head, C = 128: a single half-wide column tile
+    C.small("full-bf16-one-head", (4, 5, 6), 1, 128, "bf16", [1], 10, 64, 1, batch=2),
 ]
 
 
