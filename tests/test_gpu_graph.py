@@ -8,6 +8,7 @@ own eager work and synchronisations between the replays; the eager output
 is checked against the oracle first.
 """
 
+import numpy as np
 import pytest
 import torch
 
@@ -64,3 +65,57 @@ def test_forward_replays_in_graph(w, proj):
         torch.cuda.synchronize()
         assert torch.isfinite(other)
         assert torch.equal(out, eager), f"{w.name}: replay {i} differs from the eager call"
+
+
+def test_forward_and_backward_replay_in_one_graph():
+    """A training step's layer calls, forward (saving out and the row
+    normalisers) then backward, captured together; replays bitwise equal
+    to the eager calls."""
+    w = CASES[0][0]
+    print(f"[graph] forward + backward {w.name}", flush=True)
+    inp = I.make_inputs(w)
+    p = S.problem_from_workload(w)
+    d = {n: dev(inp[n]) for n in ("q", "k", "v", "x", "w_p", "gate_w")}
+    g = np.random.default_rng(w.seed + 77).standard_normal((w.batch, w.N, w.n_heads, w.head_dim))
+    go = dev(I.to_storage(g.astype(np.float32), w.io_dtype))
+    ws, bws = S.workspace(p), S.backward_workspace(p)
+
+    def bufs():
+        return {"out": torch.empty_like(d["q"]),
+                "lse": torch.empty((w.batch, w.n_heads, w.N), dtype=torch.float32, device="cuda"),
+                "dq": torch.empty_like(d["q"]), "dk": torch.empty_like(d["q"]), "dv": torch.empty_like(d["q"]),
+                "dx": torch.empty_like(d["x"]),
+                "dwp": torch.empty((w.head_dim, w.head_dim), dtype=torch.float32, device="cuda"),
+                "dgw": torch.empty(w.n_heads * w.head_dim, dtype=torch.float32, device="cuda"),
+                "dgb": torch.empty(1, dtype=torch.float32, device="cuda"),
+                "ds": torch.empty(w.batch, dtype=torch.float32, device="cuda")}
+
+    def step(b):
+        S.salad_attn_forward(p, d["q"], d["k"], d["v"], d["x"], d["w_p"], d["gate_w"], inp["gate_b"], b["out"], ws,
+                             lse_out=b["lse"])
+        S.salad_attn_backward(p, d["q"], d["k"], d["v"], d["x"], d["w_p"], d["gate_w"], inp["gate_b"], go,
+                              b["dq"], b["dk"], b["dv"], b["dwp"], bws, dx=b["dx"], dgate_w=b["dgw"],
+                              dgate_b=b["dgb"], ds=b["ds"], out_saved=b["out"], lse_saved=b["lse"])
+
+    eager = bufs()
+    step(eager)
+    torch.cuda.synchronize()
+    got = bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(got)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(got)
+    torch.cuda.synchronize()
+    for i in range(3):
+        for t in got.values():
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in eager:
+            assert torch.equal(got[n], eager[n]), f"replay {i}: {n} differs from the eager call"
